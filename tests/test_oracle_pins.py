@@ -1,0 +1,540 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU. Each checks the oracle against something
+other than itself: values the pages print (fixtures under tests/golden/),
+closed forms, invariants, independent library routines (torch's E4M3
+conversion, rocRAND's Philox) and brute force with exact rationals.
+"""
+import math
+import os
+import shutil
+import subprocess
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+GRID = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+        Fraction(4), Fraction(6)]
+
+
+def f32(x):
+    return np.float32(x)
+
+
+def bits_to_f32(u):
+    return np.asarray(u, dtype=np.uint32).view(np.float32)
+
+
+# ------------------------------------------------------------ page values
+
+def test_e2m1_codebook_matches_page(golden):
+    rows = golden("e2m1_codebook.txt")
+    assert len(rows) == 8
+    for code_s, value_s in rows:
+        code, value = int(code_s), float(value_s)
+        assert oracle.e2m1_decode(code) == value
+        neg = oracle.e2m1_decode(code | 8)
+        assert neg == -value
+        assert math.copysign(1.0, neg) == -1.0  # the sign bit is always mirrored (0x8 = -0)
+
+
+def test_worked_reconstruction(golden):
+    for payload_s, sblock_s, sglobal_s, expected_s in golden("worked_reconstruction.txt"):
+        payload, s_block = float(payload_s), float(sblock_s)
+        s_global, expected = float(sglobal_s), float(expected_s)
+        # payload 4 is magnitude code 6
+        code = [c for c in range(8) if oracle.e2m1_decode(c) == payload][0]
+        sb = oracle.e4m3_encode(s_block)
+        assert oracle.e4m3_decode(sb) == s_block
+        # a 16x16 tensor whose first element carries the payload, 1D scales
+        R, C = 16, 16
+        codes = np.zeros((R, C // 2), np.uint8)
+        codes[0, 0] = code
+        scales = np.full((R, C // 16), sb, np.uint8)
+        out = oracle.dequantize(codes, scales, 1, s_global, R, C)
+        assert out[0, 0] == np.float32(expected)
+        # the same through 2D tile scales
+        scales2 = np.full((R // 16, C // 16), sb, np.uint8)
+        out2 = oracle.dequantize(codes, scales2, 2, s_global, R, C)
+        assert out2[0, 0] == np.float32(expected)
+
+
+def test_format_limits(golden):
+    lim = {k: float(v) for k, v in golden("format_limits.txt")}
+    finite = [oracle.e4m3_decode(b) for b in range(256) if not math.isnan(oracle.e4m3_decode(b))]
+    assert max(finite) == lim["e4m3_max"]
+    assert max(oracle.e2m1_decode(c) for c in range(16)) == lim["e2m1_max"]
+    assert lim["e4m3_max"] * lim["e2m1_max"] == lim["global_scale_divisor"]
+    # a tensor whose amax is exactly the divisor has a unit global scale
+    assert oracle.global_scale(lim["global_scale_divisor"]) == 1.0
+    # saturation at the top of both formats
+    assert oracle.e4m3_encode(1e30) == 0x7E and oracle.e4m3_decode(0x7E) == 448.0
+    assert oracle.e2m1_rne(1e30) == 7 and oracle.e2m1_rne(float("inf")) == 7
+
+
+def test_storage_bits(golden):
+    exp = {k: (float(v), float(t)) for k, v, t in golden("storage_bits.txt")}
+    x = W.normal_tensor(64, 256, seed=11)
+    n = x.size
+    r = oracle.quantize_1d(x, rowwise=True)
+    bits_1d = 8 * (r["codes_row"].nbytes + r["scales_row"].nbytes) / n
+    v, tol = exp["bits_per_element_1d"]
+    assert abs(bits_1d - v) <= tol
+    v, tol = exp["bits_per_block_1d"]
+    assert abs(bits_1d * 16 - v) <= tol
+    v, tol = exp["local_scale_bits_per_element_1d"]
+    assert abs(8 * r["scales_row"].nbytes / n - v) <= tol
+    sg = oracle.global_scale(oracle.amax(x))
+    cr, cc, s2 = oracle.quantize_2d(x, sg)
+    bits_2d = 8 * (cr.nbytes + s2.nbytes) / n
+    v, tol = exp["bits_per_element_2d"]
+    assert abs(bits_2d - v) <= tol and bits_2d == 4.03125
+    # the 32-bit tensor scale amortised over 1,024 values
+    v, tol = exp["tensor_scale_bits_at_1024_values"]
+    assert abs(32 / 1024 - v) <= tol
+    assert np.float32(sg).nbytes * 8 == 32
+
+
+# ----------------------------------------------- scale chain closed forms
+
+@pytest.mark.parametrize("maker", [
+    lambda: W.activation_small(),
+    lambda: W.activation(256, 512, seed=5),
+    lambda: W.weight(128, 256, seed=6),
+    lambda: W.gradient(128, 512, seed=7),
+])
+def test_amax_block_gets_top_scale(maker):
+    """The block holding the tensor amax has block scale 448 and its amax
+    element encodes to +-6 (S_g = amax/(448*6)); it reconstructs to the
+    amax within 2 ulp."""
+    x = maker()
+    xf = W.bf16_bits_to_f32(x)
+    a = oracle.amax(x)
+    assert a == np.max(np.abs(xf))
+    sg = oracle.global_scale(a)
+    codes, scales = oracle.quantize_1d_rows(x, sg)
+    r, c = np.unravel_index(np.argmax(np.abs(xf)), xf.shape)
+    assert scales[r, c // 16] == 0x7E
+    nib = (codes[r, c // 2] >> (4 * (c % 2))) & 15
+    assert nib & 7 == 7
+    assert (nib >> 3) == (1 if xf[r, c] < 0 else 0)
+    deq = oracle.dequantize(codes, scales, 1, sg, *x.shape)
+    assert abs(abs(deq[r, c]) - a) <= 2 * np.spacing(a)
+
+
+def test_rne_error_bound_and_saturation():
+    """Round trip: every element lands on the nearest grid point of its
+    block's unit d = s*S_g, except the ones above 6 units, which saturate."""
+    x = W.activation_small(64, 256, seed=3)
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    sg = oracle.global_scale(oracle.amax(x))
+    codes, scales = oracle.quantize_1d_rows(x, sg)
+    deq = oracle.dequantize(codes, scales, 1, sg, *x.shape).astype(np.float64)
+    s = np.array([[oracle.e4m3_decode(b) for b in row] for row in scales])
+    unit = np.repeat(s, 16, axis=1) * float(sg)
+    ratio = np.abs(xf) / unit
+    gaps = np.where(ratio < 2, 0.5, np.where(ratio < 4, 1.0, 2.0))
+    ok = ratio <= 6
+    err = np.abs(xf - deq)
+    # within half a grid gap (plus binary32 rounding of the products)
+    assert np.all(err[ok] <= 0.5 * gaps[ok] * unit[ok] * (1 + 1e-6) + 1e-30)
+    # saturated elements reconstruct to exactly 6 units
+    assert np.all(np.abs(np.abs(deq[~ok]) - 6 * unit[~ok]) <= 1e-6 * 6 * unit[~ok])
+    # saturation only happens when the E4M3 block scale rounded down
+    sat_blocks = np.unique(np.nonzero(~ok)[0] * 1000 + np.nonzero(~ok)[1] // 16)
+    for key in sat_blocks:
+        rr, bb = divmod(int(key), 1000)
+        b = np.max(np.abs(xf[rr, bb * 16:(bb + 1) * 16]))
+        assert s[rr, bb] * float(sg) * 6 < b
+
+
+# --------------------------------------------------------------- E2M1 RNE
+
+def _e2m1_rne_thresholds(v):
+    """Independent formulation: count the exact midpoints below v, strict or
+    not according to which neighbour has the even code."""
+    v = v.astype(np.float64)
+    m = ((v > 0.25).astype(int) + (v >= 0.75) + (v > 1.25) + (v >= 1.75) + (v > 2.5)
+         + (v >= 3.5) + (v > 5.0))
+    return np.where(np.isnan(v), 0, m).astype(np.uint8)
+
+
+def _fp32_neighbourhood(points, radius):
+    out = []
+    for p in points:
+        u = int(np.float32(p).view(np.uint32))
+        lo = max(0, u - radius)
+        out.append(np.arange(lo, u + radius + 1, dtype=np.uint64).astype(np.uint32))
+    return bits_to_f32(np.concatenate(out))
+
+
+def test_e2m1_rne_matches_exact_midpoints():
+    pts = [0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6, 6.5, 8]
+    v = _fp32_neighbourhood(pts, 1 << 14)
+    rng = np.random.default_rng(0)
+    v = np.concatenate([v, rng.uniform(0, 8, 1 << 20).astype(np.float32),
+                        bits_to_f32(np.arange(0, 1 << 16, dtype=np.uint32)),  # denormals
+                        np.array([np.inf, np.nan, 1e38, 2 ** -149], np.float32)])
+    got = oracle.e2m1_rne_array(v)
+    assert np.array_equal(got, _e2m1_rne_thresholds(v))
+
+
+def test_e2m1_rne_exact_rationals():
+    """A few hundred values checked against exact rational nearest-even."""
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([rng.uniform(0, 7, 300).astype(np.float32),
+                           np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)])
+    for v in vals:
+        fv = Fraction(float(v))
+        if fv >= 6:
+            want = 7
+        else:
+            d = [abs(fv - g) for g in GRID]
+            best = min(d)
+            cands = [k for k in range(8) if d[k] == best]
+            want = [k for k in cands if k % 2 == 0][0] if len(cands) > 1 else cands[0]
+        assert oracle.e2m1_rne(float(v)) == want, v
+
+
+def test_e2m1_grid_values_are_fixed_points():
+    for k, g in enumerate(GRID):
+        assert oracle.e2m1_rne(float(g)) == k
+        for h in (0, 1, 12345, 65535):
+            assert oracle.e2m1_sr(float(g), h) == k
+
+
+# ------------------------------------------------------------------ E4M3
+
+def test_e4m3_decode_matches_torch():
+    b = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = b.view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    for i in range(256):
+        got = oracle.e4m3_decode(i)
+        if math.isnan(ref[i]):
+            assert math.isnan(got)
+        else:
+            assert got == float(ref[i]) and math.copysign(1, got) == math.copysign(1, ref[i])
+
+
+def test_e4m3_encode_matches_torch_rne():
+    """torch's float32 -> float8_e4m3fn conversion rounds to nearest even;
+    below 464 it agrees with a saturating encoder."""
+    vals = [oracle.e4m3_decode(b) for b in range(0x7F)]
+    mids = [(vals[i] + vals[i + 1]) / 2 for i in range(len(vals) - 1)]
+    v = _fp32_neighbourhood(vals + mids, 300)
+    rng = np.random.default_rng(2)
+    v = np.concatenate([v, np.exp(rng.uniform(np.log(1e-6), np.log(463.9), 1 << 18)).astype(np.float32)])
+    v = v[(v >= 0) & (v < 464)]
+    got = oracle.e4m3_encode_array(v)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+    # saturation and NaN
+    assert np.all(oracle.e4m3_encode_array(np.array([448, 464, 1e9, np.inf], np.float32)) == 0x7E)
+    assert oracle.e4m3_encode(float("nan")) == 0x7F
+
+
+# ------------------------------------------------------------------- RHT
+
+def _sylvester(n):
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def test_hadamard_is_sylvester_and_orthogonal():
+    H = np.stack([oracle.rht16(np.eye(16, dtype=np.float32)[k], 0) for k in range(16)], axis=1) * 4
+    S = _sylvester(16)
+    assert np.array_equal(H, S)
+    assert np.array_equal(H @ H.T, 16 * np.eye(16))
+
+
+def test_rht_mask_is_a_sign_diagonal():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(16).astype(np.float32)
+    for mask in (0x0001, 0x8000, 0xA5C3, 0xFFFF):
+        d = np.array([-1 if (mask >> j) & 1 else 1 for j in range(16)], np.float32)
+        assert np.array_equal(oracle.rht16(x, mask), oracle.rht16(d * x, 0))
+
+
+def test_rht_within_1e6_of_fp64_dense():
+    """The binary32 butterfly against the dense double-precision product
+    (1/4) H16 D x, along axis 0 and axis 1, on gradient-shaped data."""
+    x = W.gradient(256, 512, seed=9)
+    mask = W.rht_sign_mask()
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    H = _sylvester(16) / 4.0
+    d = np.array([-1.0 if (mask >> j) & 1 else 1.0 for j in range(16)])
+    y0 = oracle.rht16_tensor(x, 0, mask).astype(np.float64)
+    ref0 = np.einsum("jk,rkc->rjc", H, (d[None, :, None] * xf.reshape(-1, 16, xf.shape[1]))).reshape(xf.shape)
+    assert np.linalg.norm(y0 - ref0) / np.linalg.norm(ref0) <= 1e-6
+    y1 = oracle.rht16_tensor(x, 1, mask).astype(np.float64)
+    ref1 = np.einsum("jk,rck->rcj", H, (d[None, None, :] * xf.reshape(xf.shape[0], -1, 16))).reshape(xf.shape)
+    assert np.linalg.norm(y1 - ref1) / np.linalg.norm(ref1) <= 1e-6
+    # amax of the transform is the max of its magnitudes
+    assert oracle.amax_rht(x, mask) == np.max(np.abs(oracle.rht16_tensor(x, 0, mask)))
+
+
+def test_rht_preserves_norm_and_dot_products():
+    """(1/4)H16 is orthonormal: norms are kept, and with the same mask the
+    rotation cancels inside the dot product (page "Melatih model dalam 4
+    bit", section "Empat pengaman")."""
+    a = W.gradient(64, 64, seed=12)
+    b = W.activation(64, 64, seed=13)
+    mask = 0x3C5A
+    ya = oracle.rht16_tensor(a, 0, mask).astype(np.float64)
+    yb = oracle.rht16_tensor(b, 0, mask).astype(np.float64)
+    af = W.bf16_bits_to_f32(a).astype(np.float64)
+    bf = W.bf16_bits_to_f32(b).astype(np.float64)
+    assert abs(np.linalg.norm(ya) - np.linalg.norm(af)) <= 1e-6 * np.linalg.norm(af)
+    dot = ya.T @ yb  # contraction over the transformed (token) axis
+    ref = af.T @ bf
+    assert np.linalg.norm(dot - ref) <= 1e-5 * np.linalg.norm(ref)
+
+
+# -------------------------------------------------------------------- SR
+
+def test_sr_counts_over_all_draws():
+    """Brute force over all 2^16 draws: the number that round up is exactly
+    ceil(p * 2^16) with p = (v - lo)/(hi - lo) taken in exact rationals."""
+    rng = np.random.default_rng(4)
+    vs = np.concatenate([rng.uniform(0, 6, 40).astype(np.float32),
+                         np.array([0.1, 0.2500001, 1.3, 2.9999998, 4.5, 5.9999995, 2 ** -140], np.float32)])
+    h = np.arange(1 << 16, dtype=np.uint16)
+    for v in vs:
+        codes = oracle.e2m1_sr_array(np.full(1 << 16, v, np.float32), h)
+        fv = Fraction(float(v))
+        lo = max(k for k in range(8) if GRID[k] <= fv)
+        p = (fv - GRID[lo]) / (GRID[lo + 1] - GRID[lo])
+        ups = int(np.count_nonzero(codes == lo + 1))
+        assert np.all((codes == lo) | (codes == lo + 1))
+        assert ups == math.ceil(p * (1 << 16)), (v, ups)
+        # so the mean over all draws is within one 2^-16 step of v
+        mean = (GRID[lo] * ((1 << 16) - ups) + GRID[lo + 1] * ups) / (1 << 16)
+        assert abs(mean - fv) <= (GRID[lo + 1] - GRID[lo]) / (1 << 16)
+
+
+def test_sr_unbiased_empirically_across_seeds():
+    """Mean over seeds of the stochastically rounded tensor approaches the
+    input where it does not saturate (pages: the expectation of the rounded
+    value equals the original); round-to-nearest does not."""
+    x = W.gradient(32, 64, seed=21)
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    sg = oracle.global_scale(oracle.amax(x))
+    n_seeds = 64
+    acc = np.zeros_like(xf)
+    for s in range(n_seeds):
+        c, sc = oracle.quantize_1d_rows(x, sg, sr=True, seed=1000 + s)
+        acc += oracle.dequantize(c, sc, 1, sg, *x.shape)
+    mean = acc / n_seeds
+    cr, scr = oracle.quantize_1d_rows(x, sg)
+    deq_rne = oracle.dequantize(cr, scr, 1, sg, *x.shape).astype(np.float64)
+    s = np.array([[oracle.e4m3_decode(b) for b in row] for row in scr])
+    unit = np.repeat(s, 16, axis=1) * float(sg)
+    ok = (np.abs(xf) < 6 * unit) & (unit > 0)
+    err = (mean - xf)[ok] / unit[ok]
+    # per-element rounding noise has std <= gap/2 <= 1 unit; average over seeds and elements
+    sigma = 1.0 / math.sqrt(n_seeds * err.size)
+    assert abs(err.mean()) < 5 * sigma
+    # small values: RNE sends everything below a quarter unit to zero, SR keeps the mass
+    small = ok & (np.abs(xf) < 0.25 * unit) & (np.abs(xf) > 0)
+    assert np.count_nonzero(small) > 50
+    assert np.all(deq_rne[small] == 0)
+    assert abs(np.sum(np.abs(mean[small])) / np.sum(np.abs(xf[small])) - 1) < 0.15
+
+
+# ---------------------------------------------------------------- Philox
+
+PHILOX_PIN_SRC = r"""
+#include <rocrand/rocrand_philox4x32_10.h>
+#include <cstdio>
+struct Expose : rocrand_device::philox4x32_10_engine {
+  uint4 run(uint4 c, uint2 k) { return ten_rounds(c, k); }
+};
+int main() {
+  Expose e;
+  unsigned a[6];
+  while (std::scanf("%x %x %x %x %x %x", &a[0], &a[1], &a[2], &a[3], &a[4], &a[5]) == 6) {
+    uint4 c = {a[0], a[1], a[2], a[3]};
+    uint2 k = {a[4], a[5]};
+    uint4 r = e.run(c, k);
+    std::printf("%08x %08x %08x %08x\n", r.x, r.y, r.z, r.w);
+  }
+  return 0;
+}
+"""
+
+
+def _rocrand_philox(inputs):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc) or not os.path.exists("/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"):
+        pytest.skip("rocRAND headers / hipcc not available: Philox parity unpinned here")
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "pin.cpp")
+        exe = os.path.join(d, "pin")
+        with open(src, "w") as f:
+            f.write(PHILOX_PIN_SRC)
+        subprocess.check_call([hipcc, "-x", "c++", "-O1", "-I/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
+                               src, "-o", exe], stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+        text = "\n".join(" ".join(f"{v:08x}" for v in row) for row in inputs) + "\n"
+        out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True).stdout
+    return [[int(t, 16) for t in line.split()] for line in out.strip().splitlines()]
+
+
+def test_philox_matches_rocrand():
+    rng = np.random.default_rng(5)
+    inputs = [[0] * 6, [0xFFFFFFFF] * 6, [1, 0, 0, 0, 42, 0], [0, 0, 1, 0, 42, 0]]
+    inputs += rng.integers(0, 1 << 32, size=(60, 6), dtype=np.uint64).tolist()
+    ref = _rocrand_philox(inputs)
+    for row, want in zip(inputs, ref):
+        got = oracle.philox4x32_10(row[:4], row[4:]).tolist()
+        assert got == want, row
+
+
+def test_sr_draws_uniform():
+    idx = np.arange(1 << 20, dtype=np.uint64)
+    h = oracle.sr_draw_array(42, idx)
+    counts = np.bincount(h >> 8, minlength=256)
+    expected = idx.size / 256
+    chi2 = np.sum((counts - expected) ** 2 / expected)
+    assert chi2 < 255 + 6 * math.sqrt(2 * 255)
+    # the draw of element i comes from call i/8, half (i mod 2) of word (i mod 8)/2
+    w = oracle.philox4x32_10([5, 0, 0, 0], [42, 0])
+    for j in range(8):
+        want = (int(w[j >> 1]) >> (16 * (j & 1))) & 0xFFFF
+        assert oracle.sr_draw(42, 40 + j) == want
+
+
+# ------------------------------------------------------ layouts and 2D
+
+def _unpack(codes):
+    lo = codes & 15
+    hi = codes >> 4
+    return np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
+
+
+def test_colwise_is_rowwise_of_transpose():
+    x = W.activation(96, 160, seed=14)
+    sg = oracle.global_scale(oracle.amax(x))
+    cc, sc = oracle.quantize_1d_cols(x, sg)
+    cr, sr = oracle.quantize_1d_rows(np.ascontiguousarray(x.T), sg)
+    assert np.array_equal(cc, cr) and np.array_equal(sc, sr)
+
+
+def test_sr_uses_flat_index_of_input():
+    x = W.gradient(32, 48, seed=15)
+    sg = oracle.global_scale(oracle.amax(x))
+    cc, sc = oracle.quantize_1d_cols(x, sg, sr=True, seed=42)
+    cr, srw = oracle.quantize_1d_rows(x, sg, sr=True, seed=42)
+    xf = W.bf16_bits_to_f32(x)
+    qc = _unpack(cc)  # [C][R]
+    qr = _unpack(cr)  # [R][C]
+    for (r, c) in [(0, 0), (5, 7), (17, 33), (31, 47)]:
+        i = r * x.shape[1] + c
+        h = oracle.sr_draw(42, i)
+        for q, sb in ((qc[c, r], sc[c, r // 16]), (qr[r, c], srw[r, c // 16])):
+            d = np.float32(oracle.e4m3_decode(int(sb))) * sg
+            rcp = np.float32(1.0) / d
+            v = np.float32(abs(xf[r, c])) * rcp
+            assert q & 7 == oracle.e2m1_sr(float(v), h)
+
+
+def test_2d_rowwise_and_colwise_codes_identical():
+    x = W.weight(64, 96, seed=16)
+    sg = oracle.global_scale(oracle.amax(x))
+    cr, cc, s = oracle.quantize_2d(x, sg)
+    assert np.array_equal(_unpack(cr).T, _unpack(cc))
+    assert s.shape == (4, 6)
+
+
+def test_2d_tile_indexing():
+    """Constant tiles with distinct magnitudes: the scale grid is ordered
+    like the tile values and every element sits at the top code."""
+    R, C = 48, 80
+    vals = np.arange(1, (R // 16) * (C // 16) + 1, dtype=np.float32).reshape(R // 16, C // 16)
+    vals = vals[:, ::-1] * np.float32(0.37)
+    xf = np.kron(vals, np.ones((16, 16), np.float32))
+    x = W.f32_to_bf16_bits(xf)
+    sg = oracle.global_scale(oracle.amax(x))
+    cr, cc, s = oracle.quantize_2d(x, sg)
+    order_vals = np.argsort(W.bf16_bits_to_f32(x)[::16, ::16].ravel(), kind="stable")
+    assert np.all(np.diff(s.ravel()[order_vals].astype(int)) >= 0)
+    q = _unpack(cr)
+    assert np.all(q >= 6)
+
+
+# ------------------------------------------------------------- edge cases
+
+def test_zero_and_signed_zero_tensor():
+    x = np.zeros((16, 32), np.uint16)
+    x[3, 5] = 0x8000  # -0
+    r = oracle.quantize_1d(x, rowwise=True, colwise=True)
+    assert r["amax"] == 0 and r["sg"] == 0
+    assert np.all(r["scales_row"] == 0) and np.all(r["scales_col"] == 0)
+    q = _unpack(r["codes_row"])
+    assert q[3, 5] == 8 and np.count_nonzero(q) == 1
+
+
+def test_denormal_inputs_are_defined():
+    x = np.arange(1, 1 + 16 * 32, dtype=np.uint16).reshape(16, 32)  # bf16 denormals
+    r = oracle.quantize_1d(x, rowwise=True, colwise=True)
+    assert r["amax"] > 0 and np.isfinite(r["sg"])
+    deq = oracle.dequantize(r["codes_row"], r["scales_row"], 1, r["sg"], 16, 32)
+    assert np.all(np.isfinite(deq))
+
+
+def test_nan_input_gives_nan_amax():
+    x = W.normal_tensor(16, 16, seed=1)
+    x[2, 3] = 0x7FC0
+    assert np.isnan(oracle.amax(x))
+
+
+# ------------------------------------------------------------------ GEMM
+
+def test_gemm_reference_tiny_bruteforce():
+    """The double reference equals the exact rational sum of decoded
+    operands (decoded here from the codebook fixture and torch's E4M3)."""
+    M, N, K = 16, 16, 32
+    a = W.normal_tensor(M, K, seed=30)
+    b = W.normal_tensor(N, K, seed=31, std=0.02)
+    sga = oracle.global_scale(oracle.amax(a))
+    sgb = oracle.global_scale(oracle.amax(b))
+    ca, sa = oracle.quantize_1d_rows(a, sga)
+    cb, _, sb = oracle.quantize_2d(b, sgb)
+    ref = oracle.gemm_rows(ca, sa, 1, sga, cb, sb, 2, sgb, M, N, K, np.arange(M))
+    mags = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+    e4 = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+    def val(codes, scales, mode, sg, r, k):
+        byte = codes[r, k // 2]
+        q = (byte >> (4 * (k % 2))) & 15
+        s = scales[r // 16, k // 16] if mode == 2 else scales[r, k // 16]
+        v = mags[q & 7] * Fraction(float(e4[s])) * Fraction(float(sg))
+        return -v if q & 8 else v
+
+    for m in (0, 7, 15):
+        for n in (0, 9, 15):
+            exact = sum(val(ca, sa, 1, sga, m, k) * val(cb, sb, 2, sgb, n, k) for k in range(K))
+            assert abs(float(exact) - ref[m, n]) <= 1e-12 * max(1.0, abs(float(exact)))
+
+
+def test_gemm_identity_operand():
+    """A = identity blocks (code 2 = 1.0 on the diagonal, unit scales):
+    the product reproduces the reconstructed B."""
+    K = N = 32
+    a_codes = np.zeros((K, K // 2), np.uint8)
+    for i in range(K):
+        a_codes[i, i // 2] |= 2 << (4 * (i % 2))
+    a_scales = np.full((K, K // 16), oracle.e4m3_encode(1.0), np.uint8)
+    b = W.weight(N, K, seed=32)
+    sgb = oracle.global_scale(oracle.amax(b))
+    cb, _, sb = oracle.quantize_2d(b, sgb)
+    c = oracle.gemm_rows(a_codes, a_scales, 1, 1.0, cb, sb, 2, sgb, K, N, K, np.arange(K))
+    bhat = oracle.dequantize_f64_rows(cb, sb, 2, sgb, N, K, np.arange(N))
+    assert np.array_equal(c, bhat.T)
