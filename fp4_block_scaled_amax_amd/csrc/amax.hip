@@ -1,0 +1,138 @@
+// Tensor-wide amax: integer maximum of |x| bit patterns, one atomic per
+// workgroup. Exact and independent of launch geometry.
+#include "device.h"
+#include "kernels.h"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ void amax_reset_kernel(uint32_t* out) { *out = 0u; }
+
+// Reduce a per-thread maximum (binary32 bits) over the workgroup and merge
+// it into *out.
+__device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* out)
+{
+    __shared__ uint32_t partial[kThreads / 64];
+    m = wave_max_u32(m);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0)
+        partial[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = partial[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w)
+            r = max(r, partial[w]);
+        atomicMax(out, r);
+    }
+}
+
+// bf16 [n]: 16-byte vectors, UNROLL loads in flight per thread.
+template <int UNROLL>
+__global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint4* __restrict__ x,
+                                                              int64_t nvec,
+                                                              const uint16_t* __restrict__ tail,
+                                                              int tail_n, uint32_t* __restrict__ out)
+{
+    uint32_t pm = 0u;  // two u16 maxima of |bf16| patterns
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + (UNROLL - 1) * stride < nvec; i += UNROLL * stride) {
+        uint4 v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            v[u] = load16(&x[i + u * stride]);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            pm = pk_max_u16(pm, v[u].x & 0x7FFF7FFFu);
+            pm = pk_max_u16(pm, v[u].y & 0x7FFF7FFFu);
+            pm = pk_max_u16(pm, v[u].z & 0x7FFF7FFFu);
+            pm = pk_max_u16(pm, v[u].w & 0x7FFF7FFFu);
+        }
+    }
+    for (; i < nvec; i += stride) {
+        uint4 v = load16(&x[i]);
+        pm = pk_max_u16(pm, v.x & 0x7FFF7FFFu);
+        pm = pk_max_u16(pm, v.y & 0x7FFF7FFFu);
+        pm = pk_max_u16(pm, v.z & 0x7FFF7FFFu);
+        pm = pk_max_u16(pm, v.w & 0x7FFF7FFFu);
+    }
+    uint32_t m = max(pm & 0xFFFFu, pm >> 16);
+    if (blockIdx.x == 0 && (int)threadIdx.x < tail_n)
+        m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7FFFu));
+    workgroup_max_to(m << 16, out);
+}
+
+// amax of the 16-point Hadamard transform along axis 0. Work item: 16 rows
+// x 8 columns (sixteen 16-byte loads), transformed per column in registers.
+__global__ __launch_bounds__(kThreads) void amax_rht_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t rows, int64_t cols,
+                                                             uint32_t mask,
+                                                             uint32_t* __restrict__ out)
+{
+    const int64_t groups = cols >> 3;
+    const int64_t items = (rows >> 4) * groups;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    uint32_t m = 0u;
+    for (int64_t it = (int64_t)blockIdx.x * kThreads + threadIdx.x; it < items; it += stride) {
+        const int64_t rb = it / groups, cg = it - rb * groups;
+        const uint16_t* base = x + (rb * 16) * cols + cg * 8;
+        uint4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            v[i] = load16(base + i * cols);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float z[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                z[i] = bf16_at(v[i], j);
+            rht16_inplace(z, mask);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                m = max(m, __float_as_uint(z[i]) & 0x7FFFFFFFu);
+        }
+    }
+    workgroup_max_to(m, out);
+}
+
+int grid_for(int64_t work_items, int per_block)
+{
+    int64_t g = (work_items + per_block - 1) / per_block;
+    if (g < 1)
+        g = 1;
+    if (g > 4096)
+        g = 4096;
+    return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t stream)
+{
+    uint32_t* out = reinterpret_cast<uint32_t*>(amax);
+    hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(1), 0, stream, out);
+    const int64_t nvec = n >> 3;
+    constexpr int kUnroll = 4;
+    const int grid = grid_for(nvec, kThreads * kUnroll);
+    hipLaunchKernelGGL((amax_bf16_kernel<kUnroll>), dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(x), nvec, x + nvec * 8, (int)(n & 7), out);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax_rht(const uint16_t* x, int64_t rows, int64_t cols, uint32_t mask, float* amax,
+                           hipStream_t stream)
+{
+    uint32_t* out = reinterpret_cast<uint32_t*>(amax);
+    hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(1), 0, stream, out);
+    const int64_t items = (rows >> 4) * (cols >> 3);
+    const int grid = grid_for(items, kThreads);
+    hipLaunchKernelGGL(amax_rht_kernel, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, mask,
+                       out);
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,218 @@
+// C ABI entry points: argument validation (before any HIP call), then the
+// launch. See include/nvfp4.h for the contract of each call.
+#include "../../include/nvfp4.h"
+#include "kernels.h"
+
+namespace {
+
+// Flat indices and byte offsets are int64; the SR counter takes i/8 in 64
+// bits. Keep every dimension product well inside int64.
+constexpr int64_t kMaxElements = (int64_t)1 << 46;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dims_ok(int64_t rows, int64_t cols)
+{
+    return rows > 0 && cols > 0 && rows <= kMaxElements && cols <= kMaxElements &&
+           rows <= kMaxElements / cols;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int status)
+{
+    switch (status) {
+    case NVFP4_OK:
+        return "ok";
+    case NVFP4_ERR_NULL:
+        return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE:
+        return "a dimension is not positive or not a multiple of the required granule";
+    case NVFP4_ERR_ALIGN:
+        return "a pointer is not 16-byte aligned";
+    case NVFP4_ERR_FLAGS:
+        return "unknown flag or mode, or an unsupported combination";
+    case NVFP4_ERR_HIP:
+        return "the HIP runtime refused a launch";
+    case NVFP4_ERR_SIZE:
+        return "a size exceeds the supported index range";
+    default:
+        return "unknown status";
+    }
+}
+
+int nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags, uint16_t rht_mask,
+               float* amax, hipStream_t stream)
+{
+    if (x == nullptr || amax == nullptr)
+        return NVFP4_ERR_NULL;
+    if ((flags & ~NVFP4_RHT) != 0)
+        return NVFP4_ERR_FLAGS;
+    if (rows <= 0 || cols <= 0)
+        return NVFP4_ERR_SHAPE;
+    if (!dims_ok(rows, cols))
+        return NVFP4_ERR_SIZE;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(amax) & 3u) != 0)
+        return NVFP4_ERR_ALIGN;
+    if (flags & NVFP4_RHT) {
+        if (rows % 16 != 0 || cols % 8 != 0)
+            return NVFP4_ERR_SHAPE;
+        return status_of(nvfp4::launch_amax_rht(x, rows, cols, rht_mask, amax, stream));
+    }
+    return status_of(nvfp4::launch_amax(x, rows * cols, amax, stream));
+}
+
+int nvfp4_quantize_1d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                      uint32_t flags, uint16_t rht_mask, uint64_t seed, uint8_t* codes_row,
+                      uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                      float* global_scale, hipStream_t stream)
+{
+    const uint32_t known = NVFP4_ROWWISE | NVFP4_COLWISE | NVFP4_SR | NVFP4_RHT;
+    if ((flags & ~known) != 0 || (flags & (NVFP4_ROWWISE | NVFP4_COLWISE)) == 0)
+        return NVFP4_ERR_FLAGS;
+    if ((flags & NVFP4_RHT) && ((flags & NVFP4_ROWWISE) || !(flags & NVFP4_COLWISE)))
+        return NVFP4_ERR_FLAGS;
+    const bool row = (flags & NVFP4_ROWWISE) != 0, col = (flags & NVFP4_COLWISE) != 0;
+    if (x == nullptr || amax == nullptr)
+        return NVFP4_ERR_NULL;
+    if (row && (codes_row == nullptr || scales_row == nullptr))
+        return NVFP4_ERR_NULL;
+    if (col && (codes_col == nullptr || scales_col == nullptr))
+        return NVFP4_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || rows % 16 != 0 || cols % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!dims_ok(rows, cols) || rows / 256 >= (1 << 20) || cols / 256 >= (1 << 20))
+        return NVFP4_ERR_SIZE;
+    if (!aligned16(x) || (row && (!aligned16(codes_row) || !aligned16(scales_row))) ||
+        (col && (!aligned16(codes_col) || !aligned16(scales_col))))
+        return NVFP4_ERR_ALIGN;
+    nvfp4::QuantizeArgs a{};
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.amax = amax;
+    a.mask = rht_mask;
+    a.seed = seed;
+    a.rowwise = row;
+    a.colwise = col;
+    a.two_d = false;
+    a.sr = (flags & NVFP4_SR) != 0;
+    a.rht = (flags & NVFP4_RHT) != 0;
+    a.codes_row = codes_row;
+    a.scales_row = scales_row;
+    a.codes_col = codes_col;
+    a.scales_col = scales_col;
+    a.global_scale = global_scale;
+    return status_of(nvfp4::launch_quantize(a, stream));
+}
+
+int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                      uint8_t* codes_row, uint8_t* codes_col, uint8_t* scales,
+                      float* global_scale, hipStream_t stream)
+{
+    if (x == nullptr || amax == nullptr || scales == nullptr ||
+        (codes_row == nullptr && codes_col == nullptr))
+        return NVFP4_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || rows % 16 != 0 || cols % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!dims_ok(rows, cols) || rows / 256 >= (1 << 20) || cols / 256 >= (1 << 20))
+        return NVFP4_ERR_SIZE;
+    if (!aligned16(x) || !aligned16(scales) || (codes_row && !aligned16(codes_row)) ||
+        (codes_col && !aligned16(codes_col)))
+        return NVFP4_ERR_ALIGN;
+    nvfp4::QuantizeArgs a{};
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.amax = amax;
+    a.rowwise = codes_row != nullptr;
+    a.colwise = codes_col != nullptr;
+    a.two_d = true;
+    a.codes_row = codes_row;
+    a.scales_row = scales;
+    a.codes_col = codes_col;
+    a.global_scale = global_scale;
+    return status_of(nvfp4::launch_quantize(a, stream));
+}
+
+int nvfp4_rht16(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint16_t rht_mask,
+                float* y, hipStream_t stream)
+{
+    if (x == nullptr || y == nullptr)
+        return NVFP4_ERR_NULL;
+    if (axis != 0 && axis != 1)
+        return NVFP4_ERR_FLAGS;
+    if (rows <= 0 || cols <= 0)
+        return NVFP4_ERR_SHAPE;
+    if (axis == 0 && (rows % 16 != 0 || cols % 8 != 0))
+        return NVFP4_ERR_SHAPE;
+    if (axis == 1 && cols % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!dims_ok(rows, cols))
+        return NVFP4_ERR_SIZE;
+    if (!aligned16(x) || !aligned16(y))
+        return NVFP4_ERR_ALIGN;
+    return status_of(nvfp4::launch_rht16(x, rows, cols, axis, rht_mask, y, stream));
+}
+
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int scale_mode,
+                     const float* global_scale, int64_t rows, int64_t cols, void* out,
+                     int out_dtype, hipStream_t stream)
+{
+    if (codes == nullptr || scales == nullptr || global_scale == nullptr || out == nullptr)
+        return NVFP4_ERR_NULL;
+    if ((scale_mode != NVFP4_SCALE_1D && scale_mode != NVFP4_SCALE_2D) ||
+        (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16))
+        return NVFP4_ERR_FLAGS;
+    if (rows <= 0 || cols <= 0 || rows % 16 != 0 || cols % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!dims_ok(rows, cols))
+        return NVFP4_ERR_SIZE;
+    if (!aligned16(codes) || !aligned16(out))
+        return NVFP4_ERR_ALIGN;
+    return status_of(nvfp4::launch_dequantize(codes, scales, scale_mode == NVFP4_SCALE_2D,
+                                              global_scale, rows, cols, out,
+                                              out_dtype == NVFP4_BF16, stream));
+}
+
+int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode,
+               const float* a_global_scale, const uint8_t* b_codes, const uint8_t* b_scales,
+               int b_scale_mode, const float* b_global_scale, void* c, int c_dtype, int64_t M,
+               int64_t N, int64_t K, hipStream_t stream)
+{
+    if (a_codes == nullptr || a_scales == nullptr || a_global_scale == nullptr ||
+        b_codes == nullptr || b_scales == nullptr || b_global_scale == nullptr || c == nullptr)
+        return NVFP4_ERR_NULL;
+    if ((a_scale_mode != NVFP4_SCALE_1D && a_scale_mode != NVFP4_SCALE_2D) ||
+        (b_scale_mode != NVFP4_SCALE_1D && b_scale_mode != NVFP4_SCALE_2D) ||
+        (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16))
+        return NVFP4_ERR_FLAGS;
+    if (M <= 0 || N <= 0 || K <= 0 || M % 16 != 0 || N % 16 != 0 || K % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N) || M / 128 >= 65535 ||
+        N / 128 >= (1 << 30))
+        return NVFP4_ERR_SIZE;
+    if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(c))
+        return NVFP4_ERR_ALIGN;
+    nvfp4::GemmArgs g{};
+    g.a_codes = a_codes;
+    g.a_scales = a_scales;
+    g.a_two_d = a_scale_mode == NVFP4_SCALE_2D;
+    g.a_sg = a_global_scale;
+    g.b_codes = b_codes;
+    g.b_scales = b_scales;
+    g.b_two_d = b_scale_mode == NVFP4_SCALE_2D;
+    g.b_sg = b_global_scale;
+    g.c = c;
+    g.c_bf16 = c_dtype == NVFP4_BF16;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    return status_of(nvfp4::launch_gemm(g, stream));
+}
+
+}  // extern "C"

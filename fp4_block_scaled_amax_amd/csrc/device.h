@@ -1,0 +1,235 @@
+// Device-side building blocks of the NVFP4 kernels (gfx950, wave64).
+//
+// Every floating-point step here is a single binary32 operation rounded to
+// nearest even (the library is compiled with -ffp-contract=off, IEEE
+// division and denormals on), so results are bit-identical to a scalar
+// evaluation of the same steps in the same order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// --------------------------------------------------------- vector memory
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load that streams past the caches (last use of the data).
+__device__ __forceinline__ uint4 load16_stream(const void* p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 load16(const void* p)
+{
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load8_stream(const void* p)
+{
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void store16_stream(void* p, uint4 v)
+{
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store16_stream(void* p, float4 v)
+{
+    __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t*>(p));
+}
+
+// ------------------------------------------------------------------ bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Element j (0..7) of a 16-byte vector of bf16 as binary32.
+__device__ __forceinline__ float bf16_at(const uint4& v, int j)
+{
+    uint32_t w = (j >> 1) == 0 ? v.x : (j >> 1) == 1 ? v.y : (j >> 1) == 2 ? v.z : v.w;
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+__device__ __forceinline__ uint32_t word_at(const uint4& v, int k)
+{
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// Packed max of two u16 lanes (|bf16| bit patterns; integer order of
+// non-negative floats is their numeric order).
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
+{
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 x = __builtin_bit_cast(u16x2, a);
+    u16x2 y = __builtin_bit_cast(u16x2, b);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+
+// ------------------------------------------------------------ E4M3 scale
+
+// Round a non-negative binary32 (or NaN) to E4M3, nearest even, with
+// subnormals; values >= 448 (and +inf) saturate to 448 (0x7E); NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3_encode(float v)
+{
+    if (!(v < 448.0f))
+        return (v != v) ? 0x7Fu : 0x7Eu;
+    if (v < 0.015625f)                                  // below 2^-6: multiples of 2^-9
+        return (uint32_t)__builtin_rintf(v * 512.0f);   // exact scaling, RNE
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFFu + ((u >> 20) & 1u);                    // RNE at mantissa bit 20
+    return (u >> 20) - (120u << 3);                      // rebias exponent 127 -> 7
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t b)
+{
+    uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (b == 0x7Fu)
+        return __uint_as_float(0x7FC00000u);
+    if (e == 0)
+        return (float)m * 0.001953125f;                  // m * 2^-9, exact
+    return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Per-block scale chain. b_bits: binary32 bits of the block's max |x|.
+// sg = amax / 2688, t = 6 * sg. Outputs the scale byte and the element
+// multiplier r = 1 / (s * sg) (0 when that unit is 0).
+struct BlockScale {
+    uint32_t byte;
+    float r;
+};
+
+__device__ __forceinline__ BlockScale block_scale(uint32_t b_bits, float sg, float t)
+{
+    float b = __uint_as_float(b_bits);
+    float s_f = (t == 0.0f) ? 0.0f : b / t;
+    BlockScale out;
+    out.byte = e4m3_encode(s_f);
+    float d = e4m3_decode(out.byte) * sg;
+    out.r = (d == 0.0f) ? 0.0f : 1.0f / d;
+    return out;
+}
+
+// ----------------------------------------------------------- E2M1 codes
+//
+// For a scaled magnitude v, the E2M1 grid has spacing 1/2 on [0, 2), 1 on
+// [2, 4) and 2 on [4, 6]. With j = clamp(exponent(v), 1, 3), v * 2^(2-j) is
+// exact and its integer part/rounding counts grid steps; adding
+// 2^23 + 2(j-1) + 8*sign in binary32 rounds to an integer (ties to even, and
+// the even offset keeps the parity) and leaves the 4-bit code in the low
+// bits of the result.
+
+__device__ __forceinline__ uint32_t e2m1_rne_nibble(float v, uint32_t sign8)
+{
+    v = fminf(fmaxf(v, 0.0f), 6.0f);                     // NaN -> 0, saturate at 6
+    int e = __builtin_amdgcn_frexp_expf(v);
+    int j = min(max(e, 1), 3);
+    float vs = __builtin_amdgcn_ldexpf(v, 2 - j);
+    float q = vs + __uint_as_float(0x4B000000u + 2u * (uint32_t)(j - 1) + sign8);
+    return __float_as_uint(q) & 0xFu;
+}
+
+// Stochastic rounding: round up with probability p = (v - lo)/(hi - lo),
+// decided as h < p * 2^16 for the element's 16-bit draw h.
+__device__ __forceinline__ uint32_t e2m1_sr_nibble(float v, uint32_t h16, uint32_t sign8)
+{
+    v = fminf(fmaxf(v, 0.0f), 6.0f);
+    int e = __builtin_amdgcn_frexp_expf(v);
+    int j = min(max(e, 1), 3);
+    float vs = __builtin_amdgcn_ldexpf(v, 2 - j);
+    float f = __builtin_floorf(vs);
+    float p = vs - f;                                    // exact, in [0, 1)
+    uint32_t up = ((float)h16 < p * 65536.0f) ? 1u : 0u;
+    float q = f + __uint_as_float(0x4B000000u + 2u * (uint32_t)(j - 1) + sign8);
+    return (__float_as_uint(q) + up) & 0xFu;
+}
+
+// ---------------------------------------------------- Philox4x32-10 draws
+//
+// Salmon et al., "Parallel random numbers: as easy as 1, 2, 3" (SC'11):
+// ten rounds of two 32x32->64 multiplies and xors, key bumped by the Weyl
+// constants between rounds. counter = (lo, hi, 0, 0).
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t ctr_lo, uint32_t ctr_hi, uint32_t k0,
+                                               uint32_t k1)
+{
+    uint32_t c0 = ctr_lo, c1 = ctr_hi, c2 = 0u, c3 = 0u;
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+    }
+    return make_uint4(c0, c1, c2, c3);
+}
+
+// The 8 draws of flat indices 8q .. 8q+7: draw k is half (k & 1) of word k/2.
+__device__ __forceinline__ uint32_t draw16(const uint4& w, int k)
+{
+    uint32_t word = word_at(w, k >> 1);
+    return (k & 1) ? (word >> 16) : (word & 0xFFFFu);
+}
+
+// ----------------------------------------------- 16-point Hadamard (FWHT)
+//
+// z_j = mask bit j ? -x_j : x_j; butterflies h = 1, 2, 4, 8 in natural
+// (Sylvester) order; y = z / 4.
+__device__ __forceinline__ void rht16_inplace(float (&z)[16], uint32_t mask)
+{
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        if ((mask >> j) & 1u)
+            z[j] = -z[j];
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j & h)
+                continue;
+            float a = z[j], b = z[j + h];
+            z[j] = a + b;
+            z[j + h] = a - b;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        z[j] = 0.25f * z[j];
+}
+
+// ------------------------------------------------------------ wave utils
+
+// Exchange with the neighbouring lane (lane ^ 1) through DPP quad_perm.
+__device__ __forceinline__ uint32_t swap_lane1(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float swap_lane1(float v)
+{
+    return __uint_as_float(swap_lane1(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+// Global amax -> (S_g, 6*S_g).
+__device__ __forceinline__ float global_scale_from_amax(float amax) { return amax / 2688.0f; }
+
+}  // namespace nvfp4

@@ -1,0 +1,51 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+// Arguments reaching these functions have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t stream);
+hipError_t launch_amax_rht(const uint16_t* x, int64_t rows, int64_t cols, uint32_t mask, float* amax,
+                           hipStream_t stream);
+
+struct QuantizeArgs {
+    const uint16_t* x;
+    int64_t rows, cols;
+    const float* amax;
+    uint32_t mask;
+    uint64_t seed;
+    bool rowwise, colwise, two_d, sr, rht;
+    uint8_t* codes_row;
+    uint8_t* scales_row;  // 1D rowwise scales, or the 2D tile scales
+    uint8_t* codes_col;
+    uint8_t* scales_col;
+    float* global_scale;  // optional
+};
+hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
+
+hipError_t launch_rht16(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint32_t mask,
+                        float* y, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool two_d,
+                             const float* global_scale, int64_t rows, int64_t cols, void* out,
+                             bool bf16_out, hipStream_t stream);
+
+struct GemmArgs {
+    const uint8_t* a_codes;
+    const uint8_t* a_scales;
+    bool a_two_d;
+    const float* a_sg;
+    const uint8_t* b_codes;
+    const uint8_t* b_scales;
+    bool b_two_d;
+    const float* b_sg;
+    void* c;
+    bool c_bf16;
+    int64_t M, N, K;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,190 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 quantization library.
+ *
+ * NVFP4 stores a tensor as 4-bit E2M1 codes (two per byte), one FP8 E4M3
+ * scale per block of 16 elements (1D) or per 16x16 tile (2D), and one FP32
+ * scale for the whole tensor; an element reconstructs as
+ *     x = e2m1(code) * e4m3(block scale) * global scale
+ * (page "NVFP4 Is a Scaling System, Not Just a 4-Bit Number", section "The
+ * smallest example"; page "Melatih model dalam 4 bit: pengaman numerik di
+ * balik NVFP4", section "Anatomi NVFP4").
+ *
+ * Conventions shared by every call:
+ *  - Tensors are row-major [rows][cols] with cols contiguous. bf16 inputs
+ *    are passed as their 16-bit patterns.
+ *  - All pointers are DEVICE pointers (hipMalloc / torch CUDA tensors)
+ *    owned by the caller. The library allocates nothing, keeps no state
+ *    between calls and is safe to call from several host threads.
+ *  - Every call is asynchronous on `stream` (0 = the null stream) and never
+ *    synchronises the host. Outputs are valid once the stream reaches them.
+ *  - Arguments are validated before any HIP call; a failed check returns a
+ *    negative status and launches nothing. Device pointers must be 16-byte
+ *    aligned.
+ *  - Packed codes: element 2k of a row of the output layout is the low
+ *    nibble of byte k, element 2k+1 the high nibble; a nibble is
+ *    (sign << 3) | magnitude code, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ *  - Scale layouts are compact row-major, no padding: 1D rowwise
+ *    [rows][cols/16], 1D columnwise [cols][rows/16], 2D [rows/16][cols/16].
+ *  - Non-finite inputs are not an error: the amax becomes Inf or NaN and
+ *    the outputs are well defined but meaningless.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define NVFP4_OK 0
+#define NVFP4_ERR_NULL (-1)  /* a required pointer is NULL                  */
+#define NVFP4_ERR_SHAPE (-2) /* a dimension is not positive / not a multiple */
+                             /* of 16 (or of the call's stated granule)      */
+#define NVFP4_ERR_ALIGN (-3) /* a pointer is not 16-byte aligned             */
+#define NVFP4_ERR_FLAGS (-4) /* unknown flag, mode or unsupported combination */
+#define NVFP4_ERR_HIP (-5)   /* the HIP runtime refused a launch             */
+#define NVFP4_ERR_SIZE (-6)  /* a size exceeds the supported index range     */
+
+/* ---- flags ----------------------------------------------------------- */
+#define NVFP4_ROWWISE 0x1u /* blocks of 16 consecutive elements along cols  */
+#define NVFP4_COLWISE 0x2u /* blocks of 16 consecutive rows of one column   */
+#define NVFP4_SR 0x4u      /* stochastic rounding (gradients) instead of RNE */
+#define NVFP4_RHT 0x8u     /* random-sign 16-point Hadamard along rows first */
+
+/* scale_mode values */
+#define NVFP4_SCALE_1D 1 /* one scale per 16 consecutive elements of a row */
+#define NVFP4_SCALE_2D 2 /* one scale per 16x16 tile                       */
+
+/* dtype values */
+#define NVFP4_F32 0
+#define NVFP4_BF16 1
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* nvfp4_status_string(int status);
+
+/*
+ * nvfp4_amax -- tensor-wide maximum absolute value (page "Melatih model
+ * dalam 4 bit", section "Anatomi NVFP4": the global scale is derived from
+ * the tensor amax; page "NVFP4 Is a Scaling System", section "The smallest
+ * example").
+ *   x        bf16 [rows][cols]
+ *   flags    0, or NVFP4_RHT: the amax of the Hadamard-transformed tensor
+ *            (16-row segments of every column, sign mask `rht_mask`), i.e.
+ *            of what nvfp4_rht16(axis 0) would produce.
+ *   amax     one float, written with the result (the call first resets it,
+ *            stream-ordered, then reduces into it).
+ * Shapes: rows, cols >= 1; with NVFP4_RHT rows must be a multiple of 16.
+ * The maximum is an integer maximum of |x| bit patterns, so it is exact and
+ * independent of launch geometry; a NaN input yields a NaN amax.
+ */
+int nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags, uint16_t rht_mask,
+               float* amax, hipStream_t stream);
+
+/*
+ * nvfp4_quantize_1d -- NVFP4 quantization with 16-element blocks
+ * (activations and gradients; page "NVFP4 Is a Scaling System", section "A
+ * format is not a training recipe").
+ *   x          bf16 [rows][cols]; rows and cols multiples of 16.
+ *   amax       device float from nvfp4_amax of the same tensor (with the
+ *              same NVFP4_RHT flag and mask when NVFP4_RHT is set).
+ *   flags      NVFP4_ROWWISE and/or NVFP4_COLWISE (at least one), plus
+ *              NVFP4_SR (stochastic rounding, page "MXFP4 和 NVFP4 的区别",
+ *              section "随机舍入") and/or NVFP4_RHT (page "Melatih model
+ *              dalam 4 bit", section "Empat pengaman": the transform is
+ *              applied to the column-quantized wgrad operands, so
+ *              NVFP4_RHT requires NVFP4_COLWISE and excludes NVFP4_ROWWISE).
+ *   rht_mask   bit j set = negate element j of every 16-row segment before
+ *              the transform (ignored without NVFP4_RHT).
+ *   seed       stochastic-rounding key; the draw of element (r, c) is a
+ *              pure function of (seed, r*cols + c) (Philox4x32-10, one call
+ *              per 8 consecutive flat indices, 16 bits per element), so
+ *              both layouts and any launch geometry see the same draws.
+ *   codes_row  [rows][cols/2]  (NULL unless ROWWISE)
+ *   scales_row [rows][cols/16] (NULL unless ROWWISE)
+ *   codes_col  [cols][rows/2]  (NULL unless COLWISE)
+ *   scales_col [cols][rows/16] (NULL unless COLWISE)
+ *   global_scale  optional (may be NULL): receives S_g = amax / 2688.
+ * Per block: s = e4m3_rne(b / (6*S_g)) with b the block's max |x| (after
+ * the transform with NVFP4_RHT); each element is |x| * (1 / (s*S_g))
+ * rounded to E2M1 (ties to even, saturating at 6) or stochastically.
+ */
+int nvfp4_quantize_1d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                      uint32_t flags, uint16_t rht_mask, uint64_t seed, uint8_t* codes_row,
+                      uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                      float* global_scale, hipStream_t stream);
+
+/*
+ * nvfp4_quantize_2d -- weight quantization with one E4M3 scale per 16x16
+ * tile, emitted in both layouts with identical codes (page "Melatih model
+ * dalam 4 bit", section "Empat pengaman", second safeguard: rowwise and
+ * columnwise quantized weights are numerically the same). Round to
+ * nearest even only.
+ *   x          bf16 [rows][cols]; rows and cols multiples of 16.
+ *   amax       device float from nvfp4_amax(x, flags 0).
+ *   codes_row  [rows][cols/2] or NULL;  codes_col [cols][rows/2] or NULL
+ *              (at least one non-NULL).
+ *   scales     [rows/16][cols/16] (required).
+ *   global_scale  optional (may be NULL).
+ */
+int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                      uint8_t* codes_row, uint8_t* codes_col, uint8_t* scales,
+                      float* global_scale, hipStream_t stream);
+
+/*
+ * nvfp4_rht16 -- standalone random-sign 16-point Hadamard transform
+ * y = (1/4) * H16 * D * x on every 16-element segment along `axis`
+ * (0: 16 consecutive rows of a column; 1: 16 consecutive elements of a
+ * row). H16 is the natural-order Sylvester matrix (page "MXFP4 和 NVFP4
+ * 的区别", sections "随机 Hadamard 变换" and "构造 Hadamard 矩阵的方法"),
+ * evaluated as the add/subtract butterfly in binary32; D negates element j
+ * when bit j of rht_mask is set.
+ *   x  bf16 [rows][cols];  y  float [rows][cols].
+ * The extent along `axis` must be a multiple of 16; the other >= 1 (cols a
+ * multiple of 8 for axis 0).
+ */
+int nvfp4_rht16(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint16_t rht_mask,
+                float* y, hipStream_t stream);
+
+/*
+ * nvfp4_dequantize -- x = e2m1(code) * e4m3(scale) * S_g (page "NVFP4 Is a
+ * Scaling System", section "The smallest example"), in binary32:
+ * fl(fl(e2m1*scale) * S_g) (the inner product is exact), converted to bf16
+ * by round-to-nearest-even when out_dtype is NVFP4_BF16.
+ *   codes         [rows][cols/2] packed codes of one layout
+ *   scales        [rows][cols/16] (NVFP4_SCALE_1D) or [rows/16][cols/16]
+ *                 (NVFP4_SCALE_2D)
+ *   global_scale  device float S_g
+ *   out           [rows][cols] of out_dtype
+ * rows and cols multiples of 16.
+ */
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int scale_mode,
+                     const float* global_scale, int64_t rows, int64_t cols, void* out,
+                     int out_dtype, hipStream_t stream);
+
+/*
+ * nvfp4_gemm -- C = A * B^T from packed NVFP4 operands (TN layout: both
+ * operands are K-contiguous, as the NVFP4 GEMM takes them; page "NVFP4 Is a
+ * Scaling System", section "“4-bit” is a payload count"): every operand
+ * element is decoded exactly (e2m1 * e4m3 fits bf16), products are summed
+ * in fp32 on the matrix cores, and the sum is multiplied by
+ * fl(S_gA * S_gB).
+ *   a_codes [M][K/2], a_scales per a_scale_mode over [M][K]
+ *   b_codes [N][K/2], b_scales per b_scale_mode over [N][K]
+ *   a_global_scale, b_global_scale: device floats
+ *   c       [M][N] of c_dtype (fp32 or bf16, round-to-nearest-even)
+ * M, N, K multiples of 16.
+ */
+int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode,
+               const float* a_global_scale, const uint8_t* b_codes, const uint8_t* b_scales,
+               int b_scale_mode, const float* b_global_scale, void* c, int c_dtype, int64_t M,
+               int64_t N, int64_t K, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

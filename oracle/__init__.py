@@ -68,6 +68,7 @@ def _load():
         ),
         "nvfp4_oracle_quantize_2d": (None, [P, I64, I64, F, I64, I64, P, P, P]),
         "nvfp4_oracle_dequantize": (None, [P, P, ctypes.c_int, F, I64, I64, I64, I64, P]),
+        "nvfp4_oracle_dequantize_bf16": (None, [P, P, ctypes.c_int, F, I64, I64, I64, I64, P]),
         "nvfp4_oracle_dequantize_f64_rows": (None, [P, P, ctypes.c_int, F, I64, I64, P, I64, P]),
         "nvfp4_oracle_e2m1_rne_array": (None, [P, I64, P]),
         "nvfp4_oracle_e2m1_sr_array": (None, [P, P, I64, P]),
@@ -241,6 +242,19 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, scale_mode: int, sg, R: in
     out = np.empty((r1 - r0, C), np.float32)
     _load().nvfp4_oracle_dequantize(_ptr(codes), _ptr(scales), scale_mode, float(sg), R, C, r0, r1,
                                     _ptr(out))
+    return out
+
+
+def dequantize_bf16(codes: np.ndarray, scales: np.ndarray, scale_mode: int, sg, R: int, C: int,
+                    r0: int = 0, r1=None) -> np.ndarray:
+    """bf16 bit patterns of the reconstruction (binary32 value rounded to
+    nearest even)."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    r1 = R if r1 is None else r1
+    out = np.empty((r1 - r0, C), np.uint16)
+    _load().nvfp4_oracle_dequantize_bf16(_ptr(codes), _ptr(scales), scale_mode, float(sg), R, C, r0,
+                                         r1, _ptr(out))
     return out
 
 

@@ -477,6 +477,39 @@ void nvfp4_oracle_dequantize(const uint8_t* codes, const uint8_t* scales, int sc
         }
 }
 
+/* bf16 output of the reconstruction: the binary32 value of
+ * nvfp4_oracle_dequantize rounded to bf16, nearest even. */
+static uint16_t float_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+void nvfp4_oracle_dequantize_bf16(const uint8_t* codes, const uint8_t* scales, int scale_mode,
+                                  float sg, int64_t R, int64_t C, int64_t r0, int64_t r1,
+                                  uint16_t* out)
+{
+    float tmp[16];
+    for (int64_t r = r0; r < r1; ++r)
+        for (int64_t c0 = 0; c0 < C; c0 += 16) {
+            for (int j = 0; j < 16; ++j) {
+                int64_t c = c0 + j;
+                uint8_t q = nibble(codes, r * C + c);
+                uint8_t sb = (scale_mode == 2) ? scales[(r / 16) * (C / 16) + c / 16]
+                                               : scales[r * (C / 16) + c / 16];
+                float g = (float)E2M1_MAGNITUDE[q & 7];
+                float s = (float)nvfp4_oracle_e4m3_decode(sb);
+                float mag = (g * s) * sg;
+                tmp[j] = (q & 8) ? -mag : mag;
+            }
+            for (int j = 0; j < 16; ++j)
+                out[(r - r0) * C + c0 + j] = float_to_bf16_rne(tmp[j]);
+        }
+    (void)R;
+}
+
 /* Reconstructed elements in double for the listed rows of a [R][C] operand
  * (exact: at most 6 significant bits times a binary32 global scale):
  * out[t][c] = e2m1(code) * e4m3(scale) * S_g. The contraction itself is

@@ -1,0 +1,381 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Codes, scale bytes, amax and global scales must match bit for bit; the
+Hadamard transform must match the oracle's binary32 butterfly bit for bit
+(and the dense double-precision transform within 1e-6 relative); the GEMM
+must satisfy ||C - C_ref||_F / ||C_ref||_F <= 1e-5 against the double
+reference on the dequantized operands.
+
+Small cases are compared in full; the full-size workloads (8192x4096
+activation, 14336x4096 weight, 8192x14336 gradient, the 8192x14336x4096
+product) are compared on sampled rows / columns / tiles that the oracle
+computes one by one, with the same launch configuration bench.py times.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+F = None
+
+
+def setup_module(module):
+    global F
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp4_block_scaled_amax_amd as pkg
+
+    pkg.lib()  # raises if the HIP library is missing: no fallback
+    F = pkg
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x_bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def f32_bits(a) -> int:
+    return int(np.float32(a).view(np.uint32))
+
+
+# ------------------------------------------------------------- workloads
+
+@functools.lru_cache(maxsize=None)
+def wl(name):
+    log(f"[workload] generating {name}")
+    if name == "act_small":
+        return W.activation_small()
+    if name == "act":
+        return W.activation()
+    if name == "weight":
+        return W.weight()
+    if name == "grad":
+        return W.gradient()
+    if name == "ragged_act":
+        return W.activation(272, 528, seed=101)
+    if name == "ragged_grad":
+        return W.gradient(304, 400, seed=102)
+    if name == "ragged_weight":
+        return W.weight(272, 400, seed=103)
+    raise KeyError(name)
+
+
+MASK = W.rht_sign_mask()
+SEED = W.SR_SEED
+
+
+def sample_idx(n, count, seed):
+    rng = np.random.default_rng(seed)
+    idx = set(rng.choice(n, size=min(count, n), replace=False).tolist())
+    idx.update([0, n - 1])
+    return sorted(idx)
+
+
+# ------------------------------------------------------------------ amax
+
+@pytest.mark.parametrize("name", ["act_small", "ragged_act", "act", "grad"])
+def test_amax(name):
+    x = wl(name)
+    log(f"[test_amax] {name} {x.shape}")
+    got = host(F.nvfp4_amax(dev(x)))[0]
+    assert f32_bits(got) == f32_bits(oracle.amax(x))
+
+
+def test_amax_odd_length_tail():
+    x = W.normal_tensor(13, 17, seed=5)  # 221 elements: 27 vectors + a 5-element tail
+    x[12, 16] = W.f32_to_bf16_bits(np.array([-77.0], np.float32))[0]
+    got = host(F.nvfp4_amax(dev(x)))[0]
+    assert got == 77.0 and f32_bits(got) == f32_bits(oracle.amax(x))
+
+
+@pytest.mark.parametrize("name", ["ragged_grad", "grad", "act"])
+def test_amax_rht(name):
+    x = wl(name)
+    log(f"[test_amax_rht] {name} {x.shape}")
+    got = host(F.nvfp4_amax(dev(x), rht=True, rht_mask=MASK))[0]
+    assert f32_bits(got) == f32_bits(oracle.amax_rht(x, MASK))
+
+
+# -------------------------------------------------------------- 1D quantize
+
+def run_q1(x, rowwise, colwise, sr=False, rht=False):
+    xd = dev(x)
+    a = F.nvfp4_amax(xd, rht=rht, rht_mask=MASK)
+    out = F.nvfp4_quantize_1d(xd, a, rowwise=rowwise, colwise=colwise, sr=sr, rht=rht,
+                              rht_mask=MASK, seed=SEED)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in out.items()}, host(a)[0]
+
+
+def check_q1(x, got, amax_gpu, rowwise, colwise, sr, rht, rows=None, cols=None):
+    amax = oracle.amax_rht(x, MASK) if rht else oracle.amax(x)
+    assert f32_bits(amax_gpu) == f32_bits(amax)
+    sg = oracle.global_scale(amax)
+    assert f32_bits(got["global_scale"][0]) == f32_bits(sg)
+    R, C = x.shape
+    if rowwise:
+        for r in (range(R) if rows is None else rows):
+            c, s = oracle.quantize_1d_rows(x, sg, sr, SEED, r, r + 1)
+            assert np.array_equal(got["codes_row"][r], c[0]), f"row codes differ at row {r}"
+            assert np.array_equal(got["scales_row"][r], s[0]), f"row scales differ at row {r}"
+    if colwise:
+        if cols is None:
+            c, s = oracle.quantize_1d_cols(x, sg, sr, SEED, rht, MASK)
+            bad = np.nonzero(np.any(got["codes_col"] != c, axis=1))[0]
+            assert bad.size == 0, f"column codes differ at columns {bad[:10]}"
+            assert np.array_equal(got["scales_col"], s)
+        else:
+            for col in cols:
+                c, s = oracle.quantize_1d_cols(x, sg, sr, SEED, rht, MASK, col, col + 1)
+                assert np.array_equal(got["codes_col"][col], c[0]), f"column codes differ at {col}"
+                assert np.array_equal(got["scales_col"][col], s[0]), f"column scales differ at {col}"
+
+
+CASES_SMALL = [
+    # (workload, rowwise, colwise, sr, rht)
+    ("act_small", True, False, False, False),
+    ("act_small", False, True, False, False),
+    ("act_small", True, True, False, False),
+    ("ragged_act", True, True, False, False),
+    ("ragged_act", True, False, True, False),
+    ("ragged_act", False, True, True, False),
+    ("ragged_act", True, True, True, False),
+    ("ragged_grad", False, True, True, True),
+    ("ragged_grad", False, True, False, True),
+    ("ragged_grad", True, True, True, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES_SMALL, ids=lambda c: "-".join(str(v) for v in c))
+def test_quantize_1d_small(case):
+    name, rowwise, colwise, sr, rht = case
+    x = wl(name)
+    log(f"[test_quantize_1d_small] {case} {x.shape}")
+    got, a = run_q1(x, rowwise, colwise, sr, rht)
+    check_q1(x, got, a, rowwise, colwise, sr, rht)
+
+
+def test_quantize_1d_full_activation_row_and_col():
+    """The 8192x4096 activation, rowwise + columnwise RNE in one call (the
+    benchmarked step), sampled rows and columns."""
+    x = wl("act")
+    log("[test_quantize_1d_full_activation_row_and_col]")
+    got, a = run_q1(x, True, True)
+    R, C = x.shape
+    check_q1(x, got, a, True, True, False, False, rows=sample_idx(R, 48, 1), cols=sample_idx(C, 48, 2))
+
+
+@pytest.mark.parametrize("name", ["grad", "act"])
+def test_quantize_1d_full_gradient_path(name):
+    """Hadamard + stochastic rounding, columnwise, seed 42 (wgrad operands)."""
+    x = wl(name)
+    log(f"[test_quantize_1d_full_gradient_path] {name}")
+    got, a = run_q1(x, False, True, sr=True, rht=True)
+    R, C = x.shape
+    check_q1(x, got, a, False, True, True, True, cols=sample_idx(C, 32, 3))
+
+
+def test_quantize_deterministic():
+    x = wl("ragged_grad")
+    g1, _ = run_q1(x, True, True, sr=True)
+    g2, _ = run_q1(x, True, True, sr=True)
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k])
+
+
+# ------------------------------------------------------------- edge cases
+
+def edge_tensors():
+    z = np.zeros((32, 48), np.uint16)
+    neg0 = z.copy()
+    neg0[5, 7] = 0x8000
+    denorm = (np.arange(32 * 48, dtype=np.uint32) % 120 + 1).astype(np.uint16).reshape(32, 48)
+    denorm[::3] |= 0x8000
+    tiny = W.f32_to_bf16_bits(W.bf16_bits_to_f32(W.normal_tensor(32, 48, 9)) * np.float32(1e-36))
+    withnan = W.normal_tensor(32, 48, 10)
+    withnan[7, 9] = 0x7FC1
+    withinf = W.normal_tensor(32, 48, 11)
+    withinf[3, 3] = 0xFF80
+    return {"zeros": z, "neg_zero": neg0, "denormals": denorm, "tiny": tiny, "nan": withnan,
+            "inf": withinf}
+
+
+@pytest.mark.parametrize("name", list(edge_tensors().keys()))
+@pytest.mark.parametrize("sr", [False, True])
+def test_edge_cases_1d(name, sr):
+    x = edge_tensors()[name]
+    log(f"[test_edge_cases_1d] {name} sr={sr}")
+    got, a = run_q1(x, True, True, sr=sr)
+    amax = oracle.amax(x)
+    if np.isnan(amax):
+        assert np.isnan(a)
+        sg = oracle.global_scale(amax)
+        c, s = oracle.quantize_1d_rows(x, sg, sr, SEED)
+        assert np.array_equal(got["codes_row"], c) and np.array_equal(got["scales_row"], s)
+        c, s = oracle.quantize_1d_cols(x, sg, sr, SEED)
+        assert np.array_equal(got["codes_col"], c) and np.array_equal(got["scales_col"], s)
+    else:
+        check_q1(x, got, a, True, True, sr, False)
+
+
+@pytest.mark.parametrize("name", ["zeros", "denormals", "tiny", "inf"])
+def test_edge_cases_rht(name):
+    x = edge_tensors()[name]
+    got, a = run_q1(x, False, True, sr=True, rht=True)
+    check_q1(x, got, a, False, True, True, True)
+
+
+# -------------------------------------------------------------------- 2D
+
+def run_q2(x):
+    xd = dev(x)
+    a = F.nvfp4_amax(xd)
+    out = F.nvfp4_quantize_2d(xd, a)
+    return {k: host(v) for k, v in out.items()}, host(a)[0]
+
+
+def test_quantize_2d_ragged_full_compare():
+    x = wl("ragged_weight")
+    got, a = run_q2(x)
+    sg = oracle.global_scale(oracle.amax(x))
+    assert f32_bits(a) == f32_bits(oracle.amax(x))
+    assert f32_bits(got["global_scale"][0]) == f32_bits(sg)
+    cr, cc, s = oracle.quantize_2d(x, sg)
+    assert np.array_equal(got["scales"], s)
+    assert np.array_equal(got["codes_row"], cr)
+    assert np.array_equal(got["codes_col"], cc)
+
+
+def test_quantize_2d_full_weight_sampled_tiles():
+    x = wl("weight")
+    log("[test_quantize_2d_full_weight_sampled_tiles]")
+    got, a = run_q2(x)
+    amax = oracle.amax(x)
+    assert f32_bits(a) == f32_bits(amax)
+    sg = oracle.global_scale(amax)
+    R, C = x.shape
+    for tr in sample_idx(R // 16, 24, 4):
+        cr, cc, s = oracle.quantize_2d(x, sg, tr, tr + 1)
+        assert np.array_equal(got["scales"][tr], s[tr])
+        rs = slice(tr * 16, tr * 16 + 16)
+        assert np.array_equal(got["codes_row"][rs], cr[rs])
+        assert np.array_equal(got["codes_col"][:, tr * 8:tr * 8 + 8], cc[:, tr * 8:tr * 8 + 8])
+
+
+def test_quantize_2d_single_layout_outputs():
+    x = wl("ragged_weight")
+    xd = dev(x)
+    a = F.nvfp4_amax(xd)
+    both = F.nvfp4_quantize_2d(xd, a)
+    rows_only = F.nvfp4_quantize_2d(xd, a, rowwise=True, colwise=False)
+    cols_only = F.nvfp4_quantize_2d(xd, a, rowwise=False, colwise=True)
+    assert torch.equal(both["codes_row"], rows_only["codes_row"])
+    assert torch.equal(both["codes_col"], cols_only["codes_col"])
+    assert torch.equal(both["scales"], cols_only["scales"])
+
+
+# ------------------------------------------------------------------- RHT
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("name", ["ragged_grad", "act_small"])
+def test_rht16_standalone(name, axis):
+    x = wl(name)
+    y = host(F.nvfp4_rht16(dev(x), axis=axis, rht_mask=MASK))
+    ref = oracle.rht16_tensor(x, axis, MASK)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+    # against the dense double-precision transform
+    H = np.array([[(-1) ** bin(j & k).count("1") for k in range(16)] for j in range(16)], float) / 4
+    d = np.array([-1.0 if (MASK >> j) & 1 else 1.0 for j in range(16)])
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    if axis == 0:
+        dense = np.einsum("jk,rkc->rjc", H, d[None, :, None] * xf.reshape(-1, 16, xf.shape[1])).reshape(xf.shape)
+    else:
+        dense = np.einsum("jk,rck->rcj", H, d[None, None, :] * xf.reshape(xf.shape[0], -1, 16)).reshape(xf.shape)
+    assert np.linalg.norm(y - dense) / np.linalg.norm(dense) <= 1e-6
+
+
+# ------------------------------------------------------------ dequantize
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_dequantize(mode):
+    x = wl("ragged_weight") if mode == 2 else wl("ragged_act")
+    xd = dev(x)
+    a = F.nvfp4_amax(xd)
+    R, C = x.shape
+    if mode == 2:
+        q = F.nvfp4_quantize_2d(xd, a, colwise=False)
+        codes, scales = q["codes_row"], q["scales"]
+    else:
+        q = F.nvfp4_quantize_1d(xd, a)
+        codes, scales = q["codes_row"], q["scales_row"]
+    sg = q["global_scale"]
+    y32 = host(F.nvfp4_dequantize(codes, scales, mode, sg, R, C))
+    y16 = host(F.nvfp4_dequantize(codes, scales, mode, sg, R, C, out_dtype=torch.bfloat16).view(torch.int16))
+    ref = oracle.dequantize(host(codes), host(scales), mode, host(sg)[0], R, C)
+    assert np.array_equal(y32.view(np.uint32), ref.view(np.uint32))
+    ref16 = oracle.dequantize_bf16(host(codes), host(scales), mode, host(sg)[0], R, C)
+    assert np.array_equal(y16.view(np.uint16), ref16)
+
+
+# ------------------------------------------------------------------- GEMM
+
+def quantized_operands(a_bits, b_bits):
+    ad, bd = dev(a_bits), dev(b_bits)
+    qa = F.nvfp4_quantize_1d(ad, F.nvfp4_amax(ad))
+    qb = F.nvfp4_quantize_2d(bd, F.nvfp4_amax(bd), colwise=False)
+    return qa, qb
+
+
+def gemm_check(a_bits, b_bits, rows, out_dtype=torch.float32):
+    M, K = a_bits.shape
+    N = b_bits.shape[0]
+    qa, qb = quantized_operands(a_bits, b_bits)
+    c = F.nvfp4_gemm(qa["codes_row"], qa["scales_row"], 1, qa["global_scale"], qb["codes_row"],
+                     qb["scales"], 2, qb["global_scale"], M, N, K, out_dtype=out_dtype)
+    c = host(c.float() if out_dtype == torch.bfloat16 else c)
+    ref = oracle.gemm_rows(host(qa["codes_row"]), host(qa["scales_row"]), 1, host(qa["global_scale"])[0],
+                           host(qb["codes_row"]), host(qb["scales"]), 2, host(qb["global_scale"])[0],
+                           M, N, K, np.asarray(rows, np.int64))
+    got = c[np.asarray(rows)].astype(np.float64)
+    return np.linalg.norm(got - ref) / np.linalg.norm(ref), c
+
+
+def test_gemm_ragged_full():
+    a = W.normal_tensor(272, 528, seed=40)
+    b = W.normal_tensor(400, 528, seed=41, std=0.02)
+    err, _ = gemm_check(a, b, np.arange(272))
+    assert err <= 1e-5
+
+
+def test_gemm_full_size_sampled_rows():
+    log("[test_gemm_full_size_sampled_rows] generating 8192x4096 and 14336x4096 operands")
+    a, b = W.gemm_operands()
+    rows = W.gemm_sample_rows()
+    err, c32 = gemm_check(a, b, rows)
+    log(f"[test_gemm_full_size_sampled_rows] rel_fro={err:.3e}")
+    assert err <= 1e-5
+
+
+def test_gemm_bf16_output_is_rounded_fp32():
+    a = W.normal_tensor(272, 528, seed=42)
+    b = W.normal_tensor(400, 528, seed=43, std=0.02)
+    _, c32 = gemm_check(a, b, np.arange(16))
+    err16, c16 = gemm_check(a, b, np.arange(272), out_dtype=torch.bfloat16)
+    assert np.array_equal(W.f32_to_bf16_bits(c32), W.f32_to_bf16_bits(c16))
+    assert err16 <= 2.0 ** -8

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/nvfp4.h declares,
+and reject bad arguments with the documented status codes before making any
+HIP call (so these run on a machine without a GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_block_scaled_amax_amd as F
+from fp4_block_scaled_amax_amd import build as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = ctypes.c_void_p
+A = P(4096)  # a 16-byte aligned, never dereferenced stand-in pointer
+MIS = P(4097)
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    if B.is_stale():
+        B.build()
+    return F.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(F.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in F.STATUS:
+        s = F.nvfp4_status_string(code)
+        assert isinstance(s, str) and s
+    assert F.nvfp4_status_string(12345) == "unknown status"
+
+
+def test_amax_validation(L):
+    assert L.nvfp4_amax(NULL, 16, 16, 0, 0, A, NULL) == -1
+    assert L.nvfp4_amax(A, 16, 16, 0, 0, NULL, NULL) == -1
+    assert L.nvfp4_amax(A, 0, 16, 0, 0, A, NULL) == -2
+    assert L.nvfp4_amax(A, 16, -1, 0, 0, A, NULL) == -2
+    assert L.nvfp4_amax(A, 16, 16, 0x80, 0, A, NULL) == -4
+    assert L.nvfp4_amax(MIS, 16, 16, 0, 0, A, NULL) == -3
+    assert L.nvfp4_amax(A, 24, 16, F.RHT, 0, A, NULL) == -2  # rows not a multiple of 16
+    assert L.nvfp4_amax(A, 1 << 40, 1 << 40, 0, 0, A, NULL) == -6
+
+
+def q1(L, x=A, rows=64, cols=64, amax=A, flags=F.ROWWISE, cr=A, sr_=A, cc=A, sc=A):
+    return L.nvfp4_quantize_1d(x, rows, cols, amax, flags, 0, 0, cr, sr_, cc, sc, NULL, NULL)
+
+
+def test_quantize_1d_validation(L):
+    assert q1(L, flags=0) == -4
+    assert q1(L, flags=0x40 | F.ROWWISE) == -4
+    assert q1(L, flags=F.RHT | F.ROWWISE | F.COLWISE) == -4  # RHT is columnwise only
+    assert q1(L, flags=F.RHT | F.ROWWISE) == -4
+    assert q1(L, x=NULL) == -1
+    assert q1(L, amax=NULL) == -1
+    assert q1(L, cr=NULL) == -1
+    assert q1(L, flags=F.COLWISE, sc=NULL) == -1
+    assert q1(L, rows=24) == -2
+    assert q1(L, cols=8) == -2
+    assert q1(L, rows=0) == -2
+    assert q1(L, x=MIS) == -3
+    assert q1(L, flags=F.COLWISE, cc=MIS) == -3
+    assert q1(L, rows=1 << 40, cols=1 << 40) == -6
+
+
+def test_quantize_2d_validation(L):
+    assert L.nvfp4_quantize_2d(A, 32, 32, A, NULL, NULL, A, NULL, NULL) == -1
+    assert L.nvfp4_quantize_2d(A, 32, 32, A, A, A, NULL, NULL, NULL) == -1
+    assert L.nvfp4_quantize_2d(A, 40, 32, A, A, A, A, NULL, NULL) == -2
+    assert L.nvfp4_quantize_2d(A, 32, 32, A, MIS, A, A, NULL, NULL) == -3
+
+
+def test_rht_dequant_gemm_validation(L):
+    assert L.nvfp4_rht16(A, 32, 32, 2, 0, A, NULL) == -4
+    assert L.nvfp4_rht16(A, 24, 32, 0, 0, A, NULL) == -2
+    assert L.nvfp4_rht16(A, 24, 24, 1, 0, A, NULL) == -2
+    assert L.nvfp4_rht16(A, 32, 32, 0, 0, MIS, NULL) == -3
+    assert L.nvfp4_dequantize(A, A, 3, A, 32, 32, A, 0, NULL) == -4
+    assert L.nvfp4_dequantize(A, A, 1, A, 32, 32, A, 7, NULL) == -4
+    assert L.nvfp4_dequantize(A, A, 1, NULL, 32, 32, A, 0, NULL) == -1
+    assert L.nvfp4_dequantize(A, A, 1, A, 33, 32, A, 0, NULL) == -2
+    g = lambda **k: L.nvfp4_gemm(k.get("ac", A), A, k.get("am", 1), A, A, A, k.get("bm", 2), A,
+                                 k.get("c", A), k.get("dt", 0), k.get("M", 32), k.get("N", 32),
+                                 k.get("K", 32), NULL)
+    assert g(ac=NULL) == -1
+    assert g(am=0) == -4
+    assert g(dt=3) == -4
+    assert g(K=24) == -2
+    assert g(M=0) == -2
+    assert g(c=MIS) == -3
+
+
+def test_oracle_is_not_reachable_from_product():
+    """The product package never imports or links the oracle."""
+    pkg = os.path.join(ROOT, "fp4_block_scaled_amax_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
