@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""NVFP4 quantization benchmark on one MI355X.
+
+Timed step (the workload the metric is quoted on): the 8192x4096 bf16
+activation (tokens x hidden, N(0,1) with 8 outlier columns x100) goes
+through the whole 1D path -- tensor amax, global scale, E4M3 block scales,
+E2M1 round-to-nearest-even and packing -- emitting both the rowwise (fprop)
+and the columnwise (wgrad) layouts in one launch. `value` is the step's
+algorithmic bytes (2 B/element for the amax read, 2 B/element for the
+quantize read, 2 x 0.5625 B/element for the two outputs) per second.
+
+The other rows of the path are timed in the same run, each on its own
+workload, and reported under "rows": the Hadamard + stochastic-rounding
+gradient quantization (8192x14336 gradient and the activation), the 2D
+weight quantization (14336x4096), the standalone transform, dequantization
+and the dequantize-and-contract GEMM (8192x14336x4096, TFLOP/s).
+
+Prints one JSON line. Inputs are synthetic (seeded), resident in HBM before
+timing starts; the timed loop rotates over input copies whose total exceeds
+the 256 MB Infinity Cache, so each step reads its input from HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+# Plain vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one op per lane
+# per clock, no packed math).
+VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
+
+METRIC = "NVFP4 quantize GB/s & % of HBM peak; NVFP4 dequant-GEMM TFLOP/s"
+PROFILE_PMC = os.path.join(ROOT, "profiles", "quantize_rowcol_activation_8192x4096_traffic.md")
+DOMINANT_SOURCES = [
+    os.path.join(ROOT, "fp4_block_scaled_amax_amd", "csrc", "quantize.hip"),
+    os.path.join(ROOT, "fp4_block_scaled_amax_amd", "csrc", "device.h"),
+]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=5, help="input copies rotated in the timed loop")
+    p.add_argument("--no-rows", action="store_true", help="skip the secondary per-row measurements")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--row-iters", type=int, default=10)
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 256 MiB device copy (counter calibration)")
+    p.add_argument("--cpu-rows", type=int, default=8192,
+                   help="rows of the activation in the CPU baseline sample")
+    return p.parse_args()
+
+
+def sources_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed
+    counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    text = open(PROFILE_PMC).read()
+    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != sources_digest(DOMINANT_SOURCES):
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp4_block_scaled_amax_amd as F
+    import workloads as W
+
+    F.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+
+    # ---------------------------------------------------------- timed step
+    R, C = 8192, 4096
+    n = R * C
+    log("[bench] generating the 8192x4096 activation")
+    x_host = W.activation(R, C)
+    xs = [to_dev(x_host) for _ in range(args.copies)]
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    outs = []
+    for _ in range(args.copies):
+        outs.append({
+            "codes_row": torch.empty((R, C // 2), dtype=torch.uint8, device=dev),
+            "scales_row": torch.empty((R, C // 16), dtype=torch.uint8, device=dev),
+            "codes_col": torch.empty((C, R // 2), dtype=torch.uint8, device=dev),
+            "scales_col": torch.empty((C, R // 16), dtype=torch.uint8, device=dev),
+            "global_scale": torch.empty(1, dtype=torch.float32, device=dev),
+        })
+    step_bytes = n * (2 + 2 + 2 * (0.5 + 1 / 16))
+    quant_bytes = n * (2 + 2 * (0.5 + 1 / 16))
+
+    ev_q0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_q1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(k, timed):
+        x = xs[k % args.copies]
+        o = outs[k % args.copies]
+        F.nvfp4_amax(x, out=amax)
+        if timed:
+            ev_q0[k].record(stream)
+        F.nvfp4_quantize_1d(x, amax, rowwise=True, colwise=True, out=o)
+        if timed:
+            ev_q1[k].record(stream)
+
+    if args.calib_copy:
+        # A plain copy of known size: reads and writes 256 MiB each. Hardware
+        # byte counters of the dominant kernel are scaled by what they read here.
+        src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for k in range(args.warmup):
+        step(k, False)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = step_bytes / (elapsed / args.steps) / 1e9
+    q_ms = [ev_q0[k].elapsed_time(ev_q1[k]) for k in range(args.steps)]
+    q_avg_ms = sum(q_ms) / len(q_ms)
+    achieved = quant_bytes / (q_avg_ms * 1e-3) / 1e9
+    traffic = recorded_traffic()
+    roofline = {
+        "kernel": "quantize_kernel<rowwise+colwise, RNE> on 8192x4096",
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "avg_launch_us": round(q_avg_ms * 1e3, 2),
+        "alg_bytes_per_launch": quant_bytes,
+    }
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s; quantize {q_avg_ms * 1e3:.1f} us "
+        f"= {achieved:.0f} GB/s")
+
+    # ------------------------------------------------------ secondary rows
+    rows = {}
+    gemm_tflops = None
+    if not args.no_rows:
+        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+
+        def timed(fn, iters=args.row_iters):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(iters):
+                flush.zero_()  # evict the Infinity Cache between launches
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            return statistics.median(ts)
+
+        def row_hbm(name, us, nbytes, shape, note=None):
+            gbs = nbytes / (us * 1e-6) / 1e9
+            rows[name] = {"shape": shape, "us": round(us, 2), "alg_bytes": nbytes,
+                          "GB/s": round(gbs, 1), "bound": "hbm", "peak": HBM_PEAK_GBS,
+                          "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            if note:
+                rows[name]["note"] = note
+            log(f"[bench] {name}: {us:.1f} us {gbs:.0f} GB/s")
+
+        x = xs[0]
+        n_x = R * C
+        row_hbm("amax_activation", timed(lambda: F.nvfp4_amax(x, out=amax)), 2 * n_x, [R, C])
+        o = outs[0]
+        row_hbm("quantize_1d_rowwise_rne_activation",
+                timed(lambda: F.nvfp4_quantize_1d(x, amax, rowwise=True, colwise=False, out=o)),
+                n_x * 2.5625, [R, C])
+        row_hbm("quantize_1d_colwise_rne_activation",
+                timed(lambda: F.nvfp4_quantize_1d(x, amax, rowwise=False, colwise=True, out=o)),
+                n_x * 2.5625, [R, C])
+        row_hbm("quantize_1d_row_and_col_rne_activation",
+                timed(lambda: F.nvfp4_quantize_1d(x, amax, rowwise=True, colwise=True, out=o)),
+                n_x * 3.125, [R, C])
+        mask = W.rht_sign_mask()
+        a_rht = torch.empty(1, dtype=torch.float32, device=dev)
+        row_hbm("amax_rht_activation", timed(lambda: F.nvfp4_amax(x, rht=True, rht_mask=mask, out=a_rht)),
+                2 * n_x, [R, C])
+        row_hbm("quantize_colwise_rht_sr_activation",
+                timed(lambda: F.nvfp4_quantize_1d(x, a_rht, rowwise=False, colwise=True, sr=True, rht=True,
+                                                  rht_mask=mask, seed=W.SR_SEED, out=o)),
+                n_x * 2.5625, [R, C])
+        deq = torch.empty((R, C), dtype=torch.float32, device=dev)
+        F.nvfp4_quantize_1d(x, amax, rowwise=True, colwise=False, out=o)
+        row_hbm("dequantize_1d_fp32_activation",
+                timed(lambda: F.nvfp4_dequantize(o["codes_row"], o["scales_row"], 1, o["global_scale"], R, C,
+                                                 out=deq)), n_x * 4.5625, [R, C])
+        deq16 = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+        row_hbm("dequantize_1d_bf16_activation",
+                timed(lambda: F.nvfp4_dequantize(o["codes_row"], o["scales_row"], 1, o["global_scale"], R, C,
+                                                 out_dtype=torch.bfloat16, out=deq16)), n_x * 2.5625, [R, C])
+        del xs[1:], outs[1:], deq, deq16
+
+        log("[bench] generating the 8192x14336 gradient")
+        g_host = W.gradient()
+        g = to_dev(g_host)
+        del g_host
+        GR, GC = g.shape
+        n_g = GR * GC
+        row_hbm("amax_rht_gradient", timed(lambda: F.nvfp4_amax(g, rht=True, rht_mask=mask, out=a_rht)),
+                2 * n_g, [GR, GC])
+        og = {}
+        og = F.nvfp4_quantize_1d(g, a_rht, rowwise=False, colwise=True, sr=True, rht=True, rht_mask=mask,
+                                 seed=W.SR_SEED)
+        row_hbm("quantize_colwise_rht_sr_gradient",
+                timed(lambda: F.nvfp4_quantize_1d(g, a_rht, rowwise=False, colwise=True, sr=True, rht=True,
+                                                  rht_mask=mask, seed=W.SR_SEED, out=og)),
+                n_g * 2.5625, [GR, GC])
+        y = torch.empty((GR, GC), dtype=torch.float32, device=dev)
+        row_hbm("rht16_axis0_gradient", timed(lambda: F.nvfp4_rht16(g, axis=0, rht_mask=mask, out=y)),
+                n_g * 6, [GR, GC])
+        del y, og, g
+
+        log("[bench] generating the 14336x4096 weight")
+        w = to_dev(W.weight())
+        WR, WC = w.shape
+        n_w = WR * WC
+        a_w = F.nvfp4_amax(w)
+        ow = F.nvfp4_quantize_2d(w, a_w)
+        row_hbm("amax_weight", timed(lambda: F.nvfp4_amax(w, out=a_w)), 2 * n_w, [WR, WC])
+        row_hbm("quantize_2d_weight", timed(lambda: F.nvfp4_quantize_2d(w, a_w, out=ow)),
+                n_w * (2 + 2 * 0.5 + 1 / 256), [WR, WC])
+
+        log("[bench] GEMM 8192x14336x4096")
+        a_host, b_host = W.gemm_operands()
+        A = to_dev(a_host)
+        Bm = to_dev(b_host)
+        del a_host, b_host
+        qa = F.nvfp4_quantize_1d(A, F.nvfp4_amax(A))
+        qb = F.nvfp4_quantize_2d(Bm, F.nvfp4_amax(Bm), colwise=False)
+        M, N, K = 8192, 14336, 4096
+        c32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+        c16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        flop = 2.0 * M * N * K
+        for name, cc, dt in (("gemm_fp32_out", c32, torch.float32), ("gemm_bf16_out", c16, torch.bfloat16)):
+            us = timed(lambda: F.nvfp4_gemm(qa["codes_row"], qa["scales_row"], 1, qa["global_scale"],
+                                            qb["codes_row"], qb["scales"], 2, qb["global_scale"], M, N, K,
+                                            out_dtype=dt, out=cc), iters=max(3, args.row_iters // 2))
+            tf = flop / (us * 1e-6) / 1e12
+            rows[name] = {"shape": [M, N, K], "us": round(us, 1), "flop": flop, "TFLOP/s": round(tf, 1),
+                          "bound": "mfma", "peak": BF16_MFMA_PEAK_TFLOPS,
+                          "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+            log(f"[bench] {name}: {us:.0f} us {tf:.1f} TFLOP/s")
+        gemm_tflops = rows["gemm_fp32_out"]["TFLOP/s"]
+        del flush
+
+    # -------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        sample = np.ascontiguousarray(x_host[: args.cpu_rows])
+        log(f"[bench] CPU oracle on the first {args.cpu_rows} rows")
+        t0 = time.perf_counter()
+        oracle.quantize_1d(sample, rowwise=True, colwise=True)
+        t_cpu = time.perf_counter() - t0
+        ns = sample.size
+        cpu = {"value": round(ns * (2 + 2 + 2 * 0.5625) / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"first {args.cpu_rows} rows of the activation ({args.cpu_rows}x{C}), amax + rowwise "
+                         f"+ columnwise 1D RNE quantize as one tensor; {t_cpu:.1f} s single-threaded",
+               "seconds": round(t_cpu, 2)}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "activation 8192x4096 bf16, N(0,1) with 8 outlier columns x100 (seed 1): amax + "
+                        "rowwise and columnwise 1D NVFP4 quantize, round-to-nearest-even",
+            "rows": R, "cols": C, "block": 16, "layouts": ["rowwise", "colwise"],
+            "input_copies": args.copies,
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "gemm_tflops": gemm_tflops,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
