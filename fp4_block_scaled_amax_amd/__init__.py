@@ -19,6 +19,8 @@ ROWWISE = 0x1
 COLWISE = 0x2
 SR = 0x4
 RHT = 0x8
+FUSED_AMAX = 0x10
+WORKSPACE_BYTES = 32832
 SCALE_1D = 1
 SCALE_2D = 2
 F32 = 0
@@ -154,15 +156,30 @@ def nvfp4_amax(x, rht: bool = False, rht_mask: int = 0, out=None, stream=None):
     return out
 
 
+def nvfp4_workspace(device=None):
+    """A zero-filled workspace for nvfp4_quantize_1d(..., fused_amax=True)."""
+    torch = _torch()
+    return torch.zeros(WORKSPACE_BYTES // 4, dtype=torch.int32, device=device or "cuda")
+
+
 def nvfp4_quantize_1d(x, amax, rowwise: bool = True, colwise: bool = False, sr: bool = False,
                       rht: bool = False, rht_mask: int = 0, seed: int = 0, out: dict | None = None,
-                      stream=None):
+                      stream=None, fused_amax: bool = False):
     """1D NVFP4 quantization. Returns a dict with codes_row [R][C/2],
     scales_row [R][C/16], codes_col [C][R/2], scales_col [C][R/16] (the
-    requested layouts) and global_scale (float32 [1])."""
+    requested layouts) and global_scale (float32 [1]).
+
+    amax: float32 [1] from nvfp4_amax, or with fused_amax=True a workspace
+    from nvfp4_workspace() (the call computes the amax itself and leaves it
+    in the workspace's first float, readable as ws.view(torch.float32)[0])."""
     torch = _torch()
     _bits16(x)
-    _dev_tensor(amax, "amax", torch.float32)
+    if fused_amax:
+        _dev_tensor(amax, "workspace")
+        if amax.numel() * amax.element_size() < WORKSPACE_BYTES:
+            raise ValueError(f"workspace must hold {WORKSPACE_BYTES} bytes")
+    else:
+        _dev_tensor(amax, "amax", torch.float32)
     R, C = x.shape
     out = dict(out or {})
     dev = x.device
@@ -173,7 +190,8 @@ def nvfp4_quantize_1d(x, amax, rowwise: bool = True, colwise: bool = False, sr: 
         out["codes_col"] = _empty((C, R // 2), torch.uint8, dev, out.get("codes_col"))
         out["scales_col"] = _empty((C, R // 16), torch.uint8, dev, out.get("scales_col"))
     out["global_scale"] = _empty((1,), torch.float32, dev, out.get("global_scale"))
-    flags = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0) | (SR if sr else 0) | (RHT if rht else 0)
+    flags = ((ROWWISE if rowwise else 0) | (COLWISE if colwise else 0) | (SR if sr else 0)
+             | (RHT if rht else 0) | (FUSED_AMAX if fused_amax else 0))
     _check(lib().nvfp4_quantize_1d(
         _ptr(x), R, C, _ptr(amax), flags, rht_mask & 0xFFFF, seed & ((1 << 64) - 1),
         _ptr(out.get("codes_row")), _ptr(out.get("scales_row")),

@@ -8,14 +8,19 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
+// The plain amax is one read pass: few, wide workgroups (one atomic each,
+// so a few hundred atomics on one address instead of thousands).
+constexpr int kAmaxThreads = 1024;
+constexpr int kAmaxMaxBlocks = 256;
 
 __global__ void amax_reset_kernel(uint32_t* out) { *out = 0u; }
 
 // Reduce a per-thread maximum (binary32 bits) over the workgroup and merge
 // it into *out.
+template <int THREADS>
 __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* out)
 {
-    __shared__ uint32_t partial[kThreads / 64];
+    __shared__ uint32_t partial[THREADS / 64];
     m = wave_max_u32(m);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0)
@@ -24,7 +29,7 @@ __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* out)
     if (threadIdx.x == 0) {
         uint32_t r = partial[0];
 #pragma unroll
-        for (int w = 1; w < kThreads / 64; ++w)
+        for (int w = 1; w < THREADS / 64; ++w)
             r = max(r, partial[w]);
         atomicMax(out, r);
     }
@@ -32,14 +37,14 @@ __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* out)
 
 // bf16 [n]: 16-byte vectors, UNROLL loads in flight per thread.
 template <int UNROLL>
-__global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint4* __restrict__ x,
+__global__ __launch_bounds__(kAmaxThreads) void amax_bf16_kernel(const uint4* __restrict__ x,
                                                               int64_t nvec,
                                                               const uint16_t* __restrict__ tail,
                                                               int tail_n, uint32_t* __restrict__ out)
 {
     uint32_t pm = 0u;  // two u16 maxima of |bf16| patterns
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+    int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
     for (; i + (UNROLL - 1) * stride < nvec; i += UNROLL * stride) {
         uint4 v[UNROLL];
 #pragma unroll
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint4* __rest
     uint32_t m = max(pm & 0xFFFFu, pm >> 16);
     if (blockIdx.x == 0 && (int)threadIdx.x < tail_n)
         m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7FFFu));
-    workgroup_max_to(m << 16, out);
+    workgroup_max_to<kAmaxThreads>(m << 16, out);
 }
 
 // amax of the 16-point Hadamard transform along axis 0. Work item: 16 rows
@@ -96,16 +101,16 @@ __global__ __launch_bounds__(kThreads) void amax_rht_kernel(const uint16_t* __re
                 m = max(m, __float_as_uint(z[i]) & 0x7FFFFFFFu);
         }
     }
-    workgroup_max_to(m, out);
+    workgroup_max_to<kThreads>(m, out);
 }
 
-int grid_for(int64_t work_items, int per_block)
+int grid_for(int64_t work_items, int per_block, int max_blocks)
 {
     int64_t g = (work_items + per_block - 1) / per_block;
     if (g < 1)
         g = 1;
-    if (g > 4096)
-        g = 4096;
+    if (g > max_blocks)
+        g = max_blocks;
     return (int)g;
 }
 
@@ -117,8 +122,8 @@ hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t st
     hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(1), 0, stream, out);
     const int64_t nvec = n >> 3;
     constexpr int kUnroll = 4;
-    const int grid = grid_for(nvec, kThreads * kUnroll);
-    hipLaunchKernelGGL((amax_bf16_kernel<kUnroll>), dim3(grid), dim3(kThreads), 0, stream,
+    const int grid = grid_for(nvec, kAmaxThreads * kUnroll, kAmaxMaxBlocks);
+    hipLaunchKernelGGL((amax_bf16_kernel<kUnroll>), dim3(grid), dim3(kAmaxThreads), 0, stream,
                        reinterpret_cast<const uint4*>(x), nvec, x + nvec * 8, (int)(n & 7), out);
     return hipGetLastError();
 }
@@ -129,7 +134,7 @@ hipError_t launch_amax_rht(const uint16_t* x, int64_t rows, int64_t cols, uint32
     uint32_t* out = reinterpret_cast<uint32_t*>(amax);
     hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(1), 0, stream, out);
     const int64_t items = (rows >> 4) * (cols >> 3);
-    const int grid = grid_for(items, kThreads);
+    const int grid = grid_for(items, kThreads, 1024);
     hipLaunchKernelGGL(amax_rht_kernel, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, mask,
                        out);
     return hipGetLastError();

@@ -71,8 +71,10 @@ int nvfp4_quantize_1d(const uint16_t* x, int64_t rows, int64_t cols, const float
                       uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                       float* global_scale, hipStream_t stream)
 {
-    const uint32_t known = NVFP4_ROWWISE | NVFP4_COLWISE | NVFP4_SR | NVFP4_RHT;
+    const uint32_t known = NVFP4_ROWWISE | NVFP4_COLWISE | NVFP4_SR | NVFP4_RHT | NVFP4_FUSED_AMAX;
     if ((flags & ~known) != 0 || (flags & (NVFP4_ROWWISE | NVFP4_COLWISE)) == 0)
+        return NVFP4_ERR_FLAGS;
+    if ((flags & NVFP4_FUSED_AMAX) && (flags & NVFP4_RHT))
         return NVFP4_ERR_FLAGS;
     if ((flags & NVFP4_RHT) && ((flags & NVFP4_ROWWISE) || !(flags & NVFP4_COLWISE)))
         return NVFP4_ERR_FLAGS;
@@ -88,9 +90,12 @@ int nvfp4_quantize_1d(const uint16_t* x, int64_t rows, int64_t cols, const float
     if (!dims_ok(rows, cols) || rows / 256 >= (1 << 20) || cols / 256 >= (1 << 20))
         return NVFP4_ERR_SIZE;
     if (!aligned16(x) || (row && (!aligned16(codes_row) || !aligned16(scales_row))) ||
-        (col && (!aligned16(codes_col) || !aligned16(scales_col))))
+        (col && (!aligned16(codes_col) || !aligned16(scales_col))) ||
+        ((flags & NVFP4_FUSED_AMAX) && !aligned16(amax)))
         return NVFP4_ERR_ALIGN;
     nvfp4::QuantizeArgs a{};
+    a.fused_amax = (flags & NVFP4_FUSED_AMAX) != 0;
+    a.workspace = a.fused_amax ? reinterpret_cast<uint32_t*>(const_cast<float*>(amax)) : nullptr;
     a.x = x;
     a.rows = rows;
     a.cols = cols;

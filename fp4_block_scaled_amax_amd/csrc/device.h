@@ -73,15 +73,17 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
 
 // Round a non-negative binary32 (or NaN) to E4M3, nearest even, with
 // subnormals; values >= 448 (and +inf) saturate to 448 (0x7E); NaN -> 0x7F.
+// Branch-free: both the subnormal and the normal rounding are formed and
+// the right one is selected.
 __device__ __forceinline__ uint32_t e4m3_encode(float v)
 {
-    if (!(v < 448.0f))
-        return (v != v) ? 0x7Fu : 0x7Eu;
-    if (v < 0.015625f)                                  // below 2^-6: multiples of 2^-9
-        return (uint32_t)__builtin_rintf(v * 512.0f);   // exact scaling, RNE
+    const uint32_t sub = (uint32_t)__builtin_rintf(v * 512.0f);      // multiples of 2^-9, RNE
     uint32_t u = __float_as_uint(v);
-    u += 0x7FFFFu + ((u >> 20) & 1u);                    // RNE at mantissa bit 20
-    return (u >> 20) - (120u << 3);                      // rebias exponent 127 -> 7
+    u += 0x7FFFFu + ((u >> 20) & 1u);                                 // RNE at mantissa bit 20
+    const uint32_t nrm = (u >> 20) - (120u << 3);                     // rebias exponent 127 -> 7
+    uint32_t b = (v < 0.015625f) ? sub : nrm;                        // below 2^-6: subnormal
+    b = (v >= 448.0f) ? 0x7Eu : b;
+    return (v != v) ? 0x7Fu : b;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t b)
@@ -94,6 +96,14 @@ __device__ __forceinline__ float e4m3_decode(uint32_t b)
     return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
+// Element multiplier of a block whose scale byte is `byte`:
+// r = 1 / (e4m3(byte) * sg), or 0 when that unit is 0.
+__device__ __forceinline__ float unit_reciprocal(uint32_t byte, float sg)
+{
+    const float d = e4m3_decode(byte) * sg;
+    return (d == 0.0f) ? 0.0f : 1.0f / d;
+}
+
 // Per-block scale chain. b_bits: binary32 bits of the block's max |x|.
 // sg = amax / 2688, t = 6 * sg. Outputs the scale byte and the element
 // multiplier r = 1 / (s * sg) (0 when that unit is 0).
@@ -102,15 +112,27 @@ struct BlockScale {
     float r;
 };
 
+__device__ __forceinline__ uint32_t block_scale_byte(uint32_t b_bits, float t)
+{
+    const float b = __uint_as_float(b_bits);
+    const float s_f = (t == 0.0f) ? 0.0f : b / t;
+    return e4m3_encode(s_f);
+}
+
 __device__ __forceinline__ BlockScale block_scale(uint32_t b_bits, float sg, float t)
 {
-    float b = __uint_as_float(b_bits);
-    float s_f = (t == 0.0f) ? 0.0f : b / t;
     BlockScale out;
-    out.byte = e4m3_encode(s_f);
-    float d = e4m3_decode(out.byte) * sg;
-    out.r = (d == 0.0f) ? 0.0f : 1.0f / d;
+    out.byte = block_scale_byte(b_bits, t);
+    out.r = unit_reciprocal(out.byte, sg);
     return out;
+}
+
+// The 128 possible multipliers of a tensor (one per scale byte 0..127),
+// built once per workgroup in LDS by the first 128 threads.
+__device__ __forceinline__ void build_reciprocal_table(float* table, float sg)
+{
+    if (threadIdx.x < 128)
+        table[threadIdx.x] = unit_reciprocal(threadIdx.x, sg);
 }
 
 // ----------------------------------------------------------- E2M1 codes

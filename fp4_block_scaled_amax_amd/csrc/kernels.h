@@ -23,6 +23,8 @@ struct QuantizeArgs {
     uint8_t* codes_col;
     uint8_t* scales_col;
     float* global_scale;  // optional
+    bool fused_amax;      // compute the amax in the same call (workspace)
+    uint32_t* workspace;  // fused_amax: amax bits in word 0, scratch after
 };
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
 

@@ -1,17 +1,28 @@
 // NVFP4 quantization kernels: 1D (rowwise / columnwise / both, RNE or
 // stochastic, optional Hadamard) and 2D (16x16 tiles, both layouts).
 //
-// One workgroup (256 threads, 4 waves) owns a kTileR x kTileC tile of the
-// bf16 input. A work item is 16 rows x 8 columns: sixteen 16-byte loads,
-// where the 32 lanes of a half-wave cover 256 consecutive columns of a row
-// (512 contiguous bytes per load). Inside an item:
+// One workgroup (256 threads, 4 waves) owns a 128 x 256 tile of the bf16
+// input. A work item is 16 rows x 8 columns (sixteen 16-byte loads); the 32
+// lanes of a half-wave cover 256 consecutive columns of a row (512
+// contiguous bytes per load), the two half-waves of a wave cover two row
+// blocks. Inside an item:
 //   - a columnwise block is one column's 16 rows (all in one lane);
 //   - a rowwise block is one row's 16 columns, split over the lane pair
 //     (2k, 2k+1), which trade maxima and multipliers through DPP;
 //   - a 2D tile is the lane pair's 16 x 16 elements.
-// Rowwise codes are stored straight from registers (128 contiguous bytes
-// per row per half-wave). Columnwise codes are staged in LDS and written
-// as whole 128-byte column segments.
+// Rowwise codes are stored straight from registers (128 contiguous bytes per
+// row per half-wave). Columnwise codes are staged in LDS and leave as 64-byte
+// column segments; tiles are walked down the rows per XCD so that the two
+// halves of a 128-byte line are written by the same L2.
+//
+// Encoding: the element ratio v = x * r (r = 1 / (s * S_g) of its block) is
+// rounded to E2M1 by the gfx950 converter v_cvt_scalef32_pk_fp4_f32 with a
+// unit scale, which rounds to nearest even and saturates at +-6 exactly like
+// the reference rule for every non-NaN input (checked over all 2^32 binary32
+// patterns); a NaN ratio needs a non-finite r, and such blocks first map NaN
+// ratios to a signed zero. Stochastic rounding uses the software encoder.
+#include <atomic>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -20,11 +31,11 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileR = 256;
+constexpr int kTileR = 128;
 constexpr int kTileC = 256;
-constexpr int kRowBlocks = kTileR / 16;   // 16
-constexpr int kColGroups = kTileC / 8;    // 32
-constexpr int kItemsPerThread = kRowBlocks * kColGroups / kThreads;  // 2
+constexpr int kRowBlocks = kTileR / 16;  // 8
+constexpr int kColGroups = kTileC / 8;   // 32
+static_assert(kRowBlocks * kColGroups == kThreads, "one item per thread");
 
 struct Params {
     const uint16_t* x;
@@ -41,8 +52,7 @@ struct Params {
 
 // Map the workgroup index to a tile so that each XCD (workgroups are dealt
 // round-robin over 8) walks a contiguous run of tiles; `vertical` makes the
-// run go down the rows first (columnwise outputs of adjacent tiles then
-// share cache lines in the same L2).
+// run go down the rows first.
 __device__ __forceinline__ void tile_of_block(int tiles_r, int tiles_c, bool vertical, int& tr,
                                               int& tc)
 {
@@ -61,221 +71,643 @@ __device__ __forceinline__ void tile_of_block(int tiles_r, int tiles_c, bool ver
     }
 }
 
-template <bool ROW, bool COL, bool TWO_D, bool SR, bool RHT>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
+__device__ __forceinline__ bool finite_bits(float r)
 {
-    // Columnwise staging: per tile column, 16 row blocks x 8 bytes; the
-    // slot of a row block is swizzled by the column group to spread banks.
-    __shared__ uint2 lds_codes[COL ? kTileC * kRowBlocks : 1];
-    __shared__ uint8_t lds_scales[(COL && !TWO_D) ? kTileC * kRowBlocks : 16];
+    return (__float_as_uint(r) & 0x7F800000u) != 0x7F800000u;
+}
 
-    int tr, tc;
-    tile_of_block(p.tiles_r, p.tiles_c, COL, tr, tc);
-    const int64_t tile_r0 = (int64_t)tr * kTileR;
-    const int64_t tile_c0 = (int64_t)tc * kTileC;
+// ---- encoders
+//
+// A pair of values (a, b) -> one byte of codes (a in the low nibble), placed
+// at byte BYTE of a 32-bit word. MODE 0: hardware RNE; 1: hardware RNE with
+// NaN ratios replaced by a signed zero first (the reference rule gives a NaN
+// ratio magnitude 0 and keeps the element's sign; used only when a block
+// multiplier is not finite, the one way a ratio can be NaN); 2: software
+// stochastic rounding.
 
-    const float amax = *p.amax;
-    const float sg = global_scale_from_amax(amax);
-    const float t6 = 6.0f * sg;
-    if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
-        *p.sg_out = sg;
+enum { kEncHw = 0, kEncHwSafe = 1, kEncSr = 2 };
 
+__device__ __forceinline__ float nan_to_signed_zero(float v, float x)
+{
+    return (v != v) ? __uint_as_float(__float_as_uint(x) & 0x80000000u) : v;
+}
+
+template <int BYTE>
+__device__ __forceinline__ uint32_t cvt_pair(uint32_t old, float a, float b)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, BYTE);
+}
+
+template <int MODE, int BYTE>
+__device__ __forceinline__ uint32_t put_pair(uint32_t word, float a, float b, float r, uint32_t ha,
+                                             uint32_t hb)
+{
+    if (MODE == kEncHw)
+        return cvt_pair<BYTE>(word, a * r, b * r);
+    if (MODE == kEncHwSafe)
+        return cvt_pair<BYTE>(word, nan_to_signed_zero(a * r, a), nan_to_signed_zero(b * r, b));
+    const uint32_t lo = e2m1_sr_nibble(fabsf(a) * r, ha, (__float_as_uint(a) >> 28) & 8u);
+    const uint32_t hi = e2m1_sr_nibble(fabsf(b) * r, hb, (__float_as_uint(b) >> 28) & 8u);
+    return word | ((lo | (hi << 4)) << (8 * BYTE));
+}
+
+// 16 values of one column (rows in order) -> 8 bytes of codes.
+template <int MODE>
+__device__ __forceinline__ uint2 encode_column16(const float (&y)[16], float r,
+                                                 const uint4 (&draws)[16], int j)
+{
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#define NVFP4_PAIR(B)                                                                      \
+    {                                                                                      \
+        const int i = 8 * half + 2 * (B);                                                  \
+        const uint32_t ha = MODE == kEncSr ? draw16(draws[i], j) : 0u;                     \
+        const uint32_t hb = MODE == kEncSr ? draw16(draws[i + 1], j) : 0u;                 \
+        w[half] = put_pair<MODE, B>(w[half], y[i], y[i + 1], r, ha, hb);                   \
+    }
+        NVFP4_PAIR(0) NVFP4_PAIR(1) NVFP4_PAIR(2) NVFP4_PAIR(3)
+#undef NVFP4_PAIR
+    }
+    return make_uint2(w[0], w[1]);
+}
+
+// Row-and/or-column encoding of a whole item in 2x2 groups: elements
+// (i, 2k), (i, 2k+1), (i+1, 2k), (i+1, 2k+1) are unpacked once and feed byte
+// k of the two row words and byte (i/2 mod 4) of the two column words.
+template <int MODE, int IP, bool ROW, bool COL>
+__device__ __forceinline__ void encode_row_pair(const uint4 (&v)[16], const float (&rr)[16],
+                                                const float (&rc)[8], const uint4 (&draws)[16],
+                                                uint32_t (&roww)[2], uint32_t (&colw)[8][2])
+{
+    constexpr int i = 2 * IP;
+    constexpr int cb = IP & 3;     // byte within the column word
+    constexpr int ch = IP >> 2;    // which column word (rows 0..7 or 8..15)
+    roww[0] = roww[1] = 0u;
+#define NVFP4_GROUP(K)                                                                      \
+    {                                                                                       \
+        const uint32_t w0 = word_at(v[i], K), w1 = word_at(v[i + 1], K);                    \
+        const float a = bf16_lo(w0), b = bf16_hi(w0), c = bf16_lo(w1), d = bf16_hi(w1);     \
+        uint32_t ha = 0u, hb = 0u, hc = 0u, hd = 0u;                                        \
+        if (MODE == kEncSr) {                                                               \
+            ha = draw16(draws[i], 2 * K);                                                   \
+            hb = draw16(draws[i], 2 * K + 1);                                               \
+            hc = draw16(draws[i + 1], 2 * K);                                               \
+            hd = draw16(draws[i + 1], 2 * K + 1);                                           \
+        }                                                                                   \
+        if (ROW) {                                                                          \
+            roww[0] = put_pair<MODE, K>(roww[0], a, b, rr[i], ha, hb);                      \
+            roww[1] = put_pair<MODE, K>(roww[1], c, d, rr[i + 1], hc, hd);                  \
+        }                                                                                   \
+        if (COL) {                                                                          \
+            colw[2 * K][ch] = put_pair<MODE, cb>(colw[2 * K][ch], a, c, rc[2 * K], ha, hc);         \
+            colw[2 * K + 1][ch] = put_pair<MODE, cb>(colw[2 * K + 1][ch], b, d, rc[2 * K + 1], hb, hd); \
+        }                                                                                   \
+    }
+    NVFP4_GROUP(0) NVFP4_GROUP(1) NVFP4_GROUP(2) NVFP4_GROUP(3)
+#undef NVFP4_GROUP
+}
+
+template <int MODE, bool ROW, bool COL>
+__device__ __forceinline__ void encode_item(const uint4 (&v)[16], const float (&rr)[16],
+                                            const float (&rc)[8], const uint4 (&draws)[16],
+                                            uint8_t* row_dst, int64_t row_pitch,
+                                            uint32_t (&colw)[8][2])
+{
+    uint32_t roww[2];
+#define NVFP4_ROWS(IP)                                                                   \
+    encode_row_pair<MODE, IP, ROW, COL>(v, rr, rc, draws, roww, colw);                    \
+    if (ROW) {                                                                           \
+        *reinterpret_cast<uint32_t*>(row_dst + (2 * IP) * row_pitch) = roww[0];          \
+        *reinterpret_cast<uint32_t*>(row_dst + (2 * IP + 1) * row_pitch) = roww[1];      \
+    }
+    NVFP4_ROWS(0) NVFP4_ROWS(1) NVFP4_ROWS(2) NVFP4_ROWS(3)
+    NVFP4_ROWS(4) NVFP4_ROWS(5) NVFP4_ROWS(6) NVFP4_ROWS(7)
+#undef NVFP4_ROWS
+}
+
+// Position of this thread's work item inside a tile.
+struct ItemPos {
+    int64_t tile_r0, tile_c0, r0, c0;
+    int rb, cg;
+    bool odd, valid;
+};
+
+__device__ __forceinline__ ItemPos item_pos(int tr, int tc, int64_t rows, int64_t cols)
+{
+    ItemPos q;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int cg = lane & 31;
-    const bool odd = (lane & 1) != 0;
-    const int64_t rows = p.rows, cols = p.cols;
+    q.tile_r0 = (int64_t)tr * kTileR;
+    q.tile_c0 = (int64_t)tc * kTileC;
+    q.cg = lane & 31;
+    q.rb = wave * 2 + (lane >> 5);
+    q.odd = (lane & 1) != 0;
+    q.r0 = q.tile_r0 + q.rb * 16;
+    q.c0 = q.tile_c0 + q.cg * 8;
+    // Both lanes of a pair agree: cols is a multiple of 16.
+    q.valid = q.r0 < rows && q.c0 < cols;
+    return q;
+}
 
-#pragma unroll 1
-    for (int it = 0; it < kItemsPerThread; ++it) {
-        const int rb = it * (kRowBlocks / kItemsPerThread) + wave * 2 + (lane >> 5);
-        const int64_t r0 = tile_r0 + rb * 16;
-        const int64_t c0 = tile_c0 + cg * 8;
-        if (r0 >= rows || c0 >= cols)
-            continue;  // both lanes of a pair agree: cols is a multiple of 16
-
-        uint4 v[16];
-        const uint16_t* src = p.x + r0 * cols + c0;
+__device__ __forceinline__ void load_item(const Params& p, const ItemPos& q, uint4 (&v)[16])
+{
+    if (q.valid) {
+        const uint16_t* src = p.x + q.r0 * p.cols + q.c0;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            v[i] = load16_stream(src + i * cols);
+            v[i] = load16_stream(src + i * p.cols);
+    }
+}
 
-        // ---- element values (binary32) and column maxima
-        float y[8][16];
+// Quantize one work item held in registers: block scales, codes; rowwise
+// outputs go straight to memory, columnwise outputs to the LDS staging.
+template <bool ROW, bool COL, bool TWO_D, bool SR, bool RHT>
+__device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
+                                             const uint4 (&v)[16], float sg, float t6,
+                                             const float* lds_rcp, uint2* lds_codes,
+                                             uint8_t* lds_scales)
+{
+    const int64_t rows = p.rows, cols = p.cols;
+    const int64_t r0 = q.r0, c0 = q.c0;
+    const int rb = q.rb, cg = q.cg;
+    const bool odd = q.odd;
+    (void)rows;
+    // Stochastic-rounding draws: one Philox call per row covers the
+    // item's 8 consecutive flat indices.
+    uint4 draws[16];
+    if (SR) {
+        const uint64_t flat0 = (uint64_t)(r0 * cols + c0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint64_t q = (flat0 + (uint64_t)i * (uint64_t)cols) >> 3;
+            draws[i] = philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), p.seed_lo, p.seed_hi);
+        }
+    }
+
+    if (COL && !ROW && !TWO_D) {
+        // ------------------------------------------ columnwise only
         uint32_t cmax[8];
-        if (RHT) {
+        if (!RHT) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    y[j][i] = bf16_at(v[i], j);
-                rht16_inplace(y[j], p.mask);
-                uint32_t m = 0u;
+            for (int k = 0; k < 4; ++k) {
+                uint32_t pm = 0u;
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    m = max(m, __float_as_uint(y[j][i]) & 0x7FFFFFFFu);
-                cmax[j] = m;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    y[j][i] = bf16_at(v[i], j);
-            if (COL || TWO_D) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    uint32_t pm = 0u;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        pm = pk_max_u16(pm, word_at(v[i], k) & 0x7FFF7FFFu);
-                    cmax[2 * k] = pm << 16;
-                    cmax[2 * k + 1] = pm & 0xFFFF0000u;
-                }
+                    pm = pk_max_u16(pm, word_at(v[i], k) & 0x7FFF7FFFu);
+                cmax[2 * k] = pm << 16;
+                cmax[2 * k + 1] = pm & 0xFFFF0000u;
             }
         }
-
-        // ---- block scales
-        float rc[8];            // columnwise multipliers (1D)
-        float r2 = 0.0f;        // 2D tile multiplier
-        uint32_t tile_byte = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float y[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                y[i] = bf16_at(v[i], j);
+            uint32_t m;
+            if (RHT) {
+                rht16_inplace(y, p.mask);
+                m = 0u;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    m = max(m, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+            } else {
+                m = cmax[j];
+            }
+            const uint32_t byte = block_scale_byte(m, t6);
+            const float r = lds_rcp[byte];
+            uint2 words;
+            if (SR)
+                words = encode_column16<kEncSr>(y, r, draws, j);
+            else if (__all(finite_bits(r)))
+                words = encode_column16<kEncHw>(y, r, draws, j);
+            else
+                words = encode_column16<kEncHwSafe>(y, r, draws, j);
+            const int col = cg * 8 + j;
+            lds_codes[col * kRowBlocks + (rb ^ (cg & 7))] = words;
+            lds_scales[col * kRowBlocks + rb] = (uint8_t)byte;
+        }
+    } else {
+        // ------------------------- rowwise, rowwise + columnwise, 2D
+        uint32_t cmax[8];
+        if (COL || TWO_D) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                uint32_t pm = 0u;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    pm = pk_max_u16(pm, word_at(v[i], k) & 0x7FFF7FFFu);
+                cmax[2 * k] = pm << 16;
+                cmax[2 * k + 1] = pm & 0xFFFF0000u;
+            }
+        }
+        float rc[8];   // columnwise multipliers (1D), or the tile's (2D)
+        float rr[16];  // rowwise multipliers (1D), or the tile's (2D)
         uint32_t col_byte[8];
+        bool fin = true;
         if (TWO_D) {
             uint32_t m = cmax[0];
 #pragma unroll
             for (int j = 1; j < 8; ++j)
                 m = max(m, cmax[j]);
             m = max(m, swap_lane1(m));
-            BlockScale bs = block_scale(m, sg, t6);
-            r2 = bs.r;
-            tile_byte = bs.byte;
-        } else if (COL) {
+            const uint32_t byte = block_scale_byte(m, t6);
+            const float r = lds_rcp[byte];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                BlockScale bs = block_scale(cmax[j], sg, t6);
-                rc[j] = bs.r;
-                col_byte[j] = bs.byte;
+            for (int j = 0; j < 8; ++j)
+                rc[j] = r;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                rr[i] = r;
+            fin = finite_bits(r);
+            if (!odd)
+                p.scales_row[(r0 >> 4) * (cols >> 4) + (c0 >> 4)] = (uint8_t)byte;
+        } else {
+            if (COL) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    col_byte[j] = block_scale_byte(cmax[j], t6);
+                    rc[j] = lds_rcp[col_byte[j]];
+                    fin = fin && finite_bits(rc[j]);
+                }
+            }
+            if (ROW) {
+                uint32_t rm[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t pm =
+                        pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
+                                   pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu));
+                    rm[i] = max(pm & 0xFFFFu, pm >> 16) << 16;
+                }
+                // Even lanes own rows 0..7 of the pair's blocks, odd lanes 8..15.
+                const int64_t srow0 = r0 + (odd ? 8 : 0);
+                uint8_t* sdst = p.scales_row + srow0 * (cols >> 4) + (c0 >> 4);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t send = odd ? rm[k] : rm[k + 8];
+                    const uint32_t recv = swap_lane1(send);
+                    const uint32_t own = odd ? rm[k + 8] : rm[k];
+                    const uint32_t byte = block_scale_byte(max(own, recv), t6);
+                    sdst[k * (cols >> 4)] = (uint8_t)byte;
+                    const float mine = lds_rcp[byte];
+                    const float other = swap_lane1(mine);
+                    rr[k] = odd ? other : mine;
+                    rr[k + 8] = odd ? mine : other;
+                    fin = fin && finite_bits(mine);
+                }
             }
         }
-
-        float rr[16];  // rowwise multipliers (1D), one per row of the item
-        if (ROW && !TWO_D) {
-            uint32_t rm[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                uint32_t pm = pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
-                                         pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu));
-                rm[i] = max(pm & 0xFFFFu, pm >> 16) << 16;
-            }
-            // Even lanes own rows 0..7 of the pair's blocks, odd lanes 8..15.
-            const int64_t srow0 = r0 + (odd ? 8 : 0);
-            uint8_t* sdst = p.scales_row + srow0 * (cols >> 4) + (c0 >> 4);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t send = odd ? rm[k] : rm[k + 8];
-                const uint32_t recv = swap_lane1(send);
-                const uint32_t own = odd ? rm[k + 8] : rm[k];
-                BlockScale bs = block_scale(max(own, recv), sg, t6);
-                sdst[k * (cols >> 4)] = (uint8_t)bs.byte;
-                const float other = swap_lane1(bs.r);
-                rr[k] = odd ? other : bs.r;
-                rr[k + 8] = odd ? bs.r : other;
-            }
-        }
-
-        // ---- encode, row by row
         uint32_t colw[8][2];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             colw[j][0] = colw[j][1] = 0u;
-        const int64_t flat0 = r0 * cols + c0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            uint4 draws = make_uint4(0u, 0u, 0u, 0u);
-            if (SR) {
-                const uint64_t q = (uint64_t)(flat0 + i * cols) >> 3;
-                draws = philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), p.seed_lo, p.seed_hi);
-            }
-            uint32_t roww = 0u;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float xv = y[j][i];
-                const uint32_t sign8 = (__float_as_uint(xv) >> 28) & 8u;
-                const float ax = fabsf(xv);
-                const uint32_t h = SR ? draw16(draws, j) : 0u;
-                if (TWO_D) {
-                    // one code per element, emitted in both layouts
-                    const uint32_t nib = e2m1_rne_nibble(ax * r2, sign8);
-                    if (ROW)
-                        roww |= nib << (4 * j);
-                    if (COL)
-                        colw[j][i >> 3] |= nib << (4 * (i & 7));
-                } else {
-                    if (COL) {
-                        const float vv = ax * rc[j];
-                        const uint32_t nib = SR ? e2m1_sr_nibble(vv, h, sign8) : e2m1_rne_nibble(vv, sign8);
-                        colw[j][i >> 3] |= nib << (4 * (i & 7));
-                    }
-                    if (ROW) {
-                        const float vv = ax * rr[i];
-                        const uint32_t nib = SR ? e2m1_sr_nibble(vv, h, sign8) : e2m1_rne_nibble(vv, sign8);
-                        roww |= nib << (4 * j);
-                    }
-                }
-            }
-            if (ROW)
-                *reinterpret_cast<uint32_t*>(p.codes_row + (r0 + i) * (cols >> 1) + (c0 >> 1)) = roww;
-        }
-
-        if (TWO_D && !odd)
-            p.scales_row[(r0 >> 4) * (cols >> 4) + (c0 >> 4)] = (uint8_t)tile_byte;
-
+        uint8_t* row_dst = ROW ? p.codes_row + r0 * (cols >> 1) + (c0 >> 1) : nullptr;
+        const int64_t row_pitch = cols >> 1;
+        if (SR)
+            encode_item<kEncSr, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
+        else if (__all(fin))
+            encode_item<kEncHw, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
+        else
+            encode_item<kEncHwSafe, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
         if (COL) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int col = cg * 8 + j;
-                const int slot = rb ^ (cg & 15);
-                lds_codes[col * kRowBlocks + slot] = make_uint2(colw[j][0], colw[j][1]);
+                lds_codes[col * kRowBlocks + (rb ^ (cg & 7))] = make_uint2(colw[j][0], colw[j][1]);
                 if (!TWO_D)
                     lds_scales[col * kRowBlocks + rb] = (uint8_t)col_byte[j];
             }
         }
     }
+}
 
-    if (COL) {
-        __syncthreads();
-        // Codes: 8-byte chunks, 16 lanes per tile column (one 128-byte segment).
-        const int64_t pitch = rows >> 1;
+// Write a tile's staged columnwise codes (and 1D column scales) to memory.
+template <bool TWO_D>
+__device__ __forceinline__ void write_col_tile(const Params& p, int64_t tile_r0, int64_t tile_c0,
+                                               const uint2* lds_codes, const uint8_t* lds_scales)
+{
+    const int64_t rows = p.rows, cols = p.cols;
+    // Codes: 8-byte chunks; 8 lanes cover one tile column's 64 bytes.
+    const int64_t pitch = rows >> 1;
 #pragma unroll
-        for (int k = 0; k < kTileC * kRowBlocks / kThreads; ++k) {
-            const int q = k * kThreads + threadIdx.x;
-            const int col = q >> 4, part = q & 15;
-            const int64_t c = tile_c0 + col, r = tile_r0 + part * 16;
-            if (c < cols && r < rows) {
-                const int slot = part ^ ((col >> 3) & 15);
-                *reinterpret_cast<uint2*>(p.codes_col + c * pitch + (r >> 1)) =
-                    lds_codes[col * kRowBlocks + slot];
-            }
+    for (int k = 0; k < kTileC * kRowBlocks / kThreads; ++k) {
+        const int q = k * kThreads + threadIdx.x;
+        const int col = q >> 3, part = q & 7;
+        const int64_t c = tile_c0 + col, r = tile_r0 + part * 16;
+        if (c < cols && r < rows) {
+            const int slot = part ^ ((col >> 3) & 7);
+            *reinterpret_cast<uint2*>(p.codes_col + c * pitch + (r >> 1)) =
+                lds_codes[col * kRowBlocks + slot];
         }
-        if (!TWO_D) {
-            // Scales: one tile column's 16 bytes per thread.
-            const int col = threadIdx.x;
-            const int64_t c = tile_c0 + col;
-            if (c < cols) {
-                const int64_t spitch = rows >> 4;
-                uint8_t* dst = p.scales_col + c * spitch + (tile_r0 >> 4);
-                const int64_t nb64 = (rows - tile_r0) >> 4;
-                const int nb = nb64 < kRowBlocks ? (int)nb64 : kRowBlocks;
-                const uint8_t* srcs = &lds_scales[col * kRowBlocks];
-                if (nb == kRowBlocks && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
-                    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(srcs);
-                } else {
-                    for (int b = 0; b < nb; ++b)
-                        dst[b] = srcs[b];
-                }
+    }
+    if (!TWO_D) {
+        // Scales: one tile column's 8 bytes per thread.
+        const int col = threadIdx.x;
+        const int64_t c = tile_c0 + col;
+        if (c < cols) {
+            const int64_t spitch = rows >> 4;
+            uint8_t* dst = p.scales_col + c * spitch + (tile_r0 >> 4);
+            const int64_t nb64 = (rows - tile_r0) >> 4;
+            const int nb = nb64 < kRowBlocks ? (int)nb64 : kRowBlocks;
+            const uint8_t* srcs = &lds_scales[col * kRowBlocks];
+            if (nb == kRowBlocks && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
+                *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(srcs);
+            } else {
+                for (int b = 0; b < nb; ++b)
+                    dst[b] = srcs[b];
             }
         }
     }
+}
+
+template <bool ROW, bool COL, bool TWO_D, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
+{
+    // Columnwise staging: per tile column, 8 row blocks x 8 bytes; the slot
+    // of a row block is swizzled by the column group to spread LDS banks.
+    __shared__ uint2 lds_codes[COL ? kTileC * kRowBlocks : 1];
+    __shared__ uint8_t lds_scales[(COL && !TWO_D) ? kTileC * kRowBlocks : 16];
+    __shared__ float lds_rcp[128];
+
+    int tr, tc;
+    tile_of_block(p.tiles_r, p.tiles_c, COL, tr, tc);
+    const ItemPos q = item_pos(tr, tc, p.rows, p.cols);
+    uint4 v[16];
+    load_item(p, q, v);
+
+    const float amax = *p.amax;
+    const float sg = global_scale_from_amax(amax);
+    const float t6 = 6.0f * sg;
+    if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+        *p.sg_out = sg;
+    build_reciprocal_table(lds_rcp, sg);
+    __syncthreads();
+
+    if (q.valid)
+        compute_item<ROW, COL, TWO_D, SR, RHT>(p, q, v, sg, t6, lds_rcp, lds_codes, lds_scales);
+    if (COL) {
+        __syncthreads();
+        write_col_tile<TWO_D>(p, q.tile_r0, q.tile_c0, lds_codes, lds_scales);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused amax + quantize: one persistent launch in which every thread keeps
+// two work items (2 x 256 bytes of bf16) in registers, so the tensor is read
+// from HBM once. The workgroups exchange their block-local maxima through a
+// small workspace without read-modify-write atomics: each workgroup posts
+// (generation, max) in its own arrival slot, workgroup 0 collects them all
+// and posts (generation, amax) in every workgroup's own release slot, so no
+// address is polled by more than a few workgroups. The grid is sized so all
+// workgroups fit on the device at once; the waits are bounded by wall-clock
+// time and, should they expire (workgroups not co-resident), a workgroup
+// computes the exact amax directly from the tensor, so the result is always
+// the same and the device can never hang.
+//
+// Workspace (32-bit words): [0] amax bits, [1] generation of the last
+// completed call, [2] slow-path counter, then 2 words per workgroup of
+// arrival slots and 2 words per workgroup of release slots.
+
+constexpr int kWsAmax = 0, kWsGen = 1, kWsSlow = 2, kWsArrive = 16;
+constexpr int kMaxFusedBlocks = 2048;
+constexpr int kWsRelease = kWsArrive + 2 * kMaxFusedBlocks;
+constexpr uint64_t kWaitTicks = 200000;  // 2 ms of the 100 MHz real-time counter
+
+// All exchange traffic is relaxed device-scope atomics: the value travels
+// inside the atomic word itself, so no other memory needs ordering (and
+// acquire/release at device scope would write back or invalidate the
+// non-coherent per-XCD L2s).
+__device__ __forceinline__ uint32_t ws_load(const uint32_t* a)
+{
+    return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ws_store(uint32_t* a, uint32_t v)
+{
+    __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A (generation, value) pair in one 64-bit word, so a reader sees both or neither.
+__device__ __forceinline__ uint64_t slot_load(const uint32_t* a)
+{
+    return __hip_atomic_load(reinterpret_cast<const uint64_t*>(a), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void slot_store(uint32_t* a, uint32_t gen, uint32_t value)
+{
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(a), ((uint64_t)value << 32) | gen,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t item_abs_max(const ItemPos& q, const uint4 (&v)[16], uint32_t pm)
+{
+    if (q.valid) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            pm = pk_max_u16(pm, v[i].x & 0x7FFF7FFFu);
+            pm = pk_max_u16(pm, v[i].y & 0x7FFF7FFFu);
+            pm = pk_max_u16(pm, v[i].z & 0x7FFF7FFFu);
+            pm = pk_max_u16(pm, v[i].w & 0x7FFF7FFFu);
+        }
+    }
+    return pm;
+}
+
+// Maximum over the workgroup; every thread gets the result.
+__device__ __forceinline__ uint32_t workgroup_max(uint32_t m, uint32_t* red)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    m = wave_max_u32(m);
+    __syncthreads();
+    if (lane == 0)
+        red[wave] = m;
+    __syncthreads();
+    uint32_t r = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w)
+        r = max(r, red[w]);
+    return r;
+}
+
+// Exact amax of the whole tensor by this workgroup alone (slow path).
+__device__ uint32_t direct_amax(const Params& p, uint32_t* red)
+{
+    const int64_t n = p.rows * p.cols;
+    uint32_t pm = 0u;
+    for (int64_t i = (int64_t)threadIdx.x * 8; i < n; i += (int64_t)kThreads * 8) {
+        const uint4 v = load16(p.x + i);
+        pm = pk_max_u16(pm, v.x & 0x7FFF7FFFu);
+        pm = pk_max_u16(pm, v.y & 0x7FFF7FFFu);
+        pm = pk_max_u16(pm, v.z & 0x7FFF7FFFu);
+        pm = pk_max_u16(pm, v.w & 0x7FFF7FFFu);
+    }
+    return workgroup_max(max(pm & 0xFFFFu, pm >> 16) << 16, red);
+}
+
+// Grid-wide maximum of one value per workgroup (binary32 bits); every
+// workgroup returns the same result.
+__device__ uint32_t grid_max(uint32_t m, uint32_t* ws, const Params& p)
+{
+    __shared__ uint32_t red[kThreads / 64];
+    __shared__ uint32_t gen_s, result_s, ok_s;
+    m = workgroup_max(m, red);
+    if (threadIdx.x == 0) {
+        const uint32_t gen = ws_load(&ws[kWsGen]) + 1u;  // this call's generation
+        gen_s = gen;
+        slot_store(&ws[kWsArrive + 2 * blockIdx.x], gen, m);
+    }
+    __syncthreads();
+    const uint32_t gen = gen_s;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    if (blockIdx.x == 0) {
+        // Collect every workgroup's maximum.
+        uint32_t mm = 0u;
+        bool ok = true;
+        for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads) {
+            uint64_t w = slot_load(&ws[kWsArrive + 2 * i]);
+            while ((uint32_t)w != gen) {
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(4);
+                w = slot_load(&ws[kWsArrive + 2 * i]);
+            }
+            if (!ok)
+                break;
+            mm = max(mm, (uint32_t)(w >> 32));
+        }
+        if (threadIdx.x == 0)
+            ok_s = 1u;
+        __syncthreads();
+        if (!ok)
+            ok_s = 0u;
+        const uint32_t r = workgroup_max(mm, red);
+        if (ok_s == 0u) {
+            result_s = direct_amax(p, red);
+        } else if (threadIdx.x == 0) {
+            result_s = r;
+        }
+        __syncthreads();
+        const uint32_t amax = result_s;
+        if (threadIdx.x == 0) {
+            ws_store(&ws[kWsAmax], amax);
+            if (ok_s == 0u)
+                __hip_atomic_fetch_add(&ws[kWsSlow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads)
+            slot_store(&ws[kWsRelease + 2 * i], gen, amax);
+        __syncthreads();
+        if (threadIdx.x == 0)
+            ws_store(&ws[kWsGen], gen);
+        return amax;
+    }
+    if (threadIdx.x == 0) {
+        uint64_t w = slot_load(&ws[kWsRelease + 2 * blockIdx.x]);
+        ok_s = 1u;
+        while ((uint32_t)w != gen) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+                ok_s = 0u;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(4);
+            w = slot_load(&ws[kWsRelease + 2 * blockIdx.x]);
+        }
+        result_s = (uint32_t)(w >> 32);
+    }
+    __syncthreads();
+    if (ok_s == 0u) {
+        const uint32_t amax = direct_amax(p, red);
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(&ws[kWsSlow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return amax;
+    }
+    return result_s;
+}
+
+template <bool ROW, bool COL, bool SR>
+__global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint32_t* ws)
+{
+    __shared__ uint2 lds_codes[COL ? kTileC * kRowBlocks : 1];
+    __shared__ uint8_t lds_scales[COL ? kTileC * kRowBlocks : 16];
+    __shared__ float lds_rcp[128];
+
+    const int nt = p.tiles_r * p.tiles_c;
+    const int ta = blockIdx.x;
+    const int tb = blockIdx.x + gridDim.x;
+    const bool has_b = tb < nt;  // uniform over the workgroup
+    const ItemPos qa = item_pos(ta % p.tiles_r, ta / p.tiles_r, p.rows, p.cols);
+    const ItemPos qb = item_pos(tb % p.tiles_r, tb / p.tiles_r, p.rows, p.cols);
+    uint4 va[16], vb[16];
+    load_item(p, qa, va);
+    if (has_b)
+        load_item(p, qb, vb);
+
+    uint32_t pm = item_abs_max(qa, va, 0u);
+    if (has_b)
+        pm = item_abs_max(qb, vb, pm);
+    const uint32_t amax_bits = grid_max(max(pm & 0xFFFFu, pm >> 16) << 16, ws, p);
+
+    const float sg = global_scale_from_amax(__uint_as_float(amax_bits));
+    const float t6 = 6.0f * sg;
+    if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+        *p.sg_out = sg;
+    build_reciprocal_table(lds_rcp, sg);
+    __syncthreads();
+
+    if (qa.valid)
+        compute_item<ROW, COL, false, SR, false>(p, qa, va, sg, t6, lds_rcp, lds_codes, lds_scales);
+    if (COL) {
+        __syncthreads();
+        write_col_tile<false>(p, qa.tile_r0, qa.tile_c0, lds_codes, lds_scales);
+    }
+    if (has_b) {
+        if (COL)
+            __syncthreads();
+        if (qb.valid)
+            compute_item<ROW, COL, false, SR, false>(p, qb, vb, sg, t6, lds_rcp, lds_codes, lds_scales);
+        if (COL) {
+            __syncthreads();
+            write_col_tile<false>(p, qb.tile_r0, qb.tile_c0, lds_codes, lds_scales);
+        }
+    }
+}
+
+// Workgroups of one fused kernel that fit on the device at once (cached).
+template <bool ROW, bool COL, bool SR>
+int fused_capacity()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0)
+        return c;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(quantize_fused_kernel<ROW, COL, SR>), kThreads, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    c = per_cu * cus;
+    if (c > 0)
+        cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+template <bool ROW, bool COL, bool SR>
+hipError_t launch_fused_variant(Params p, uint32_t* ws, hipStream_t stream, bool& launched)
+{
+    launched = false;
+    const int nt = p.tiles_r * p.tiles_c;
+    const int grid = (nt + 1) / 2;
+    if (grid > kMaxFusedBlocks || grid > fused_capacity<ROW, COL, SR>())
+        return hipSuccess;
+    hipLaunchKernelGGL((quantize_fused_kernel<ROW, COL, SR>), dim3(grid), dim3(kThreads), 0, stream, p,
+                       ws);
+    launched = true;
+    return hipGetLastError();
 }
 
 template <bool ROW, bool COL, bool TWO_D, bool SR, bool RHT>
@@ -291,6 +723,45 @@ hipError_t launch_variant(const Params& p, hipStream_t stream)
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
 {
+    if (a.fused_amax) {
+        Params p;
+        p.x = a.x;
+        p.rows = a.rows;
+        p.cols = a.cols;
+        p.amax = reinterpret_cast<const float*>(a.workspace);
+        p.mask = 0u;
+        p.seed_lo = (uint32_t)a.seed;
+        p.seed_hi = (uint32_t)(a.seed >> 32);
+        p.codes_row = a.codes_row;
+        p.scales_row = a.scales_row;
+        p.codes_col = a.codes_col;
+        p.scales_col = a.scales_col;
+        p.sg_out = a.global_scale;
+        p.tiles_r = (int)((a.rows + kTileR - 1) / kTileR);
+        p.tiles_c = (int)((a.cols + kTileC - 1) / kTileC);
+        bool launched = false;
+        hipError_t e;
+        if (a.rowwise && a.colwise)
+            e = a.sr ? launch_fused_variant<true, true, true>(p, a.workspace, stream, launched)
+                     : launch_fused_variant<true, true, false>(p, a.workspace, stream, launched);
+        else if (a.rowwise)
+            e = a.sr ? launch_fused_variant<true, false, true>(p, a.workspace, stream, launched)
+                     : launch_fused_variant<true, false, false>(p, a.workspace, stream, launched);
+        else
+            e = a.sr ? launch_fused_variant<false, true, true>(p, a.workspace, stream, launched)
+                     : launch_fused_variant<false, true, false>(p, a.workspace, stream, launched);
+        if (e != hipSuccess || launched)
+            return e;
+        // Too large to keep on chip: the two-pass path, amax into the workspace.
+        float* amax = reinterpret_cast<float*>(a.workspace);
+        e = launch_amax(a.x, a.rows * a.cols, amax, stream);
+        if (e != hipSuccess)
+            return e;
+        QuantizeArgs b = a;
+        b.fused_amax = false;
+        b.amax = amax;
+        return launch_quantize(b, stream);
+    }
     Params p;
     p.x = a.x;
     p.rows = a.rows;

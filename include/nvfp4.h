@@ -54,6 +54,10 @@ extern "C" {
 #define NVFP4_COLWISE 0x2u /* blocks of 16 consecutive rows of one column   */
 #define NVFP4_SR 0x4u      /* stochastic rounding (gradients) instead of RNE */
 #define NVFP4_RHT 0x8u     /* random-sign 16-point Hadamard along rows first */
+#define NVFP4_FUSED_AMAX 0x10u /* compute the amax inside nvfp4_quantize_1d  */
+
+/* Size of the workspace nvfp4_quantize_1d takes with NVFP4_FUSED_AMAX. */
+#define NVFP4_WORKSPACE_BYTES 32832
 
 /* scale_mode values */
 #define NVFP4_SCALE_1D 1 /* one scale per 16 consecutive elements of a row */
@@ -111,6 +115,18 @@ int nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags, ui
  * Per block: s = e4m3_rne(b / (6*S_g)) with b the block's max |x| (after
  * the transform with NVFP4_RHT); each element is |x| * (1 / (s*S_g))
  * rounded to E2M1 (ties to even, saturating at 6) or stochastically.
+ *
+ * NVFP4_FUSED_AMAX (not with NVFP4_RHT): the call computes the tensor amax
+ * itself, in the same pass over x when the tensor fits on chip (the data
+ * stays in registers between the amax and the encoding, so x is read from
+ * memory once). `amax` then points to a caller-owned device workspace of
+ * NVFP4_WORKSPACE_BYTES bytes, zero-filled before its first use and reused
+ * as is afterwards; its first float receives the amax (exactly what
+ * nvfp4_amax would give). The single pass needs all of its workgroups on
+ * the device at once; if they are not (another kernel holds the device),
+ * a bounded wait expires, the amax is computed from x directly (same
+ * result, slower) and 32-bit word 2 of the workspace is incremented. Calls
+ * that overlap in time must use different workspaces.
  */
 int nvfp4_quantize_1d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
                       uint32_t flags, uint16_t rht_mask, uint64_t seed, uint8_t* codes_row,

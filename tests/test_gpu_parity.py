@@ -379,3 +379,44 @@ def test_gemm_bf16_output_is_rounded_fp32():
     err16, c16 = gemm_check(a, b, np.arange(272), out_dtype=torch.bfloat16)
     assert np.array_equal(W.f32_to_bf16_bits(c32), W.f32_to_bf16_bits(c16))
     assert err16 <= 2.0 ** -8
+
+
+# ------------------------------------------------ fused amax + quantize
+
+@pytest.mark.parametrize("name,sr", [("act_small", False), ("ragged_act", False), ("ragged_act", True),
+                                     ("act", False), ("act", True), ("grad", False)])
+@pytest.mark.parametrize("layouts", [(True, True), (True, False), (False, True)])
+def test_fused_amax_quantize(name, sr, layouts):
+    """One call computes the amax and quantizes (a single pass over the
+    tensor when it fits on chip, else the two-pass path): bit-identical to
+    the oracle, and to the two-call path."""
+    rowwise, colwise = layouts
+    x = wl(name)
+    log(f"[test_fused_amax_quantize] {name} sr={sr} layouts={layouts}")
+    xd = dev(x)
+    ws = F.nvfp4_workspace()
+    got = None
+    for rep in range(2):  # the workspace is reused as is
+        out = F.nvfp4_quantize_1d(xd, ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED, fused_amax=True)
+        torch.cuda.synchronize()
+        got = {k: host(v) for k, v in out.items()}
+        wsh = host(ws)
+        assert wsh[2] == 0, "in-kernel exchange fell back to the slow path"
+        amax_gpu = wsh[:1].view(np.float32)[0]
+        check_q1(x, got, amax_gpu, rowwise, colwise, sr, False,
+                 rows=None if x.shape[0] <= 512 else sample_idx(x.shape[0], 16, 7 + rep),
+                 cols=None if x.shape[1] <= 1024 else sample_idx(x.shape[1], 16, 9 + rep))
+    two, _ = run_q1(x, rowwise, colwise, sr=sr)
+    for k in two:
+        assert np.array_equal(got[k], two[k]), k
+
+
+def test_fused_workspace_across_tensors():
+    """Consecutive fused calls on different tensors through one workspace."""
+    ws = F.nvfp4_workspace()
+    for seed, scale in ((21, 1.0), (22, 1e-3), (23, 300.0)):
+        x = W.f32_to_bf16_bits(W.bf16_bits_to_f32(W.activation(640, 768, seed=seed)) * np.float32(scale))
+        out = F.nvfp4_quantize_1d(dev(x), ws, rowwise=True, colwise=True, fused_amax=True)
+        torch.cuda.synchronize()
+        got = {k: host(v) for k, v in out.items()}
+        check_q1(x, got, host(ws)[:1].view(np.float32)[0], True, True, False, False)
