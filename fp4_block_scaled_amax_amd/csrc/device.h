@@ -127,6 +127,24 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t b_bits, float sg, flo
     return out;
 }
 
+// Same byte, cheaper: one multiply by inv_t = fl(1/t) instead of the IEEE
+// division. y = fl(b * inv_t) is within 3 ulp of fl(b / t), so both round to
+// the same E4M3 value unless an E4M3 rounding midpoint lies within 3 ulp of y
+// (low 20 mantissa bits within 3 of 0x80000) or y is in the E4M3 subnormal
+// range (below 2^-6, different rounding granularity); those lanes take the
+// exact division. Requires t > 0 with t and inv_t finite (then b <= amax is
+// finite and y <= 448 * (1 + 2^-22)).
+__device__ __forceinline__ uint32_t block_scale_byte_fast(uint32_t b_bits, float t, float inv_t)
+{
+    const float b = __uint_as_float(b_bits);
+    float y = b * inv_t;
+    const uint32_t u = __float_as_uint(y);
+    if (!(y >= 0.015625f) || (((u & 0xFFFFFu) - 0x7FFFDu) < 7u))
+        return block_scale_byte(b_bits, t);
+    const uint32_t r = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+    return r < 0x7Eu ? r : 0x7Eu;  // 432 and above round to (or saturate at) 448
+}
+
 // The 128 possible multipliers of a tensor (one per scale byte 0..127),
 // built once per workgroup in LDS by the first 128 threads.
 __device__ __forceinline__ void build_reciprocal_table(float* table, float sg)

@@ -98,14 +98,22 @@ __device__ __forceinline__ uint32_t cvt_pair(uint32_t old, float a, float b)
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, BYTE);
 }
 
+// A fresh word whose bytes will all be written: its initial contents do not
+// matter, so let the compiler pick any register (no zero-fill).
+__device__ __forceinline__ uint32_t fresh_word() { return __builtin_nondeterministic_value(0u); }
+
 template <int MODE, int BYTE>
 __device__ __forceinline__ uint32_t put_pair(uint32_t word, float a, float b, float r, uint32_t ha,
                                              uint32_t hb)
 {
     if (MODE == kEncHw)
         return cvt_pair<BYTE>(word, a * r, b * r);
-    if (MODE == kEncHwSafe)
-        return cvt_pair<BYTE>(word, nan_to_signed_zero(a * r, a), nan_to_signed_zero(b * r, b));
+    if (MODE == kEncHwSafe) {
+        // fma(x, r, -0) equals x * r for every input; spelling it differently
+        // keeps the compiler from sharing (and hoisting) it with the fast path.
+        return cvt_pair<BYTE>(word, nan_to_signed_zero(__builtin_fmaf(a, r, -0.0f), a),
+                              nan_to_signed_zero(__builtin_fmaf(b, r, -0.0f), b));
+    }
     const uint32_t lo = e2m1_sr_nibble(fabsf(a) * r, ha, (__float_as_uint(a) >> 28) & 8u);
     const uint32_t hi = e2m1_sr_nibble(fabsf(b) * r, hb, (__float_as_uint(b) >> 28) & 8u);
     return word | ((lo | (hi << 4)) << (8 * BYTE));
@@ -116,7 +124,7 @@ template <int MODE>
 __device__ __forceinline__ uint2 encode_column16(const float (&y)[16], float r,
                                                  const uint4 (&draws)[16], int j)
 {
-    uint32_t w[2] = {0u, 0u};
+    uint32_t w[2] = {MODE == kEncSr ? 0u : fresh_word(), MODE == kEncSr ? 0u : fresh_word()};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #define NVFP4_PAIR(B)                                                                      \
@@ -143,7 +151,12 @@ __device__ __forceinline__ void encode_row_pair(const uint4 (&v)[16], const floa
     constexpr int i = 2 * IP;
     constexpr int cb = IP & 3;     // byte within the column word
     constexpr int ch = IP >> 2;    // which column word (rows 0..7 or 8..15)
-    roww[0] = roww[1] = 0u;
+    roww[0] = roww[1] = MODE == kEncSr ? 0u : fresh_word();
+    if (MODE != kEncSr && COL && cb == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            colw[j][ch] = fresh_word();
+    }
 #define NVFP4_GROUP(K)                                                                      \
     {                                                                                       \
         const uint32_t w0 = word_at(v[i], K), w1 = word_at(v[i + 1], K);                    \
@@ -220,19 +233,56 @@ __device__ __forceinline__ void load_item(const Params& p, const ItemPos& q, uin
     }
 }
 
+// Column maxima of an item (binary32 bits of max |x| over its 16 rows), from
+// packed u16 maxima of the |bf16| patterns.
+__device__ __forceinline__ void column_maxima(const uint4 (&v)[16], uint32_t (&cmax)[8])
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t pm = 0u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            pm = pk_max_u16(pm, word_at(v[i], k) & 0x7FFF7FFFu);
+        cmax[2 * k] = pm << 16;
+        cmax[2 * k + 1] = pm & 0xFFFF0000u;
+    }
+}
+
+// Per-tensor constants of the scale chain.
+struct ScaleCtx {
+    float sg, t6, inv_t6;
+    bool fast;  // t6 > 0 with t6 and 1/t6 finite: block_scale_byte_fast applies
+};
+
+__device__ __forceinline__ ScaleCtx scale_ctx(float amax)
+{
+    ScaleCtx c;
+    c.sg = global_scale_from_amax(amax);
+    c.t6 = 6.0f * c.sg;
+    c.inv_t6 = 1.0f / c.t6;
+    c.fast = c.t6 > 0.0f && finite_bits(c.t6) && finite_bits(c.inv_t6);
+    return c;
+}
+
+__device__ __forceinline__ uint32_t scale_byte(uint32_t b_bits, const ScaleCtx& c)
+{
+    return c.fast ? block_scale_byte_fast(b_bits, c.t6, c.inv_t6) : block_scale_byte(b_bits, c.t6);
+}
+
 // Quantize one work item held in registers: block scales, codes; rowwise
 // outputs go straight to memory, columnwise outputs to the LDS staging.
+// cmax: the item's column maxima (ignored with RHT, which recomputes them
+// from the transformed values).
 template <bool ROW, bool COL, bool TWO_D, bool SR, bool RHT>
 __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
-                                             const uint4 (&v)[16], float sg, float t6,
-                                             const float* lds_rcp, uint2* lds_codes,
-                                             uint8_t* lds_scales)
+                                             const uint4 (&v)[16], const uint32_t (&cmax)[8],
+                                             const ScaleCtx& sc, const float* lds_rcp,
+                                             uint2* lds_codes, uint8_t* lds_scales)
 {
-    const int64_t rows = p.rows, cols = p.cols;
+    const int64_t cols = p.cols;
     const int64_t r0 = q.r0, c0 = q.c0;
     const int rb = q.rb, cg = q.cg;
     const bool odd = q.odd;
-    (void)rows;
     // Stochastic-rounding draws: one Philox call per row covers the
     // item's 8 consecutive flat indices.
     uint4 draws[16];
@@ -240,25 +290,13 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
         const uint64_t flat0 = (uint64_t)(r0 * cols + c0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const uint64_t q = (flat0 + (uint64_t)i * (uint64_t)cols) >> 3;
-            draws[i] = philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), p.seed_lo, p.seed_hi);
+            const uint64_t qq = (flat0 + (uint64_t)i * (uint64_t)cols) >> 3;
+            draws[i] = philox4x32_10((uint32_t)qq, (uint32_t)(qq >> 32), p.seed_lo, p.seed_hi);
         }
     }
 
     if (COL && !ROW && !TWO_D) {
-        // ------------------------------------------ columnwise only
-        uint32_t cmax[8];
-        if (!RHT) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                uint32_t pm = 0u;
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    pm = pk_max_u16(pm, word_at(v[i], k) & 0x7FFF7FFFu);
-                cmax[2 * k] = pm << 16;
-                cmax[2 * k + 1] = pm & 0xFFFF0000u;
-            }
-        }
+        // -------------------------------------------- columnwise only
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             float y[16];
@@ -275,7 +313,7 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
             } else {
                 m = cmax[j];
             }
-            const uint32_t byte = block_scale_byte(m, t6);
+            const uint32_t byte = scale_byte(m, sc);
             const float r = lds_rcp[byte];
             uint2 words;
             if (SR)
@@ -288,97 +326,86 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
             lds_codes[col * kRowBlocks + (rb ^ (cg & 7))] = words;
             lds_scales[col * kRowBlocks + rb] = (uint8_t)byte;
         }
-    } else {
-        // ------------------------- rowwise, rowwise + columnwise, 2D
-        uint32_t cmax[8];
-        if (COL || TWO_D) {
+        return;
+    }
+
+    // ----------------------------- rowwise, rowwise + columnwise, 2D
+    float rc[8];   // columnwise multipliers (1D), or the tile's (2D)
+    float rr[16];  // rowwise multipliers (1D), or the tile's (2D)
+    uint32_t col_byte[8];
+    bool fin = true;
+    if (TWO_D) {
+        uint32_t m = cmax[0];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                uint32_t pm = 0u;
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    pm = pk_max_u16(pm, word_at(v[i], k) & 0x7FFF7FFFu);
-                cmax[2 * k] = pm << 16;
-                cmax[2 * k + 1] = pm & 0xFFFF0000u;
-            }
-        }
-        float rc[8];   // columnwise multipliers (1D), or the tile's (2D)
-        float rr[16];  // rowwise multipliers (1D), or the tile's (2D)
-        uint32_t col_byte[8];
-        bool fin = true;
-        if (TWO_D) {
-            uint32_t m = cmax[0];
-#pragma unroll
-            for (int j = 1; j < 8; ++j)
-                m = max(m, cmax[j]);
-            m = max(m, swap_lane1(m));
-            const uint32_t byte = block_scale_byte(m, t6);
-            const float r = lds_rcp[byte];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                rc[j] = r;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                rr[i] = r;
-            fin = finite_bits(r);
-            if (!odd)
-                p.scales_row[(r0 >> 4) * (cols >> 4) + (c0 >> 4)] = (uint8_t)byte;
-        } else {
-            if (COL) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    col_byte[j] = block_scale_byte(cmax[j], t6);
-                    rc[j] = lds_rcp[col_byte[j]];
-                    fin = fin && finite_bits(rc[j]);
-                }
-            }
-            if (ROW) {
-                uint32_t rm[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const uint32_t pm =
-                        pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
-                                   pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu));
-                    rm[i] = max(pm & 0xFFFFu, pm >> 16) << 16;
-                }
-                // Even lanes own rows 0..7 of the pair's blocks, odd lanes 8..15.
-                const int64_t srow0 = r0 + (odd ? 8 : 0);
-                uint8_t* sdst = p.scales_row + srow0 * (cols >> 4) + (c0 >> 4);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const uint32_t send = odd ? rm[k] : rm[k + 8];
-                    const uint32_t recv = swap_lane1(send);
-                    const uint32_t own = odd ? rm[k + 8] : rm[k];
-                    const uint32_t byte = block_scale_byte(max(own, recv), t6);
-                    sdst[k * (cols >> 4)] = (uint8_t)byte;
-                    const float mine = lds_rcp[byte];
-                    const float other = swap_lane1(mine);
-                    rr[k] = odd ? other : mine;
-                    rr[k + 8] = odd ? mine : other;
-                    fin = fin && finite_bits(mine);
-                }
-            }
-        }
-        uint32_t colw[8][2];
+        for (int j = 1; j < 8; ++j)
+            m = max(m, cmax[j]);
+        m = max(m, swap_lane1(m));
+        const uint32_t byte = scale_byte(m, sc);
+        const float r = lds_rcp[byte];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            colw[j][0] = colw[j][1] = 0u;
-        uint8_t* row_dst = ROW ? p.codes_row + r0 * (cols >> 1) + (c0 >> 1) : nullptr;
-        const int64_t row_pitch = cols >> 1;
-        if (SR)
-            encode_item<kEncSr, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
-        else if (__all(fin))
-            encode_item<kEncHw, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
-        else
-            encode_item<kEncHwSafe, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
+            rc[j] = r;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            rr[i] = r;
+        fin = finite_bits(r);
+        if (!odd)
+            p.scales_row[(r0 >> 4) * (cols >> 4) + (c0 >> 4)] = (uint8_t)byte;
+    } else {
         if (COL) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int col = cg * 8 + j;
-                lds_codes[col * kRowBlocks + (rb ^ (cg & 7))] = make_uint2(colw[j][0], colw[j][1]);
-                if (!TWO_D)
-                    lds_scales[col * kRowBlocks + rb] = (uint8_t)col_byte[j];
+                col_byte[j] = scale_byte(cmax[j], sc);
+                rc[j] = lds_rcp[col_byte[j]];
+                fin = fin && finite_bits(rc[j]);
             }
+        }
+        if (ROW) {
+            uint32_t rm[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t pm =
+                    pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
+                               pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu));
+                rm[i] = max(pm & 0xFFFFu, pm >> 16) << 16;
+            }
+            // Even lanes own rows 0..7 of the pair's blocks, odd lanes 8..15.
+            const int64_t srow0 = r0 + (odd ? 8 : 0);
+            uint8_t* sdst = p.scales_row + srow0 * (cols >> 4) + (c0 >> 4);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t send = odd ? rm[k] : rm[k + 8];
+                const uint32_t recv = swap_lane1(send);
+                const uint32_t own = odd ? rm[k + 8] : rm[k];
+                const uint32_t byte = scale_byte(max(own, recv), sc);
+                sdst[k * (cols >> 4)] = (uint8_t)byte;
+                const float mine = lds_rcp[byte];
+                const float other = swap_lane1(mine);
+                rr[k] = odd ? other : mine;
+                rr[k + 8] = odd ? mine : other;
+                fin = fin && finite_bits(mine);
+            }
+        }
+    }
+    uint32_t colw[8][2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        colw[j][0] = colw[j][1] = 0u;
+    uint8_t* row_dst = ROW ? p.codes_row + r0 * (cols >> 1) + (c0 >> 1) : nullptr;
+    const int64_t row_pitch = cols >> 1;
+    if (SR)
+        encode_item<kEncSr, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
+    else if (__all(fin))
+        encode_item<kEncHw, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
+    else
+        encode_item<kEncHwSafe, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
+    if (COL) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int col = cg * 8 + j;
+            lds_codes[col * kRowBlocks + (rb ^ (cg & 7))] = make_uint2(colw[j][0], colw[j][1]);
+            if (!TWO_D)
+                lds_scales[col * kRowBlocks + rb] = (uint8_t)col_byte[j];
         }
     }
 }
@@ -437,16 +464,18 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
     uint4 v[16];
     load_item(p, q, v);
 
-    const float amax = *p.amax;
-    const float sg = global_scale_from_amax(amax);
-    const float t6 = 6.0f * sg;
+    const ScaleCtx sc = scale_ctx(*p.amax);
     if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
-        *p.sg_out = sg;
-    build_reciprocal_table(lds_rcp, sg);
+        *p.sg_out = sc.sg;
+    build_reciprocal_table(lds_rcp, sc.sg);
     __syncthreads();
 
-    if (q.valid)
-        compute_item<ROW, COL, TWO_D, SR, RHT>(p, q, v, sg, t6, lds_rcp, lds_codes, lds_scales);
+    if (q.valid) {
+        uint32_t cmax[8];
+        if (!RHT)
+            column_maxima(v, cmax);
+        compute_item<ROW, COL, TWO_D, SR, RHT>(p, q, v, cmax, sc, lds_rcp, lds_codes, lds_scales);
+    }
     if (COL) {
         __syncthreads();
         write_col_tile<TWO_D>(p, q.tile_r0, q.tile_c0, lds_codes, lds_scales);
@@ -497,20 +526,6 @@ __device__ __forceinline__ void slot_store(uint32_t* a, uint32_t gen, uint32_t v
 {
     __hip_atomic_store(reinterpret_cast<uint64_t*>(a), ((uint64_t)value << 32) | gen,
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint32_t item_abs_max(const ItemPos& q, const uint4 (&v)[16], uint32_t pm)
-{
-    if (q.valid) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            pm = pk_max_u16(pm, v[i].x & 0x7FFF7FFFu);
-            pm = pk_max_u16(pm, v[i].y & 0x7FFF7FFFu);
-            pm = pk_max_u16(pm, v[i].z & 0x7FFF7FFFu);
-            pm = pk_max_u16(pm, v[i].w & 0x7FFF7FFFu);
-        }
-    }
-    return pm;
 }
 
 // Maximum over the workgroup; every thread gets the result.
@@ -643,20 +658,31 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
     if (has_b)
         load_item(p, qb, vb);
 
-    uint32_t pm = item_abs_max(qa, va, 0u);
-    if (has_b)
-        pm = item_abs_max(qb, vb, pm);
-    const uint32_t amax_bits = grid_max(max(pm & 0xFFFFu, pm >> 16) << 16, ws, p);
+    // Column maxima while the data arrives; the block-local amax follows.
+    uint32_t ca[8], cb[8];
+    uint32_t m = 0u;
+    if (qa.valid) {
+        column_maxima(va, ca);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            m = max(m, ca[j]);
+    }
+    if (has_b && qb.valid) {
+        column_maxima(vb, cb);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            m = max(m, cb[j]);
+    }
+    const uint32_t amax_bits = grid_max(m, ws, p);
 
-    const float sg = global_scale_from_amax(__uint_as_float(amax_bits));
-    const float t6 = 6.0f * sg;
+    const ScaleCtx sc = scale_ctx(__uint_as_float(amax_bits));
     if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
-        *p.sg_out = sg;
-    build_reciprocal_table(lds_rcp, sg);
+        *p.sg_out = sc.sg;
+    build_reciprocal_table(lds_rcp, sc.sg);
     __syncthreads();
 
     if (qa.valid)
-        compute_item<ROW, COL, false, SR, false>(p, qa, va, sg, t6, lds_rcp, lds_codes, lds_scales);
+        compute_item<ROW, COL, false, SR, false>(p, qa, va, ca, sc, lds_rcp, lds_codes, lds_scales);
     if (COL) {
         __syncthreads();
         write_col_tile<false>(p, qa.tile_r0, qa.tile_c0, lds_codes, lds_scales);
@@ -665,7 +691,7 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
         if (COL)
             __syncthreads();
         if (qb.valid)
-            compute_item<ROW, COL, false, SR, false>(p, qb, vb, sg, t6, lds_rcp, lds_codes, lds_scales);
+            compute_item<ROW, COL, false, SR, false>(p, qb, vb, cb, sc, lds_rcp, lds_codes, lds_scales);
         if (COL) {
             __syncthreads();
             write_col_tile<false>(p, qb.tile_r0, qb.tile_c0, lds_codes, lds_scales);
