@@ -39,7 +39,7 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 (= bf16) matrix peak, TFLOP/s
 # Plain vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one op per lane
 # per clock, no packed math).
 VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
@@ -191,14 +191,14 @@ def main():
     rows = {}
     gemm_tflops = None
     if not args.no_rows:
-        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
 
         def timed(fn, iters=args.row_iters):
             fn()
             torch.cuda.synchronize()
             ts = []
             for _ in range(iters):
-                flush.zero_()  # evict the Infinity Cache between launches
+                flush.max()  # read 512 MiB: evicts the Infinity Cache, leaves no dirty lines
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
@@ -300,14 +300,20 @@ def main():
         c32 = torch.empty((M, N), dtype=torch.float32, device=dev)
         c16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         flop = 2.0 * M * N * K
+        # sustained matrix work raises the clock over the first tens of ms:
+        # time only after ~50 ms of it
+        for _ in range(50):
+            F.nvfp4_gemm(qa["codes_row"], qa["scales_row"], 1, qa["global_scale"], qb["codes_row"],
+                         qb["scales"], 2, qb["global_scale"], M, N, K, out=c32)
+        torch.cuda.synchronize()
         for name, cc, dt in (("gemm_fp32_out", c32, torch.float32), ("gemm_bf16_out", c16, torch.bfloat16)):
             us = timed(lambda: F.nvfp4_gemm(qa["codes_row"], qa["scales_row"], 1, qa["global_scale"],
                                             qb["codes_row"], qb["scales"], 2, qb["global_scale"], M, N, K,
                                             out_dtype=dt, out=cc), iters=max(3, args.row_iters // 2))
             tf = flop / (us * 1e-6) / 1e12
             rows[name] = {"shape": [M, N, K], "us": round(us, 1), "flop": flop, "TFLOP/s": round(tf, 1),
-                          "bound": "mfma", "peak": BF16_MFMA_PEAK_TFLOPS,
-                          "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+                          "bound": "mfma", "peak": F16_MFMA_PEAK_TFLOPS,
+                          "frac": round(tf / F16_MFMA_PEAK_TFLOPS, 4)}
             log(f"[bench] {name}: {us:.0f} us {tf:.1f} TFLOP/s")
         gemm_tflops = rows["gemm_fp32_out"]["TFLOP/s"]
         del flush

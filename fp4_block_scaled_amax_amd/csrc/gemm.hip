@@ -2,22 +2,28 @@
 // TN layout (both operands K-contiguous).
 //
 // Every operand element e2m1(code) * e4m3(scale) has at most 6 significant
-// bits and lies in [2^-10, 2688], so it is exact in bf16; products are summed
-// in fp32 by v_mfma_f32_32x32x16_bf16. One MFMA consumes K = 16, exactly one
+// bits and lies in [2^-10, 2688], so it is exact in fp16; products are summed
+// in fp32 by v_mfma_f32_32x32x16_f16. One MFMA consumes K = 16, exactly one
 // NVFP4 scale block.
 //
-// Structure (one workgroup = 8 waves, a 256 x 256 tile of C):
+// Structure (one workgroup = 8 waves, a 256 x 256 tile of C at a time):
 //   - K advances 32 at a time. Each of the 512 threads owns one row (256 of
 //     A, then 256 of B) for the stage: it loads 16 bytes of packed codes and
-//     the two scale bytes, decodes the 32 codes (hardware FP4 -> fp32
-//     convert, times the scale, exact; packed to bf16, exact) and writes them
-//     to LDS. Each element is decoded once per workgroup.
-//   - LDS rows are 80 bytes apart (32 bf16 + 16 bytes of padding) so the
+//     the two scale bytes and decodes the 32 codes into LDS. Decoding is
+//     three exact hardware steps: both scale bytes to fp16 in one E4M3
+//     convert, two codes to fp16 per E2M1 convert, one packed fp16 multiply
+//     per two codes. Each element is decoded once per workgroup.
+//   - LDS rows are 80 bytes apart (32 fp16 + 16 bytes of padding) so the
 //     16-byte operand reads of 8 consecutive rows hit distinct banks.
 //   - Waves form a 4 x 2 grid; each computes a 64 x 128 sub-tile (2 x 4 MFMA
 //     tiles, 128 fp32 accumulators per lane), so two waves share a SIMD and
 //     one's decode overlaps the other's MFMAs. Stages are double-buffered in
-//     LDS, and the packed codes are fetched two stages ahead.
+//     LDS, and the packed codes are fetched two stages ahead into two
+//     alternating register sets.
+//   - The grid is persistent (one workgroup per CU); a tile's output stores
+//     drain while the next tile starts.
+#include <atomic>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -25,8 +31,8 @@ namespace nvfp4 {
 
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(16))) float floatx16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
@@ -34,79 +40,78 @@ constexpr int kThreads = 512;
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 32;
-constexpr int kRowBytes = kBK * 2 + 16;          // 80: padded LDS row of bf16
+constexpr int kRowBytes = kBK * 2 + 16;          // 80: padded LDS row of fp16
 constexpr int kStageBytes = (kBM + kBN) * kRowBytes;  // A rows then B rows
+constexpr int kGroupM = 4;  // tile rows per group of the tile order
 
-// E4M3 scale byte -> binary32, branch-free (0x7F decodes to NaN).
-__device__ __forceinline__ float scale_value(uint32_t b)
-{
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    const float sub = (float)m * 0.001953125f;  // exponent field 0: m * 2^-9
-    const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
-    const float v = e == 0u ? sub : nrm;
-    return b == 0x7Fu ? __uint_as_float(0x7FC00000u) : v;
-}
-
-// Two codes (byte SEL of `w`) times scale s -> two bf16 packed in a dword.
+// Byte SEL of `w` (two codes) -> two fp16, times the packed pair `s2`
+// (both halves the block's scale). Both converts are exact: E2M1 and E4M3
+// values are fp16 values, and so is their product (at most 6 significant
+// bits, magnitude in [2^-10, 2688]).
 template <int SEL>
-__device__ __forceinline__ uint32_t decode_pair(uint32_t w, float s)
+__device__ __forceinline__ uint32_t decode_pair(uint32_t w, f16x2 s2)
 {
-    const auto g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-    const float a = g[0] * s, b = g[1] * s;  // exact: <= 6 significant bits
-    const bf16x2 p = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32 (exact here)
-    return __builtin_bit_cast(uint32_t, p);
+    const auto g = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, g) * s2);
 }
 
 // One row's packed codes for a K stage: 16 bytes (32 codes) and the two
 // scale bytes (low byte: first 16 codes).
 struct RowStage {
     uint4 codes;
-    uint32_t scales;
+    uint16_t scales;
 };
 
-// Fetch stage `stage` of this thread's row; rows past the end read row 0
-// of the operand and are zeroed (codes and scales 0 decode to 0).
+// Scale bytes read by rows past the end of an operand: scale 0 makes every
+// code of such a row decode to zero without touching the loaded values.
+__device__ __attribute__((aligned(16))) const uint8_t kZeroScales[16] = {};
+
+// Fetch stage `stage` of this thread's row: 16 bytes of codes and the two
+// scale bytes at scale_row + stage * sstride (sstride 0 for rows past the
+// end, which read kZeroScales).
 template <bool WIDE>
 __device__ __forceinline__ RowStage fetch_stage(const uint8_t* code_row, const uint8_t* scale_row,
-                                                int stage, int64_t K, bool valid)
+                                                int stage, int sstride, int64_t K)
 {
     RowStage st;
     const int64_t k0 = (int64_t)stage * kBK;
+    const uint8_t* sp = scale_row + (int64_t)stage * sstride;
     if (WIDE) {
         st.codes = load16(code_row + (k0 >> 1));
-        st.scales = *reinterpret_cast<const uint16_t*>(scale_row + (k0 >> 4));
+        st.scales = *(const __attribute__((address_space(1))) uint16_t*)sp;
     } else {
         // K is an odd multiple of 16: the last stage has one block.
         const bool has2 = k0 + 16 < K;
         const uint2 lo = *reinterpret_cast<const uint2*>(code_row + (k0 >> 1));
         const uint2 hi = has2 ? *reinterpret_cast<const uint2*>(code_row + (k0 >> 1) + 8) : make_uint2(0u, 0u);
         st.codes = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        st.scales = scale_row[k0 >> 4] | (has2 ? (uint32_t)scale_row[(k0 >> 4) + 1] << 8 : 0u);
-    }
-    if (!valid) {
-        st.codes = make_uint4(0u, 0u, 0u, 0u);
-        st.scales = 0u;
+        const __attribute__((address_space(1))) uint8_t* gp =
+            (const __attribute__((address_space(1))) uint8_t*)sp;
+        st.scales = (uint16_t)(gp[0] | (has2 ? (uint32_t)gp[sstride >> 1] << 8 : 0u));
     }
     return st;
 }
 
-// Decode one row's stage and write its 32 bf16 (64 bytes) to LDS.
+// Decode one row's stage and write its 32 fp16 (64 bytes) to LDS.
 __device__ __forceinline__ void decode_stage_to_lds(const RowStage& st, uint8_t* lds_row)
 {
-    const float s0 = scale_value(st.scales & 0xFFu), s1 = scale_value((st.scales >> 8) & 0xFFu);
+    // Both scale bytes to fp16 in one convert.
+    const auto sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.scales, 1.0f, false);
+    const f16x2 s = __builtin_bit_cast(f16x2, sc);
+    const f16x2 s0 = {s[0], s[0]}, s1 = {s[1], s[1]};
     const uint32_t w[4] = {st.codes.x, st.codes.y, st.codes.z, st.codes.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const float sc = q < 2 ? s0 : s1;
-        const u32x4 o = {decode_pair<0>(w[q], sc), decode_pair<1>(w[q], sc), decode_pair<2>(w[q], sc),
-                         decode_pair<3>(w[q], sc)};
+        const f16x2 sq = q < 2 ? s0 : s1;
+        const u32x4 o = {decode_pair<0>(w[q], sq), decode_pair<1>(w[q], sq), decode_pair<2>(w[q], sq),
+                         decode_pair<3>(w[q], sq)};
         *reinterpret_cast<u32x4*>(lds_row + 16 * q) = o;
     }
 }
 
-__device__ __forceinline__ bf16x8 lds_fragment(const uint8_t* lds, int row, int kbyte)
+__device__ __forceinline__ f16x8 lds_fragment(const uint8_t* lds, int row, int kbyte)
 {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds + row * kRowBytes + kbyte));
+    return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(lds + row * kRowBytes + kbyte));
 }
 
 // The MFMAs of one stage for this wave's 64 x 128 sub-tile.
@@ -115,7 +120,7 @@ __device__ __forceinline__ void stage_mfma(const uint8_t* buf, int wm, int wn, i
 {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 fa[2], fb[4];
+        f16x8 fa[2], fb[4];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
             fa[a] = lds_fragment(buf, wm + a * 32 + frow, ks * 32 + fk);
@@ -126,23 +131,20 @@ __device__ __forceinline__ void stage_mfma(const uint8_t* buf, int wm, int wn, i
         for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[a], fb[b], acc[a][b], 0, 0, 0);
     }
 }
 
-// Workgroup -> output tile. Workgroups are dealt round-robin over the 8
-// XCDs; give each XCD a contiguous range of tiles, walked along N, so the
-// workgroups resident on one XCD share A rows in its L2.
-__device__ __forceinline__ void gemm_tile_of_block(int tiles_m, int tiles_n, int& tm, int& tn)
+// Position in the tile order of this workgroup's tile in round `round`.
+// Workgroups are dealt round-robin over the 8 XCDs; in each round give each
+// XCD a contiguous run of positions.
+__device__ __forceinline__ int gemm_tile_index(int round)
 {
-    const int nt = tiles_m * tiles_n;
-    int t = blockIdx.x;
-    if ((nt & 7) == 0) {
-        const int per = nt >> 3;
-        t = (t & 7) * per + (t >> 3);
-    }
-    tm = t / tiles_n;
-    tn = t % tiles_n;
+    const int G = gridDim.x;
+    int w = blockIdx.x;
+    if ((G & 7) == 0)
+        w = (w & 7) * (G >> 3) + (w >> 3);
+    return round * G + w;
 }
 
 template <bool BF16_OUT, bool WIDE>
@@ -150,77 +152,143 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
 
-    int tm, tn;
-    gemm_tile_of_block(tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
     const int64_t K = g.K;
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
     const int nstages = (int)((K + kBK - 1) / kBK);
-
-    // This thread's row: A rows 0..255, then B rows 0..255.
-    const bool is_b = t >= kBM;
-    const int64_t row = is_b ? n0 + (t - kBM) : m0 + t;
-    const int64_t rows = is_b ? g.N : g.M;
-    const bool valid = row < rows;
-    const int64_t rc = valid ? row : 0;
-    const uint8_t* code_row = (is_b ? g.b_codes : g.a_codes) + rc * (K >> 1);
-    const bool two_d = is_b ? g.b_two_d : g.a_two_d;
-    const uint8_t* scale_row = (is_b ? g.b_scales : g.a_scales) + (two_d ? (rc >> 4) : rc) * (K >> 4);
-    uint8_t* my_row0 = lds + t * kRowBytes;
-
-    floatx16 acc[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-            acc[a][b] = floatx16{};
-
     const int last = nstages - 1;
-    decode_stage_to_lds(fetch_stage<WIDE>(code_row, scale_row, 0, K, valid), my_row0);
-    RowStage st1 = fetch_stage<WIDE>(code_row, scale_row, min(1, last), K, valid);  // stage s+1
-    RowStage st2 = fetch_stage<WIDE>(code_row, scale_row, min(2, last), K, valid);  // stage s+2
-    __syncthreads();
-
     const int frow = lane & 31;
     const int fk = (lane >> 5) * 16;  // byte offset of the lane's 8 K-elements
-    for (int s = 0; s < nstages; ++s) {
-        const int cur = (s & 1) * kStageBytes;
-        // MFMAs of stage s; decode stage s+1 into the other buffer (after the
-        // last stage this decodes a repeat of it into the idle buffer).
-        stage_mfma(lds + cur, wm, wn, frow, fk, acc);
-        decode_stage_to_lds(st1, my_row0 + (kStageBytes - cur));
-        // (the compiler interleaves the decode with the MFMAs well enough; an
-        // explicit sched_group_barrier pattern measured slower)
-        st1 = st2;
-        st2 = fetch_stage<WIDE>(code_row, scale_row, min(s + 3, last), K, valid);
-        __syncthreads();
-    }
-
+    const bool is_b = t >= kBM;
+    const int64_t rows = is_b ? g.N : g.M;
+    const bool two_d = is_b ? g.b_two_d : g.a_two_d;
+    const uint8_t* codes = is_b ? g.b_codes : g.a_codes;
+    const uint8_t* scales = is_b ? g.b_scales : g.a_scales;
+    uint8_t* my_row0 = lds + t * kRowBytes;
     const float scale = (*g.a_sg) * (*g.b_sg);
+
+    // Persistent: each workgroup walks tiles; a tile's output stores drain
+    // while the next tile's first stages load and decode.
+    const int nt = tiles_m * tiles_n;
+    for (int round = 0;; ++round) {
+        const int tile = gemm_tile_index(round);
+        if (tile >= nt)
+            break;
+        // Tiles are ordered in groups of kGroupM tile rows, column by column
+        // inside a group. At one workgroup per CU an XCD's share of a round
+        // is 32 consecutive positions, inside a group a 4 x 8 block of tiles:
+        // A panels are shared by 8 workgroups and B panels by 4 in its L2.
+        const int group = tile / (kGroupM * tiles_n);
+        const int gm = min(kGroupM, tiles_m - group * kGroupM);
+        const int in_group = tile - group * kGroupM * tiles_n;
+        const int tm = group * kGroupM + in_group % gm, tn = in_group / gm;
+        const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+
+        // This thread's row: A rows 0..255, then B rows 0..255.
+        const int64_t row = is_b ? n0 + (t - kBM) : m0 + t;
+        const bool valid = row < rows;
+        const int64_t rc = valid ? row : 0;
+        const uint8_t* code_row = codes + rc * (K >> 1);
+        const uint8_t* scale_row = valid ? scales + (two_d ? (rc >> 4) : rc) * (K >> 4) : kZeroScales;
+        const int sstride = valid ? kBK / 16 : 0;
+
+        floatx16 acc[2][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int64_t col = n0 + wn + b * 32 + (lane & 31);
-            if (col >= g.N)
-                continue;
+            for (int b = 0; b < 4; ++b)
+                acc[a][b] = floatx16{};
+
+        decode_stage_to_lds(fetch_stage<WIDE>(code_row, scale_row, 0, sstride, K), my_row0);
+        // Two register sets alternate (stage s+1 in one, s+2 in the other)
+        // so a fetch lands in registers the decode has just consumed: no
+        // copies of in-flight loads, hence no wait on the newest fetch.
+        RowStage sa = fetch_stage<WIDE>(code_row, scale_row, min(1, last), sstride, K);
+        __builtin_amdgcn_sched_barrier(0);  // issue order sa, sb as in the loop
+        RowStage sb = fetch_stage<WIDE>(code_row, scale_row, min(2, last), sstride, K);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+
+        int s = 0;
+        for (; s + 1 < nstages; s += 2) {
+            stage_mfma(lds, wm, wn, frow, fk, acc);
+            decode_stage_to_lds(sa, my_row0 + kStageBytes);
+            sa = fetch_stage<WIDE>(code_row, scale_row, min(s + 3, last), sstride, K);
+            __syncthreads();
+            // keep each half's work in its half: the scheduler would
+            // otherwise hoist the next decode and wait on the newest fetch
+            __builtin_amdgcn_sched_barrier(0);
+            stage_mfma(lds + kStageBytes, wm, wn, frow, fk, acc);
+            decode_stage_to_lds(sb, my_row0);
+            sb = fetch_stage<WIDE>(code_row, scale_row, min(s + 4, last), sstride, K);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (s < nstages) {
+            stage_mfma(lds, wm, wn, frow, fk, acc);
+            __syncthreads();  // buffer 0 is rewritten by the next tile
+        }
+
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int64_t r = m0 + wm + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                if (r >= g.M)
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int64_t col = n0 + wn + b * 32 + (lane & 31);
+                if (col >= g.N)
                     continue;
-                const float v = acc[a][b][i] * scale;
-                if (BF16_OUT) {
-                    const uint32_t u = __float_as_uint(v);
-                    reinterpret_cast<uint16_t*>(g.c)[r * g.N + col] =
-                        (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-                } else {
-                    reinterpret_cast<float*>(g.c)[r * g.N + col] = v;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int64_t r = m0 + wm + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    if (r >= g.M)
+                        continue;
+                    const float v = acc[a][b][i] * scale;
+                    if (BF16_OUT) {
+                        const uint32_t u = __float_as_uint(v);
+                        reinterpret_cast<uint16_t*>(g.c)[r * g.N + col] =
+                            (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                    } else {
+                        reinterpret_cast<float*>(g.c)[r * g.N + col] = v;
+                    }
                 }
             }
-        }
+    }
+}
+
+// Workgroups resident at once on the current device (one per CU at this
+// tile size), cached per device.
+template <bool BF16_OUT, bool WIDE>
+int gemm_capacity()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0)
+        return c;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(gemm_kernel<BF16_OUT, WIDE>), kThreads, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    c = (per_cu > 0 ? per_cu : 1) * cus;
+    if (c > 0)
+        cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+template <bool BF16_OUT, bool WIDE>
+hipError_t launch_variant(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t stream)
+{
+    const int cap = gemm_capacity<BF16_OUT, WIDE>();
+    if (cap <= 0)
+        return hipErrorInvalidDevice;
+    const int nt = tiles_m * tiles_n;
+    const dim3 grid((unsigned)(nt < cap ? nt : cap));
+    hipLaunchKernelGGL((gemm_kernel<BF16_OUT, WIDE>), grid, dim3(kThreads), 0, stream, a, tiles_m, tiles_n);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -229,20 +297,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream)
 {
     const int tiles_m = (int)((a.M + kBM - 1) / kBM);
     const int tiles_n = (int)((a.N + kBN - 1) / kBN);
-    const dim3 grid((unsigned)(tiles_m * tiles_n));
     const bool wide = (a.K % kBK) == 0;
-    if (a.c_bf16) {
-        if (wide)
-            hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(kThreads), 0, stream, a, tiles_m, tiles_n);
-        else
-            hipLaunchKernelGGL((gemm_kernel<true, false>), grid, dim3(kThreads), 0, stream, a, tiles_m, tiles_n);
-    } else {
-        if (wide)
-            hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(kThreads), 0, stream, a, tiles_m, tiles_n);
-        else
-            hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(kThreads), 0, stream, a, tiles_m, tiles_n);
-    }
-    return hipGetLastError();
+    if (a.c_bf16)
+        return wide ? launch_variant<true, true>(a, tiles_m, tiles_n, stream)
+                    : launch_variant<true, false>(a, tiles_m, tiles_n, stream);
+    return wide ? launch_variant<false, true>(a, tiles_m, tiles_n, stream)
+                : launch_variant<false, false>(a, tiles_m, tiles_n, stream);
 }
 
 }  // namespace nvfp4

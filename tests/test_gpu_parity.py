@@ -372,6 +372,36 @@ def test_gemm_full_size_sampled_rows():
     assert err <= 1e-5
 
 
+@pytest.mark.parametrize("a_mode,b_mode", [(1, 2), (2, 1)])
+def test_gemm_more_tiles_than_workgroups(a_mode, b_mode):
+    """More 256 x 256 output tiles than resident workgroups (each workgroup
+    walks several), ragged in M and N, K an odd multiple of 16, and both
+    assignments of 1D / 2D scales to the operands: every output row checked."""
+    M, N, K = 2064, 8208, 48  # 9 x 33 = 297 tiles
+    a = W.normal_tensor(M, K, seed=44)
+    b = W.normal_tensor(N, K, seed=45, std=0.02)
+    log(f"[test_gemm_more_tiles_than_workgroups] modes=({a_mode},{b_mode})")
+    ad, bd = dev(a), dev(b)
+
+    def quant(xd, mode):
+        if mode == 1:
+            q = F.nvfp4_quantize_1d(xd, F.nvfp4_amax(xd))
+            return q["codes_row"], q["scales_row"], q["global_scale"]
+        q = F.nvfp4_quantize_2d(xd, F.nvfp4_amax(xd), colwise=False)
+        return q["codes_row"], q["scales"], q["global_scale"]
+
+    ac, as_, ag = quant(ad, a_mode)
+    bc, bs, bg = quant(bd, b_mode)
+    c = host(F.nvfp4_gemm(ac, as_, a_mode, ag, bc, bs, b_mode, bg, M, N, K))
+    ref = oracle.gemm_rows(host(ac), host(as_), a_mode, host(ag)[0], host(bc), host(bs), b_mode,
+                           host(bg)[0], M, N, K, np.arange(M, dtype=np.int64))
+    err = np.linalg.norm(c.astype(np.float64) - ref) / np.linalg.norm(ref)
+    assert err <= 1e-5
+    # each row separately too, so a wrong tile cannot hide in the norm
+    row_err = np.linalg.norm(c.astype(np.float64) - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    assert row_err.max() <= 1e-5
+
+
 def test_gemm_bf16_output_is_rounded_fp32():
     a = W.normal_tensor(272, 528, seed=42)
     b = W.normal_tensor(400, 528, seed=43, std=0.02)
