@@ -233,9 +233,20 @@ __device__ __forceinline__ void load_item(const Params& p, const ItemPos& q, uin
     }
 }
 
-// Column maxima of an item (binary32 bits of max |x| over its 16 rows), from
-// packed u16 maxima of the |bf16| patterns.
-__device__ __forceinline__ void column_maxima(const uint4 (&v)[16], uint32_t (&cmax)[8])
+// Block maxima of an item as packed pairs of |bf16| patterns (16 bits each,
+// the upper 16 bits of the binary32 maximum).
+//   col[k]: columns 2k (low half) and 2k+1 (high half), over the 16 rows;
+//   row[k]: the rowwise blocks (16 columns, split over the lane pair) of
+//           rows 2k (low half) and 2k+1 (high half) of this lane's half of
+//           the item's rows: rows 0..7 on even lanes, 8..15 on odd lanes.
+// Both depend on the data alone, so the fused kernel takes them before the
+// grid-wide amax is known.
+struct BlockMax {
+    uint32_t col[4];
+    uint32_t row[4];
+};
+
+__device__ __forceinline__ void column_maxima(const uint4 (&v)[16], BlockMax& bm)
 {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -243,9 +254,40 @@ __device__ __forceinline__ void column_maxima(const uint4 (&v)[16], uint32_t (&c
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             pm = pk_max_u16(pm, word_at(v[i], k) & 0x7FFF7FFFu);
-        cmax[2 * k] = pm << 16;
-        cmax[2 * k + 1] = pm & 0xFFFF0000u;
+        bm.col[k] = pm;
     }
+}
+
+// Row maxima trade halves through DPP with the pair lane: every lane of the
+// pair must be active (both are, as the item validity is pairwise).
+__device__ __forceinline__ void row_maxima(const uint4 (&v)[16], bool odd, BlockMax& bm)
+{
+    uint32_t rm[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t pm = pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
+                                       pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu));
+        rm[i] = max(pm & 0xFFFFu, pm >> 16);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+        const uint32_t send = (odd ? rm[k] : rm[k + 8]) | ((odd ? rm[k + 1] : rm[k + 9]) << 16);
+        const uint32_t own = (odd ? rm[k + 8] : rm[k]) | ((odd ? rm[k + 9] : rm[k + 1]) << 16);
+        bm.row[k >> 1] = pk_max_u16(own, swap_lane1(send));
+    }
+}
+
+// Binary32 bits of a packed half: the low (H = 0) or high (H = 1) 16 bits.
+template <int H>
+__device__ __forceinline__ uint32_t half_bits(uint32_t packed)
+{
+    return H ? (packed & 0xFFFF0000u) : (packed << 16);
+}
+
+__device__ __forceinline__ uint32_t item_max(const BlockMax& bm)
+{
+    uint32_t pm = pk_max_u16(pk_max_u16(bm.col[0], bm.col[1]), pk_max_u16(bm.col[2], bm.col[3]));
+    return max(pm & 0xFFFFu, pm >> 16) << 16;
 }
 
 // Per-tensor constants of the scale chain.
@@ -271,11 +313,12 @@ __device__ __forceinline__ uint32_t scale_byte(uint32_t b_bits, const ScaleCtx& 
 
 // Quantize one work item held in registers: block scales, codes; rowwise
 // outputs go straight to memory, columnwise outputs to the LDS staging.
-// cmax: the item's column maxima (ignored with RHT, which recomputes them
-// from the transformed values).
+// bm: the item's block maxima (column maxima are ignored with RHT, which
+// recomputes them from the transformed values; row maxima are needed for
+// rowwise 1D only).
 template <bool ROW, bool COL, bool TWO_D, bool SR, bool RHT>
 __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
-                                             const uint4 (&v)[16], const uint32_t (&cmax)[8],
+                                             const uint4 (&v)[16], const BlockMax& bm,
                                              const ScaleCtx& sc, const float* lds_rcp,
                                              uint2* lds_codes, uint8_t* lds_scales)
 {
@@ -311,7 +354,7 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
                 for (int i = 0; i < 16; ++i)
                     m = max(m, __float_as_uint(y[i]) & 0x7FFFFFFFu);
             } else {
-                m = cmax[j];
+                m = (j & 1) ? half_bits<1>(bm.col[j >> 1]) : half_bits<0>(bm.col[j >> 1]);
             }
             const uint32_t byte = scale_byte(m, sc);
             const float r = lds_rcp[byte];
@@ -335,10 +378,7 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
     uint32_t col_byte[8];
     bool fin = true;
     if (TWO_D) {
-        uint32_t m = cmax[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j)
-            m = max(m, cmax[j]);
+        uint32_t m = item_max(bm);
         m = max(m, swap_lane1(m));
         const uint32_t byte = scale_byte(m, sc);
         const float r = lds_rcp[byte];
@@ -355,29 +395,20 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
         if (COL) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                col_byte[j] = scale_byte(cmax[j], sc);
+                const uint32_t m = (j & 1) ? half_bits<1>(bm.col[j >> 1]) : half_bits<0>(bm.col[j >> 1]);
+                col_byte[j] = scale_byte(m, sc);
                 rc[j] = lds_rcp[col_byte[j]];
                 fin = fin && finite_bits(rc[j]);
             }
         }
         if (ROW) {
-            uint32_t rm[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t pm =
-                    pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
-                               pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu));
-                rm[i] = max(pm & 0xFFFFu, pm >> 16) << 16;
-            }
             // Even lanes own rows 0..7 of the pair's blocks, odd lanes 8..15.
             const int64_t srow0 = r0 + (odd ? 8 : 0);
             uint8_t* sdst = p.scales_row + srow0 * (cols >> 4) + (c0 >> 4);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const uint32_t send = odd ? rm[k] : rm[k + 8];
-                const uint32_t recv = swap_lane1(send);
-                const uint32_t own = odd ? rm[k + 8] : rm[k];
-                const uint32_t byte = scale_byte(max(own, recv), sc);
+                const uint32_t m = (k & 1) ? half_bits<1>(bm.row[k >> 1]) : half_bits<0>(bm.row[k >> 1]);
+                const uint32_t byte = scale_byte(m, sc);
                 sdst[k * (cols >> 4)] = (uint8_t)byte;
                 const float mine = lds_rcp[byte];
                 const float other = swap_lane1(mine);
@@ -471,10 +502,12 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
     __syncthreads();
 
     if (q.valid) {
-        uint32_t cmax[8];
+        BlockMax bm;
         if (!RHT)
-            column_maxima(v, cmax);
-        compute_item<ROW, COL, TWO_D, SR, RHT>(p, q, v, cmax, sc, lds_rcp, lds_codes, lds_scales);
+            column_maxima(v, bm);
+        if (ROW && !TWO_D)
+            row_maxima(v, q.odd, bm);
+        compute_item<ROW, COL, TWO_D, SR, RHT>(p, q, v, bm, sc, lds_rcp, lds_codes, lds_scales);
     }
     if (COL) {
         __syncthreads();
@@ -643,8 +676,10 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t* ws, const Params& p)
 template <bool ROW, bool COL, bool SR>
 __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint32_t* ws)
 {
-    __shared__ uint2 lds_codes[COL ? kTileC * kRowBlocks : 1];
-    __shared__ uint8_t lds_scales[COL ? kTileC * kRowBlocks : 16];
+    // Two columnwise staging buffers: the second item's encode overlaps the
+    // first item's column stores.
+    __shared__ uint2 lds_codes[2][COL ? kTileC * kRowBlocks : 1];
+    __shared__ uint8_t lds_scales[2][COL ? kTileC * kRowBlocks : 16];
     __shared__ float lds_rcp[128];
 
     const int nt = p.tiles_r * p.tiles_c;
@@ -658,20 +693,23 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
     if (has_b)
         load_item(p, qb, vb);
 
-    // Column maxima while the data arrives; the block-local amax follows.
-    uint32_t ca[8], cb[8];
+    // Block maxima while the data arrives; the workgroup's maximum follows.
+    // (With stochastic rounding the row maxima wait until after the
+    // exchange: holding them across it would cost occupancy.)
+    constexpr bool kEarlyRows = ROW && !SR;
+    BlockMax ba, bb;
     uint32_t m = 0u;
     if (qa.valid) {
-        column_maxima(va, ca);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            m = max(m, ca[j]);
+        column_maxima(va, ba);
+        if (kEarlyRows)
+            row_maxima(va, qa.odd, ba);
+        m = item_max(ba);
     }
     if (has_b && qb.valid) {
-        column_maxima(vb, cb);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            m = max(m, cb[j]);
+        column_maxima(vb, bb);
+        if (kEarlyRows)
+            row_maxima(vb, qb.odd, bb);
+        m = max(m, item_max(bb));
     }
     const uint32_t amax_bits = grid_max(m, ws, p);
 
@@ -681,20 +719,24 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
     build_reciprocal_table(lds_rcp, sc.sg);
     __syncthreads();
 
-    if (qa.valid)
-        compute_item<ROW, COL, false, SR, false>(p, qa, va, ca, sc, lds_rcp, lds_codes, lds_scales);
+    if (qa.valid) {
+        if (ROW && !kEarlyRows)
+            row_maxima(va, qa.odd, ba);
+        compute_item<ROW, COL, false, SR, false>(p, qa, va, ba, sc, lds_rcp, lds_codes[0], lds_scales[0]);
+    }
     if (COL) {
         __syncthreads();
-        write_col_tile<false>(p, qa.tile_r0, qa.tile_c0, lds_codes, lds_scales);
+        write_col_tile<false>(p, qa.tile_r0, qa.tile_c0, lds_codes[0], lds_scales[0]);
     }
     if (has_b) {
-        if (COL)
-            __syncthreads();
-        if (qb.valid)
-            compute_item<ROW, COL, false, SR, false>(p, qb, vb, cb, sc, lds_rcp, lds_codes, lds_scales);
+        if (qb.valid) {
+            if (ROW && !kEarlyRows)
+                row_maxima(vb, qb.odd, bb);
+            compute_item<ROW, COL, false, SR, false>(p, qb, vb, bb, sc, lds_rcp, lds_codes[1], lds_scales[1]);
+        }
         if (COL) {
             __syncthreads();
-            write_col_tile<false>(p, qb.tile_r0, qb.tile_c0, lds_codes, lds_scales);
+            write_col_tile<false>(p, qb.tile_r0, qb.tile_c0, lds_codes[1], lds_scales[1]);
         }
     }
 }
