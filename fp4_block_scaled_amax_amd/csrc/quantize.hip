@@ -187,12 +187,15 @@ __device__ __forceinline__ void encode_item(const uint4 (&v)[16], const float (&
                                             uint8_t* row_dst, int64_t row_pitch,
                                             uint32_t (&colw)[8][2])
 {
+    // A half-wave's rowwise codes of one row are a whole 128-byte line:
+    // stream them past the caches.
     uint32_t roww[2];
 #define NVFP4_ROWS(IP)                                                                   \
     encode_row_pair<MODE, IP, ROW, COL>(v, rr, rc, draws, roww, colw);                    \
     if (ROW) {                                                                           \
-        *reinterpret_cast<uint32_t*>(row_dst + (2 * IP) * row_pitch) = roww[0];          \
-        *reinterpret_cast<uint32_t*>(row_dst + (2 * IP + 1) * row_pitch) = roww[1];      \
+        uint8_t* d = row_dst + (2 * IP) * row_pitch;                                     \
+        __builtin_nontemporal_store(roww[0], reinterpret_cast<uint32_t*>(d));            \
+        __builtin_nontemporal_store(roww[1], reinterpret_cast<uint32_t*>(d + row_pitch)); \
     }
     NVFP4_ROWS(0) NVFP4_ROWS(1) NVFP4_ROWS(2) NVFP4_ROWS(3)
     NVFP4_ROWS(4) NVFP4_ROWS(5) NVFP4_ROWS(6) NVFP4_ROWS(7)
@@ -673,21 +676,76 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t* ws, const Params& p)
     return result_s;
 }
 
+// Write the staged columnwise output of two vertically adjacent tiles (A at
+// rows tile_r0.., B below it; B may be absent or ragged). Per column the
+// pair covers 256 rows: 128 bytes of codes, one whole line, written by 8
+// lanes as 16-byte streaming stores, and 16 scale bytes.
+__device__ __forceinline__ void write_col_pair(const Params& p, int64_t tile_r0, int64_t tile_c0,
+                                               const uint2* codes_a, const uint2* codes_b,
+                                               const uint8_t* scales_a, const uint8_t* scales_b)
+{
+    typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+    const int64_t rows = p.rows, cols = p.cols;
+    const int64_t pitch = rows >> 1;
+    const bool wide = (pitch & 15) == 0;  // 16-byte chunks are aligned
+#pragma unroll
+    for (int k = 0; k < kTileC * 8 / kThreads; ++k) {
+        const int q = k * kThreads + threadIdx.x;
+        const int col = q >> 3, part = q & 7;  // part: 32 rows = two row blocks
+        const int64_t c = tile_c0 + col, r = tile_r0 + part * 32;
+        if (c >= cols || r >= rows)
+            continue;
+        const uint2* src = part < 4 ? codes_a : codes_b;
+        const int swz = (col >> 3) & 7;
+        const int rb0 = (2 * part) & 7;
+        const uint2 lo = src[col * kRowBlocks + (rb0 ^ swz)];
+        uint8_t* dst = p.codes_col + c * pitch + (r >> 1);
+        if (r + 32 <= rows) {
+            const uint2 hi = src[col * kRowBlocks + ((rb0 + 1) ^ swz)];
+            if (wide) {
+                __builtin_nontemporal_store(u32x4_nt{lo.x, lo.y, hi.x, hi.y},
+                                            reinterpret_cast<u32x4_nt*>(dst));
+            } else {
+                *reinterpret_cast<uint2*>(dst) = lo;
+                *reinterpret_cast<uint2*>(dst + 8) = hi;
+            }
+        } else {
+            *reinterpret_cast<uint2*>(dst) = lo;  // ragged bottom: one row block
+        }
+    }
+    // Scales: one column's 16 bytes (8 per tile) per thread.
+    const int col = threadIdx.x;
+    const int64_t c = tile_c0 + col;
+    if (c < cols) {
+        const int64_t spitch = rows >> 4;
+        uint8_t* dst = p.scales_col + c * spitch + (tile_r0 >> 4);
+        const int64_t nb64 = (rows - tile_r0) >> 4;
+        const int nb = nb64 < 2 * kRowBlocks ? (int)nb64 : 2 * kRowBlocks;
+        const uint2 sa = *reinterpret_cast<const uint2*>(&scales_a[col * kRowBlocks]);
+        if (nb == 2 * kRowBlocks && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
+            const uint2 sb = *reinterpret_cast<const uint2*>(&scales_b[col * kRowBlocks]);
+            *reinterpret_cast<uint4*>(dst) = make_uint4(sa.x, sa.y, sb.x, sb.y);
+        } else {
+            for (int b = 0; b < nb; ++b)
+                dst[b] = b < kRowBlocks ? scales_a[col * kRowBlocks + b] : scales_b[col * kRowBlocks + b - kRowBlocks];
+        }
+    }
+}
+
 template <bool ROW, bool COL, bool SR>
 __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint32_t* ws)
 {
-    // Two columnwise staging buffers: the second item's encode overlaps the
-    // first item's column stores.
+    // Columnwise staging for the two tiles.
     __shared__ uint2 lds_codes[2][COL ? kTileC * kRowBlocks : 1];
     __shared__ uint8_t lds_scales[2][COL ? kTileC * kRowBlocks : 16];
     __shared__ float lds_rcp[128];
 
-    const int nt = p.tiles_r * p.tiles_c;
-    const int ta = blockIdx.x;
-    const int tb = blockIdx.x + gridDim.x;
-    const bool has_b = tb < nt;  // uniform over the workgroup
-    const ItemPos qa = item_pos(ta % p.tiles_r, ta / p.tiles_r, p.rows, p.cols);
-    const ItemPos qb = item_pos(tb % p.tiles_r, tb / p.tiles_r, p.rows, p.cols);
+    // Two vertically adjacent tiles per workgroup (B below A), so a
+    // column's codes of the pair form whole 128-byte lines.
+    const int tra = 2 * (blockIdx.x / p.tiles_c), tc = blockIdx.x % p.tiles_c;
+    const bool has_b = tra + 1 < p.tiles_r;  // uniform over the workgroup
+    const ItemPos qa = item_pos(tra, tc, p.rows, p.cols);
+    const ItemPos qb = item_pos(tra + 1, tc, p.rows, p.cols);
     uint4 va[16], vb[16];
     load_item(p, qa, va);
     if (has_b)
@@ -724,20 +782,14 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
             row_maxima(va, qa.odd, ba);
         compute_item<ROW, COL, false, SR, false>(p, qa, va, ba, sc, lds_rcp, lds_codes[0], lds_scales[0]);
     }
+    if (has_b && qb.valid) {
+        if (ROW && !kEarlyRows)
+            row_maxima(vb, qb.odd, bb);
+        compute_item<ROW, COL, false, SR, false>(p, qb, vb, bb, sc, lds_rcp, lds_codes[1], lds_scales[1]);
+    }
     if (COL) {
         __syncthreads();
-        write_col_tile<false>(p, qa.tile_r0, qa.tile_c0, lds_codes[0], lds_scales[0]);
-    }
-    if (has_b) {
-        if (qb.valid) {
-            if (ROW && !kEarlyRows)
-                row_maxima(vb, qb.odd, bb);
-            compute_item<ROW, COL, false, SR, false>(p, qb, vb, bb, sc, lds_rcp, lds_codes[1], lds_scales[1]);
-        }
-        if (COL) {
-            __syncthreads();
-            write_col_tile<false>(p, qb.tile_r0, qb.tile_c0, lds_codes[1], lds_scales[1]);
-        }
+        write_col_pair(p, qa.tile_r0, qa.tile_c0, lds_codes[0], lds_codes[1], lds_scales[0], lds_scales[1]);
     }
 }
 
@@ -768,8 +820,7 @@ template <bool ROW, bool COL, bool SR>
 hipError_t launch_fused_variant(Params p, uint32_t* ws, hipStream_t stream, bool& launched)
 {
     launched = false;
-    const int nt = p.tiles_r * p.tiles_c;
-    const int grid = (nt + 1) / 2;
+    const int grid = ((p.tiles_r + 1) / 2) * p.tiles_c;
     if (grid > kMaxFusedBlocks || grid > fused_capacity<ROW, COL, SR>())
         return hipSuccess;
     hipLaunchKernelGGL((quantize_fused_kernel<ROW, COL, SR>), dim3(grid), dim3(kThreads), 0, stream, p,
