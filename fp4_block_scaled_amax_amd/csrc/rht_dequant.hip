@@ -82,8 +82,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// One 16-element block per item: 8 bytes of codes and one scale byte.
-// Magnitude m decodes through a packed table of 2*value: {0,1,2,3,4,6,8,12}.
+// Each thread owns E consecutive elements of a row (E = 4 for binary32
+// output, 8 for bf16: 16 bytes either way) and walks down the rows, so a
+// wave's stores are 1 KB contiguous. Decoding is exact hardware work: the
+// scale byte through the E4M3 convert, two codes per E2M1 convert (unit
+// scale); then (G * s) is exact and one rounding multiplies by S_g. A NaN
+// scale gives NaN with the code's sign (the reconstruction negates the
+// block's NaN magnitude for negative codes).
 template <bool TWO_D, bool BF16>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint8_t* __restrict__ codes,
                                                                const uint8_t* __restrict__ scales,
@@ -91,37 +96,43 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint8_t* __r
                                                                int64_t rows, int64_t cols,
                                                                void* __restrict__ out)
 {
+    constexpr int E = BF16 ? 8 : 4;
+    const int64_t chunk = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t c0 = chunk * E;
+    if (c0 >= cols)
+        return;
     const float sg = *sgp;
-    const int64_t bpr = cols >> 4;  // blocks per row
-    const int64_t nblocks = rows * bpr;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks; blk += stride) {
-        const uint2 cw = load8_stream(codes + blk * 8);
-        const int64_t r = blk / bpr, cb = blk - r * bpr;
-        const uint32_t sb = TWO_D ? scales[(r >> 4) * bpr + cb] : scales[blk];
-        const float hs = 0.5f * e4m3_decode(sb);  // exact
-        float val[16];
+    const int64_t bpr = cols >> 4;  // scale blocks per row
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+        const uint8_t* cp = codes + ((r * cols + c0) >> 1);
+        const uint32_t w = BF16 ? *reinterpret_cast<const uint32_t*>(cp)
+                                : (uint32_t)*reinterpret_cast<const uint16_t*>(cp);
+        const uint32_t sb = TWO_D ? scales[(r >> 4) * bpr + (c0 >> 4)] : scales[r * bpr + (c0 >> 4)];
+        const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.0f, false)[0];
+        float v[E];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t word = (k < 8) ? cw.x : cw.y;
-            const uint32_t nib = (word >> (4 * (k & 7))) & 15u;
-            const uint32_t twice = __builtin_amdgcn_ubfe(0xC8643210u, 4u * (nib & 7u), 4u);
-            const float mag = ((float)twice * hs) * sg;
-            val[k] = __uint_as_float(__float_as_uint(mag) | ((nib & 8u) << 28));
+        for (int j = 0; j < E / 2; ++j) {
+            auto g = j == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
+                   : j == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
+                   : j == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
+                            : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                v[2 * j + h] = (g[h] * s) * sg;
+            if (s != s) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    v[2 * j + h] = __uint_as_float(0x7FC00000u | (__float_as_uint(g[h]) & 0x80000000u));
+            }
         }
         if (BF16) {
-            uint4* dst = reinterpret_cast<uint4*>(out) + blk * 2;
-            uint32_t w[8];
+            uint32_t q[4];
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                w[q] = f32_to_bf16_rne(val[2 * q]) | (f32_to_bf16_rne(val[2 * q + 1]) << 16);
-            store16_stream(dst, make_uint4(w[0], w[1], w[2], w[3]));
-            store16_stream(dst + 1, make_uint4(w[4], w[5], w[6], w[7]));
+            for (int k = 0; k < 4; ++k)
+                q[k] = f32_to_bf16_rne(v[2 * k]) | (f32_to_bf16_rne(v[2 * k + 1]) << 16);
+            store16_stream(reinterpret_cast<uint16_t*>(out) + r * cols + c0, make_uint4(q[0], q[1], q[2], q[3]));
         } else {
-            float4* dst = reinterpret_cast<float4*>(out) + blk * 4;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                store16_stream(dst + q, make_float4(val[4 * q], val[4 * q + 1], val[4 * q + 2], val[4 * q + 3]));
+            store16_stream(reinterpret_cast<float*>(out) + r * cols + c0, make_float4(v[0], v[1], v[2], v[3]));
         }
     }
 }
@@ -147,21 +158,31 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool t
                              const float* global_scale, int64_t rows, int64_t cols, void* out,
                              bool bf16_out, hipStream_t stream)
 {
-    const int grid = grid_for(rows * (cols >> 4));
+    // x: 16-byte column chunks of a row; y: rows, walked with a stride so
+    // that about 2048 workgroups cover the tensor.
+    const int64_t chunks = cols / (bf16_out ? 8 : 4);
+    const int64_t gx = (chunks + kThreads - 1) / kThreads;
+    int64_t gy = 2048 / gx;
+    gy = gy < 1 ? 1 : gy;
+    gy = gy > rows ? rows : gy;
+    gy = gy > 65535 ? 65535 : gy;
+    if (gx > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)gx, (unsigned)gy);
     if (two_d) {
         if (bf16_out)
-            hipLaunchKernelGGL((dequantize_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream,
-                               codes, scales, global_scale, rows, cols, out);
+            hipLaunchKernelGGL((dequantize_kernel<true, true>), grid, dim3(kThreads), 0, stream, codes,
+                               scales, global_scale, rows, cols, out);
         else
-            hipLaunchKernelGGL((dequantize_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream,
-                               codes, scales, global_scale, rows, cols, out);
+            hipLaunchKernelGGL((dequantize_kernel<true, false>), grid, dim3(kThreads), 0, stream, codes,
+                               scales, global_scale, rows, cols, out);
     } else {
         if (bf16_out)
-            hipLaunchKernelGGL((dequantize_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream,
-                               codes, scales, global_scale, rows, cols, out);
+            hipLaunchKernelGGL((dequantize_kernel<false, true>), grid, dim3(kThreads), 0, stream, codes,
+                               scales, global_scale, rows, cols, out);
         else
-            hipLaunchKernelGGL((dequantize_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream,
-                               codes, scales, global_scale, rows, cols, out);
+            hipLaunchKernelGGL((dequantize_kernel<false, false>), grid, dim3(kThreads), 0, stream, codes,
+                               scales, global_scale, rows, cols, out);
     }
     return hipGetLastError();
 }

@@ -333,6 +333,36 @@ def test_dequantize(mode):
     assert np.array_equal(y16.view(np.uint16), ref16)
 
 
+@pytest.mark.parametrize("mode", [1, 2])
+def test_dequantize_every_code_and_scale_byte(mode):
+    """Arbitrary codes and all 256 scale bytes (negative, zero, subnormal,
+    448, NaN): bit-identical to the oracle, NaN results compared as NaN with
+    the oracle's sign (the payload is not a property of the method)."""
+    rng = np.random.default_rng(7)
+    R, C = 272, 4096  # a 2D tile row covers all 256 scale bytes per 16 rows
+    codes = rng.integers(0, 256, size=(R, C // 2), dtype=np.uint8)
+    if mode == 1:
+        scales = np.tile(np.arange(256, dtype=np.uint8), R * (C // 16) // 256 + 1)[: R * (C // 16)]
+        scales = scales.reshape(R, C // 16)
+    else:
+        scales = np.tile(np.arange(256, dtype=np.uint8), (R // 16) * (C // 16) // 256 + 1)
+        scales = scales[: (R // 16) * (C // 16)].reshape(R // 16, C // 16)
+    sg = np.array([0.37109375], dtype=np.float32)
+    cd, sd, gd = (torch.from_numpy(a).to("cuda") for a in (codes, scales, sg))
+    y32 = host(F.nvfp4_dequantize(cd, sd, mode, gd, R, C))
+    y16 = host(F.nvfp4_dequantize(cd, sd, mode, gd, R, C, out_dtype=torch.bfloat16).view(torch.int16))
+    ref = oracle.dequantize(codes, scales, mode, sg[0], R, C)
+    ref16 = oracle.dequantize_bf16(codes, scales, mode, sg[0], R, C)
+    for got, want, top in ((y32.view(np.uint32), ref.view(np.uint32), np.uint32(0x80000000)),
+                           (y16.view(np.uint16), ref16.view(np.uint16), np.uint16(0x8000))):
+        nan_w = (want & ~top) > (np.uint32(0x7F800000) if top == 0x80000000 else np.uint16(0x7F80))
+        nan_g = (got & ~top) > (np.uint32(0x7F800000) if top == 0x80000000 else np.uint16(0x7F80))
+        assert nan_w.any()
+        assert np.array_equal(nan_w, nan_g)
+        assert np.array_equal(got[~nan_w], want[~nan_w])
+        assert np.array_equal(got[nan_w] & top, want[nan_w] & top)
+
+
 # ------------------------------------------------------------------- GEMM
 
 def quantized_operands(a_bits, b_bits):
