@@ -536,8 +536,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
 // arrival slots and 2 words per workgroup of release slots.
 
 constexpr int kWsAmax = 0, kWsGen = 1, kWsSlow = 2, kWsArrive = 16;
-constexpr int kMaxFusedBlocks = 2048;
+constexpr int kMaxFusedBlocks = 2048;                       // slots in the workspace
 constexpr int kWsRelease = kWsArrive + 2 * kMaxFusedBlocks;
+constexpr int kMaxFusedGrid = 1024;                         // largest grid launched
 constexpr uint64_t kWaitTicks = 200000;  // 2 ms of the 100 MHz real-time counter
 
 // All exchange traffic is relaxed device-scope atomics: the value travels
@@ -595,38 +596,60 @@ __device__ uint32_t direct_amax(const Params& p, uint32_t* red)
     return workgroup_max(max(pm & 0xFFFFu, pm >> 16) << 16, red);
 }
 
+// This call's generation: one more than the last completed call's. Read at
+// the start of the kernel, off the exchange's critical path (the word only
+// changes once every workgroup of this call has posted its arrival).
+__device__ __forceinline__ uint32_t call_generation(const uint32_t* ws)
+{
+    return ws_load(&ws[kWsGen]) + 1u;
+}
+
 // Grid-wide maximum of one value per workgroup (binary32 bits); every
-// workgroup returns the same result.
-__device__ uint32_t grid_max(uint32_t m, uint32_t* ws, const Params& p)
+// workgroup returns the same result. gen: call_generation(), read by
+// thread 0.
+__device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t* ws, const Params& p)
 {
     __shared__ uint32_t red[kThreads / 64];
     __shared__ uint32_t gen_s, result_s, ok_s;
     m = workgroup_max(m, red);
     if (threadIdx.x == 0) {
-        const uint32_t gen = ws_load(&ws[kWsGen]) + 1u;  // this call's generation
-        gen_s = gen;
-        slot_store(&ws[kWsArrive + 2 * blockIdx.x], gen, m);
+        gen_s = gen0;
+        slot_store(&ws[kWsArrive + 2 * blockIdx.x], gen0, m);
     }
     __syncthreads();
     const uint32_t gen = gen_s;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     if (blockIdx.x == 0) {
-        // Collect every workgroup's maximum.
+        // Collect every workgroup's maximum. Each thread watches the slots
+        // t, t + 256, ...; every round re-reads all of its pending slots at
+        // once, so their round trips overlap.
+        constexpr int kPer = kMaxFusedGrid / kThreads;
         uint32_t mm = 0u;
         bool ok = true;
-        for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads) {
-            uint64_t w = slot_load(&ws[kWsArrive + 2 * i]);
-            while ((uint32_t)w != gen) {
-                if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
-                    ok = false;
-                    break;
+        uint32_t pending = 0u;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            if ((int)threadIdx.x + k * kThreads < (int)gridDim.x)
+                pending |= 1u << k;
+        while (pending != 0u) {
+            uint64_t w[kPer];
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                w[k] = (pending >> k) & 1u ? slot_load(&ws[kWsArrive + 2 * (threadIdx.x + k * kThreads)]) : 0u;
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                if (((pending >> k) & 1u) && (uint32_t)w[k] == gen) {
+                    mm = max(mm, (uint32_t)(w[k] >> 32));
+                    pending &= ~(1u << k);
                 }
-                __builtin_amdgcn_s_sleep(4);
-                w = slot_load(&ws[kWsArrive + 2 * i]);
             }
-            if (!ok)
+            if (pending == 0u)
                 break;
-            mm = max(mm, (uint32_t)(w >> 32));
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(4);
         }
         if (threadIdx.x == 0)
             ok_s = 1u;
@@ -746,6 +769,9 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
     const bool has_b = tra + 1 < p.tiles_r;  // uniform over the workgroup
     const ItemPos qa = item_pos(tra, tc, p.rows, p.cols);
     const ItemPos qb = item_pos(tra + 1, tc, p.rows, p.cols);
+    uint32_t gen = 0u;
+    if (threadIdx.x == 0)
+        gen = call_generation(ws);
     uint4 va[16], vb[16];
     load_item(p, qa, va);
     if (has_b)
@@ -769,7 +795,7 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
             row_maxima(vb, qb.odd, bb);
         m = max(m, item_max(bb));
     }
-    const uint32_t amax_bits = grid_max(m, ws, p);
+    const uint32_t amax_bits = grid_max(m, gen, ws, p);
 
     const ScaleCtx sc = scale_ctx(__uint_as_float(amax_bits));
     if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
@@ -821,7 +847,7 @@ hipError_t launch_fused_variant(Params p, uint32_t* ws, hipStream_t stream, bool
 {
     launched = false;
     const int grid = ((p.tiles_r + 1) / 2) * p.tiles_c;
-    if (grid > kMaxFusedBlocks || grid > fused_capacity<ROW, COL, SR>())
+    if (grid > kMaxFusedGrid || grid > fused_capacity<ROW, COL, SR>())
         return hipSuccess;
     hipLaunchKernelGGL((quantize_fused_kernel<ROW, COL, SR>), dim3(grid), dim3(kThreads), 0, stream, p,
                        ws);
