@@ -204,9 +204,10 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t ctr_lo, uint32_t ctr_hi,
         }
         uint64_t p0 = (uint64_t)0xD2511F53u * c0;
         uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        // three-input XORs (truth table 0x96) in one instruction each
+        uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
         uint32_t n1 = (uint32_t)p1;
-        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
         uint32_t n3 = (uint32_t)p0;
         c0 = n0;
         c1 = n1;

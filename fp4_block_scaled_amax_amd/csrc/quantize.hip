@@ -85,7 +85,75 @@ __device__ __forceinline__ bool finite_bits(float r)
 // multiplier is not finite, the one way a ratio can be NaN); 2: software
 // stochastic rounding.
 
-enum { kEncHw = 0, kEncHwSafe = 1, kEncSr = 2 };
+enum { kEncHw = 0, kEncHwSafe = 1, kEncSr = 2, kEncSrHw = 3 };
+
+constexpr bool is_sr(int mode) { return mode == kEncSr || mode == kEncSrHw; }
+
+// ---- stochastic rounding on the hardware converter
+//
+// v_cvt_scalef32_sr_pk_fp4_f32 rounds its first element up when the
+// fraction bits it keeps below the E2M1 grid step (22 of them, aligned to
+// the step), plus the top 22 bits of the random word, carry out. With the
+// random word's top 16 bits = ~h and the rest ones, that is "up iff
+// F > 64 h" for the kept fraction F = floor(p * 2^22) -- the rule's
+// "h < p * 2^16" whenever p * 2^22 is an integer. It is for |v| >= 1; below
+// 1 the value can have fraction bits under the kept ones, so |v| is first
+// rounded up to a multiple of 2^-23 (which makes F = ceil(p * 2^22), and
+// "F > 64 h" again equals the rule). The scaling by 2^23 is exact and is
+// undone by the converter's power-of-two scale. Checked on the GPU against
+// e2m1_sr_nibble for every 16-bit draw and 52,832 values (all binades from
+// 2^-40 to 8 with random mantissas, every float within 300 ulp of each grid
+// point and midpoint, both signs, zeros, subnormals, infinities,
+// saturation); NaN ratios take the software encoder.
+
+// Random word for the draw in the low (HALF = 0) or high half of `w`.
+template <int HALF>
+__device__ __forceinline__ uint32_t sr_random_word(uint32_t w)
+{
+    return HALF ? (~w | 0xFFFFu) : ~(w << 16);
+}
+
+// v -> the converter operand (2^23 |v|, rounded up below 2^23, sign of v).
+__device__ __forceinline__ float sr_operand(float v)
+{
+    const float t = fabsf(v) * 0x1p23f;
+    const float tc = __builtin_amdgcn_fmed3f(__builtin_ceilf(t), t, 0x1p23f);
+    return __uint_as_float((__float_as_uint(tc) & 0x7FFFFFFFu) | (__float_as_uint(v) & 0x80000000u));
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Byte BYTE of `word` <- the stochastic codes of (a, b) with random words
+// (ra, rb). Each value is converted alone as the first element of a pair
+// whose second element is 0 (code 0), into byte 0: only byte 0 of the
+// convert's result is used (the instruction leaves the other bytes of its
+// destination register as they were, and the compiler does not tie them to
+// an input), then the two codes are merged and byte-permuted into place.
+template <int BYTE>
+__device__ __forceinline__ uint32_t sr_hw_pair(uint32_t word, float a, float b, uint32_t ra, uint32_t rb)
+{
+    const f32x2_t pa = {sr_operand(a), 0.0f};
+    const f32x2_t pb = {sr_operand(b), 0.0f};
+    const uint32_t ca = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pa, ra, 0x1p23f, 0);
+    const uint32_t cb = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pb, rb, 0x1p23f, 0);
+    const uint32_t pair = (cb << 4) | (ca & 0xFu);  // byte 0: code a | code b << 4
+    // v_perm: selector bytes 0..3 pick `pair`, 4..7 pick `word`
+    constexpr uint32_t sel = ((BYTE == 0 ? 0u : 4u) << 0) | ((BYTE == 1 ? 0u : 5u) << 8) |
+                             ((BYTE == 2 ? 0u : 6u) << 16) | ((BYTE == 3 ? 0u : 7u) << 24);
+    return __builtin_amdgcn_perm(word, pair, sel);
+}
+
+// Per-element random input of mode MODE for column/element k of a Philox
+// output: the 16-bit draw (software encoder) or the converter's random word.
+template <int MODE>
+__device__ __forceinline__ uint32_t sr_input(const uint4& w, int k)
+{
+    if (MODE == kEncSrHw) {
+        const uint32_t word = word_at(w, k >> 1);
+        return (k & 1) ? sr_random_word<1>(word) : sr_random_word<0>(word);
+    }
+    return draw16(w, k);
+}
 
 __device__ __forceinline__ float nan_to_signed_zero(float v, float x)
 {
@@ -114,6 +182,8 @@ __device__ __forceinline__ uint32_t put_pair(uint32_t word, float a, float b, fl
         return cvt_pair<BYTE>(word, nan_to_signed_zero(__builtin_fmaf(a, r, -0.0f), a),
                               nan_to_signed_zero(__builtin_fmaf(b, r, -0.0f), b));
     }
+    if (MODE == kEncSrHw)
+        return sr_hw_pair<BYTE>(word, a * r, b * r, ha, hb);
     const uint32_t lo = e2m1_sr_nibble(fabsf(a) * r, ha, (__float_as_uint(a) >> 28) & 8u);
     const uint32_t hi = e2m1_sr_nibble(fabsf(b) * r, hb, (__float_as_uint(b) >> 28) & 8u);
     return word | ((lo | (hi << 4)) << (8 * BYTE));
@@ -130,8 +200,8 @@ __device__ __forceinline__ uint2 encode_column16(const float (&y)[16], float r,
 #define NVFP4_PAIR(B)                                                                      \
     {                                                                                      \
         const int i = 8 * half + 2 * (B);                                                  \
-        const uint32_t ha = MODE == kEncSr ? draw16(draws[i], j) : 0u;                     \
-        const uint32_t hb = MODE == kEncSr ? draw16(draws[i + 1], j) : 0u;                 \
+        const uint32_t ha = is_sr(MODE) ? sr_input<MODE>(draws[i], j) : 0u;               \
+        const uint32_t hb = is_sr(MODE) ? sr_input<MODE>(draws[i + 1], j) : 0u;           \
         w[half] = put_pair<MODE, B>(w[half], y[i], y[i + 1], r, ha, hb);                   \
     }
         NVFP4_PAIR(0) NVFP4_PAIR(1) NVFP4_PAIR(2) NVFP4_PAIR(3)
@@ -162,11 +232,11 @@ __device__ __forceinline__ void encode_row_pair(const uint4 (&v)[16], const floa
         const uint32_t w0 = word_at(v[i], K), w1 = word_at(v[i + 1], K);                    \
         const float a = bf16_lo(w0), b = bf16_hi(w0), c = bf16_lo(w1), d = bf16_hi(w1);     \
         uint32_t ha = 0u, hb = 0u, hc = 0u, hd = 0u;                                        \
-        if (MODE == kEncSr) {                                                               \
-            ha = draw16(draws[i], 2 * K);                                                   \
-            hb = draw16(draws[i], 2 * K + 1);                                               \
-            hc = draw16(draws[i + 1], 2 * K);                                               \
-            hd = draw16(draws[i + 1], 2 * K + 1);                                           \
+        if (is_sr(MODE)) {                                                                  \
+            ha = sr_input<MODE>(draws[i], 2 * K);                                           \
+            hb = sr_input<MODE>(draws[i], 2 * K + 1);                                       \
+            hc = sr_input<MODE>(draws[i + 1], 2 * K);                                       \
+            hd = sr_input<MODE>(draws[i + 1], 2 * K + 1);                                   \
         }                                                                                   \
         if (ROW) {                                                                          \
             roww[0] = put_pair<MODE, K>(roww[0], a, b, rr[i], ha, hb);                      \
@@ -363,7 +433,8 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
             const float r = lds_rcp[byte];
             uint2 words;
             if (SR)
-                words = encode_column16<kEncSr>(y, r, draws, j);
+                words = __all(finite_bits(r)) ? encode_column16<kEncSrHw>(y, r, draws, j)
+                                              : encode_column16<kEncSr>(y, r, draws, j);
             else if (__all(finite_bits(r)))
                 words = encode_column16<kEncHw>(y, r, draws, j);
             else
@@ -427,7 +498,9 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
         colw[j][0] = colw[j][1] = 0u;
     uint8_t* row_dst = ROW ? p.codes_row + r0 * (cols >> 1) + (c0 >> 1) : nullptr;
     const int64_t row_pitch = cols >> 1;
-    if (SR)
+    if (SR && __all(fin))
+        encode_item<kEncSrHw, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
+    else if (SR)
         encode_item<kEncSr, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
     else if (__all(fin))
         encode_item<kEncHw, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
