@@ -191,6 +191,36 @@ def test_quantize_1d_full_gradient_path(name):
     check_q1(x, got, a, False, True, True, True, cols=sample_idx(C, 32, 3))
 
 
+def wide_range_blocks(rows, cols, seed):
+    """Every 16-element block (along rows and along columns) spans a huge
+    dynamic range: its ratios |x|/(s*S_g) cover 2^-42 .. 6, both signs,
+    exact grid points and midpoints included, so stochastic rounding meets
+    tiny ratios (no fraction bits left for a 22-bit window), ratios in
+    [0.5, 1) with odd last mantissa bits, and saturation."""
+    rng = np.random.default_rng(seed)
+    mag = np.exp2(rng.uniform(-44.0, 2.6, size=(rows, cols))).astype(np.float32)
+    grid = np.array([0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0],
+                    np.float32) / np.float32(6.0)
+    pick = rng.random((rows, cols)) < 0.1
+    mag[pick] = rng.choice(grid, size=int(pick.sum()))
+    mag[::16, :] = 1.0  # a block maximum in every column block
+    mag[:, ::16] = 1.0  # and in every row block
+    sign = np.where(rng.random((rows, cols)) < 0.5, -1.0, 1.0).astype(np.float32)
+    return W.f32_to_bf16_bits(mag * sign)
+
+
+@pytest.mark.parametrize("layouts", [(True, False), (False, True), (True, True)])
+def test_sr_wide_dynamic_range(layouts):
+    """Stochastic rounding over ratios from 2^-42 to 6: bit-identical to the
+    oracle in both layouts (the rule 'round up iff h < p * 2^16' at every
+    magnitude)."""
+    rowwise, colwise = layouts
+    x = wide_range_blocks(512, 1024, 77)
+    log(f"[test_sr_wide_dynamic_range] {layouts}")
+    got, a = run_q1(x, rowwise, colwise, sr=True)
+    check_q1(x, got, a, rowwise, colwise, True, False)
+
+
 def test_quantize_deterministic():
     x = wl("ragged_grad")
     g1, _ = run_q1(x, True, True, sr=True)
