@@ -19,36 +19,38 @@ int grid_for(int64_t items)
     return (int)g;
 }
 
-// Axis 0: item = 16 rows x 8 columns; writes the same footprint as fp32.
+// Axis 0: item = 16 rows x 4 columns (an 8-byte load and a 16-byte binary32
+// store per row), so the 64 lanes of a wave cover 256 consecutive columns:
+// 512 contiguous bytes per load and 1 KB per store instruction.
 __global__ __launch_bounds__(kThreads) void rht16_axis0_kernel(const uint16_t* __restrict__ x,
                                                                 int64_t rows, int64_t cols,
                                                                 uint32_t mask,
                                                                 float* __restrict__ y)
 {
-    const int64_t groups = cols >> 3;
+    const int64_t groups = cols >> 2;
     const int64_t items = (rows >> 4) * groups;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t it = (int64_t)blockIdx.x * kThreads + threadIdx.x; it < items; it += stride) {
         const int64_t rb = it / groups, cg = it - rb * groups;
-        const int64_t off = (rb * 16) * cols + cg * 8;
-        uint4 v[16];
+        const int64_t off = (rb * 16) * cols + cg * 4;
+        uint2 v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            v[i] = load16_stream(x + off + i * cols);
-        float z[8][16];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                z[j][i] = bf16_at(v[i], j);
-            rht16_inplace(z[j], mask);
-        }
+            v[i] = load8_stream(x + off + i * cols);
+        float z[4][16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float4* dst = reinterpret_cast<float4*>(y + off + i * cols);
-            store16_stream(dst, make_float4(z[0][i], z[1][i], z[2][i], z[3][i]));
-            store16_stream(dst + 1, make_float4(z[4][i], z[5][i], z[6][i], z[7][i]));
+            z[0][i] = bf16_lo(v[i].x);
+            z[1][i] = bf16_hi(v[i].x);
+            z[2][i] = bf16_lo(v[i].y);
+            z[3][i] = bf16_hi(v[i].y);
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            rht16_inplace(z[j], mask);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            store16_stream(y + off + i * cols, make_float4(z[0][i], z[1][i], z[2][i], z[3][i]));
     }
 }
 
@@ -143,7 +145,7 @@ hipError_t launch_rht16(const uint16_t* x, int64_t rows, int64_t cols, int axis,
                         float* y, hipStream_t stream)
 {
     if (axis == 0) {
-        const int64_t items = (rows >> 4) * (cols >> 3);
+        const int64_t items = (rows >> 4) * (cols >> 2);
         hipLaunchKernelGGL(rht16_axis0_kernel, dim3(grid_for(items)), dim3(kThreads), 0, stream, x,
                            rows, cols, mask, y);
     } else {
