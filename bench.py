@@ -39,6 +39,8 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+ALU_NOTE = ("vector-ALU bound, not HBM: Philox (two 32x32->64 multiplies per round, 10 rounds per "
+            "8 elements), the 16-point butterfly and the SR encode; the HBM fraction is context")
 F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 (= bf16) matrix peak, TFLOP/s
 # Plain vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one op per lane
 # per clock, no packed math).
@@ -252,7 +254,7 @@ def main():
         row_hbm("quantize_colwise_rht_sr_activation",
                 timed(lambda: F.nvfp4_quantize_1d(x, a_rht, rowwise=False, colwise=True, sr=True, rht=True,
                                                   rht_mask=mask, seed=W.SR_SEED, out=o)),
-                n_x * 2.5625, [R, C])
+                n_x * 2.5625, [R, C], note=ALU_NOTE)
         deq = torch.empty((R, C), dtype=torch.float32, device=dev)
         F.nvfp4_quantize_1d(x, amax, rowwise=True, colwise=False, out=o)
         row_hbm("dequantize_1d_fp32_activation",
@@ -278,7 +280,7 @@ def main():
         row_hbm("quantize_colwise_rht_sr_gradient",
                 timed(lambda: F.nvfp4_quantize_1d(g, a_rht, rowwise=False, colwise=True, sr=True, rht=True,
                                                   rht_mask=mask, seed=W.SR_SEED, out=og)),
-                n_g * 2.5625, [GR, GC])
+                n_g * 2.5625, [GR, GC], note=ALU_NOTE)
         y = torch.empty((GR, GC), dtype=torch.float32, device=dev)
         row_hbm("rht16_axis0_gradient", timed(lambda: F.nvfp4_rht16(g, axis=0, rht_mask=mask, out=y)),
                 n_g * 6, [GR, GC])
