@@ -169,7 +169,9 @@ int nvfp4_rht16(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint16_
  * nvfp4_dequantize -- x = e2m1(code) * e4m3(scale) * S_g (page "NVFP4 Is a
  * Scaling System", section "The smallest example"), in binary32:
  * fl(fl(e2m1*scale) * S_g) (the inner product is exact), converted to bf16
- * by round-to-nearest-even when out_dtype is NVFP4_BF16.
+ * by round-to-nearest-even when out_dtype is NVFP4_BF16. Any scale byte is
+ * accepted: a set sign bit negates the scale, and the E4M3 NaN bytes (0x7F,
+ * 0xFF) give NaN carrying the code's sign.
  *   codes         [rows][cols/2] packed codes of one layout
  *   scales        [rows][cols/16] (NVFP4_SCALE_1D) or [rows/16][cols/16]
  *                 (NVFP4_SCALE_2D)
@@ -185,9 +187,11 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int scale_mode
  * nvfp4_gemm -- C = A * B^T from packed NVFP4 operands (TN layout: both
  * operands are K-contiguous, as the NVFP4 GEMM takes them; page "NVFP4 Is a
  * Scaling System", section "“4-bit” is a payload count"): every operand
- * element is decoded exactly (e2m1 * e4m3 fits bf16), products are summed
+ * element is decoded exactly (e2m1 * e4m3 has at most 6 significant bits
+ * and lies in [2^-10, 2688], so it is an fp16 value), products are summed
  * in fp32 on the matrix cores, and the sum is multiplied by
- * fl(S_gA * S_gB).
+ * fl(S_gA * S_gB). The summation order differs from a sequential sum, so
+ * results match an exact product to fp32 rounding, not bit for bit.
  *   a_codes [M][K/2], a_scales per a_scale_mode over [M][K]
  *   b_codes [N][K/2], b_scales per b_scale_mode over [N][K]
  *   a_global_scale, b_global_scale: device floats
