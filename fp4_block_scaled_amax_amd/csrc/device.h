@@ -145,12 +145,49 @@ __device__ __forceinline__ uint32_t block_scale_byte_fast(uint32_t b_bits, float
     return r < 0x7Eu ? r : 0x7Eu;  // 432 and above round to (or saturate at) 448
 }
 
+// What decides whether a batch of block_scale_byte_approx results are all
+// exact: every y must be a normal E4M3 value (2^-6 <= y, byte <= 0x7E, so
+// not NaN, infinite or past the rounding to 480) and no y may lie within 3
+// ulp of an E4M3 rounding midpoint.
+struct ScaleVote {
+    uint32_t min_y = 0xFFFFFFFFu;
+    uint32_t min_guard = 0xFFFFFFFFu;
+    uint32_t max_byte = 0u;
+    __device__ __forceinline__ bool ok() const
+    {
+        return min_y >= 0x3C800000u && min_guard >= 7u && max_byte <= 0x7Eu;
+    }
+};
+
+// Branch-free form of block_scale_byte_fast for batches: the byte of
+// y = fl(b * inv_t) by integer rounding (exponent rebiased in the same add),
+// with the checks deferred to `vote`. When vote.ok() holds for the batch,
+// every byte equals block_scale_byte(b, t).
+__device__ __forceinline__ uint32_t block_scale_byte_approx(uint32_t b_bits, float inv_t,
+                                                            ScaleVote& vote)
+{
+    const uint32_t u = __float_as_uint(__uint_as_float(b_bits) * inv_t);
+    vote.min_y = min(vote.min_y, u);
+    vote.min_guard = min(vote.min_guard, (u & 0xFFFFFu) - 0x7FFFDu);
+    const uint32_t byte = (u + (0x7FFFFu - (960u << 20)) + ((u >> 20) & 1u)) >> 20;
+    vote.max_byte = max(vote.max_byte, byte);
+    return byte;
+}
+
 // The 128 possible multipliers of a tensor (one per scale byte 0..127),
 // built once per workgroup in LDS by the first 128 threads.
 __device__ __forceinline__ void build_reciprocal_table(float* table, float sg)
 {
     if (threadIdx.x < 128)
         table[threadIdx.x] = unit_reciprocal(threadIdx.x, sg);
+}
+
+// Sufficient for every multiplier of a byte 0..126 to be finite: then
+// d = fl(s * sg) is 0 (byte 0) or lies in [2^-109, 2^109] for the scales
+// s in [2^-9, 448], so 1/d is finite. False for NaN.
+__device__ __forceinline__ bool reciprocals_finite(float sg)
+{
+    return sg >= 0x1p-100f && sg <= 0x1p100f;
 }
 
 // ----------------------------------------------------------- E2M1 codes
@@ -260,6 +297,17 @@ __device__ __forceinline__ uint32_t swap_lane1(uint32_t v)
 __device__ __forceinline__ float swap_lane1(float v)
 {
     return __uint_as_float(swap_lane1(__float_as_uint(v)));
+}
+
+// The value of the even (from_even_lane) or odd lane of each lane pair, on
+// both lanes of the pair.
+__device__ __forceinline__ float from_even_lane(float v)
+{
+    return __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(v), 0xA0, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float from_odd_lane(float v)
+{
+    return __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(v), 0xF5, 0xF, 0xF, false));
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)

@@ -335,17 +335,22 @@ __device__ __forceinline__ void column_maxima(const uint4 (&v)[16], BlockMax& bm
 // pair must be active (both are, as the item validity is pairwise).
 __device__ __forceinline__ void row_maxima(const uint4 (&v)[16], bool odd, BlockMax& bm)
 {
-    uint32_t rm[16];
+    uint32_t pm[16];  // per row: packed maxima of the lane's 4 column pairs
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t pm = pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
-                                       pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu));
-        rm[i] = max(pm & 0xFFFFu, pm >> 16);
-    }
+    for (int i = 0; i < 16; ++i)
+        pm[i] = pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
+                           pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu));
 #pragma unroll
     for (int k = 0; k < 8; k += 2) {
-        const uint32_t send = (odd ? rm[k] : rm[k + 8]) | ((odd ? rm[k + 1] : rm[k + 9]) << 16);
-        const uint32_t own = (odd ? rm[k + 8] : rm[k]) | ((odd ? rm[k + 9] : rm[k + 1]) << 16);
+        // This lane's maxima of rows k, k+1 (low, high half) and of rows
+        // k+8, k+9: the low halves of a row pair in one word, the high
+        // halves in the other, then one packed max.
+        const uint32_t lo = pk_max_u16(__builtin_amdgcn_perm(pm[k + 1], pm[k], 0x05040100u),
+                                       __builtin_amdgcn_perm(pm[k + 1], pm[k], 0x07060302u));
+        const uint32_t hi = pk_max_u16(__builtin_amdgcn_perm(pm[k + 9], pm[k + 8], 0x05040100u),
+                                       __builtin_amdgcn_perm(pm[k + 9], pm[k + 8], 0x07060302u));
+        const uint32_t own = odd ? hi : lo;
+        const uint32_t send = odd ? lo : hi;
         bm.row[k >> 1] = pk_max_u16(own, swap_lane1(send));
     }
 }
@@ -357,6 +362,16 @@ __device__ __forceinline__ uint32_t half_bits(uint32_t packed)
     return H ? (packed & 0xFFFF0000u) : (packed << 16);
 }
 
+__device__ __forceinline__ uint32_t col_max_bits(const BlockMax& bm, int j)
+{
+    return (j & 1) ? half_bits<1>(bm.col[j >> 1]) : half_bits<0>(bm.col[j >> 1]);
+}
+
+__device__ __forceinline__ uint32_t row_max_bits(const BlockMax& bm, int k)
+{
+    return (k & 1) ? half_bits<1>(bm.row[k >> 1]) : half_bits<0>(bm.row[k >> 1]);
+}
+
 __device__ __forceinline__ uint32_t item_max(const BlockMax& bm)
 {
     uint32_t pm = pk_max_u16(pk_max_u16(bm.col[0], bm.col[1]), pk_max_u16(bm.col[2], bm.col[3]));
@@ -366,7 +381,8 @@ __device__ __forceinline__ uint32_t item_max(const BlockMax& bm)
 // Per-tensor constants of the scale chain.
 struct ScaleCtx {
     float sg, t6, inv_t6;
-    bool fast;  // t6 > 0 with t6 and 1/t6 finite: block_scale_byte_fast applies
+    bool fast;      // t6 > 0 with t6 and 1/t6 finite: block_scale_byte_fast applies
+    bool table_ok;  // every multiplier of a byte 0..126 is known to be finite
 };
 
 __device__ __forceinline__ ScaleCtx scale_ctx(float amax)
@@ -376,6 +392,7 @@ __device__ __forceinline__ ScaleCtx scale_ctx(float amax)
     c.t6 = 6.0f * c.sg;
     c.inv_t6 = 1.0f / c.t6;
     c.fast = c.t6 > 0.0f && finite_bits(c.t6) && finite_bits(c.inv_t6);
+    c.table_ok = reciprocals_finite(c.sg);
     return c;
 }
 
@@ -466,14 +483,44 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
         if (!odd)
             p.scales_row[(r0 >> 4) * (cols >> 4) + (c0 >> 4)] = (uint8_t)byte;
     } else {
+        // All of the item's scale bytes by the branch-free approximate
+        // chain, checked once for the wave; a wave holding any block it
+        // cannot settle redoes them all with the exact chain.
+        uint32_t row_byte[8];
+        ScaleVote vote;
         if (COL) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t m = (j & 1) ? half_bits<1>(bm.col[j >> 1]) : half_bits<0>(bm.col[j >> 1]);
-                col_byte[j] = scale_byte(m, sc);
-                rc[j] = lds_rcp[col_byte[j]];
-                fin = fin && finite_bits(rc[j]);
+            for (int j = 0; j < 8; ++j)
+                col_byte[j] = block_scale_byte_approx(col_max_bits(bm, j), sc.inv_t6, vote);
+        }
+        if (ROW) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                row_byte[k] = block_scale_byte_approx(row_max_bits(bm, k), sc.inv_t6, vote);
+        }
+        fin = sc.table_ok;
+        if (!__all(sc.fast && vote.ok())) {
+            uint32_t mb = 0u;
+            if (COL) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    col_byte[j] = scale_byte(col_max_bits(bm, j), sc);
+                    mb = max(mb, col_byte[j]);
+                }
             }
+            if (ROW) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    row_byte[k] = scale_byte(row_max_bits(bm, k), sc);
+                    mb = max(mb, row_byte[k]);
+                }
+            }
+            fin = fin && mb <= 0x7Eu;  // 0x7F (a NaN block) has no finite multiplier
+        }
+        if (COL) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                rc[j] = lds_rcp[col_byte[j]];
         }
         if (ROW) {
             // Even lanes own rows 0..7 of the pair's blocks, odd lanes 8..15.
@@ -481,15 +528,22 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
             uint8_t* sdst = p.scales_row + srow0 * (cols >> 4) + (c0 >> 4);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const uint32_t m = (k & 1) ? half_bits<1>(bm.row[k >> 1]) : half_bits<0>(bm.row[k >> 1]);
-                const uint32_t byte = scale_byte(m, sc);
-                sdst[k * (cols >> 4)] = (uint8_t)byte;
-                const float mine = lds_rcp[byte];
-                const float other = swap_lane1(mine);
-                rr[k] = odd ? other : mine;
-                rr[k + 8] = odd ? mine : other;
-                fin = fin && finite_bits(mine);
+                sdst[k * (cols >> 4)] = (uint8_t)row_byte[k];
+                const float mine = lds_rcp[row_byte[k]];
+                rr[k] = from_even_lane(mine);     // rows 0..7: settled by the even lane
+                rr[k + 8] = from_odd_lane(mine);  // rows 8..15: by the odd lane
             }
+        }
+        if (!sc.table_ok) {
+            // Some multiplier is not finite (tiny or non-finite amax): test
+            // the ones in use.
+            fin = true;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                fin = fin && (!COL || finite_bits(rc[j]));
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                fin = fin && (!ROW || finite_bits(rr[k]));
         }
     }
     uint32_t colw[8][2];
