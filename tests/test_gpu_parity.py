@@ -221,6 +221,61 @@ def test_sr_wide_dynamic_range(layouts):
     check_q1(x, got, a, rowwise, colwise, True, False)
 
 
+def scale_straddlers(amax):
+    """Positive bf16 block maxima b <= amax whose E4M3 scale byte differs
+    between fl(b / t), the rule, and fl(b * fl(1/t)), a multiply by the
+    reciprocal (t = 6 * S_g): the blocks where that shortcut would round
+    the scale the wrong way."""
+    b = (np.arange(1, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    b = b[b <= amax]
+    t = np.float32(6.0) * np.float32(oracle.global_scale(amax))
+    by_rcp = oracle.e4m3_encode_array(b * (np.float32(1.0) / t))
+    by_div = oracle.e4m3_encode_array(b / t)
+    return b[by_rcp != by_div]
+
+
+def straddle_tensor(rows, cols, seed):
+    """amax 0.00189208984375 (bf16 0x3AF8) has a straddling block maximum in
+    each of 15 binades. Every 16x16 tile carries one on its diagonal (so it is
+    the maximum of one row block and one column block), over noise 16x
+    smaller; every fifth tile is all zeros, and one element is the amax."""
+    amax = np.float32(0.00189208984375)
+    hits = scale_straddlers(amax)
+    assert hits.size >= 10
+    rng = np.random.default_rng(seed)
+    x = (rng.uniform(-1.0, 1.0, size=(rows, cols)) * float(hits.min()) / 16.0).astype(np.float32)
+    i = np.arange(rows)
+    for c0 in range(0, cols, 16):
+        diag = rng.choice(hits, size=rows) * np.where(rng.random(rows) < 0.5, -1.0, 1.0)
+        x[i, c0 + (i % 16)] = diag
+    for t, (r0, c0) in enumerate((r, c) for r in range(0, rows, 16) for c in range(0, cols, 16)):
+        if t % 5 == 3:
+            x[r0:r0 + 16, c0:c0 + 16] = 0.0
+    x[1, 1] = amax
+    return W.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("layouts", [(True, True), (True, False), (False, True)])
+def test_scale_bytes_near_rounding_midpoints(layouts, fused):
+    """Block maxima whose scale sits next to an E4M3 rounding midpoint, all
+    through the tensor and mixed with all-zero blocks in the same waves:
+    scale bytes and codes bit-identical to the oracle (division rule)."""
+    rowwise, colwise = layouts
+    x = straddle_tensor(128, 512, 31)
+    log(f"[test_scale_bytes_near_rounding_midpoints] {layouts} fused={fused}")
+    if fused:
+        out = F.nvfp4_quantize_1d(dev(x), F.nvfp4_workspace(), rowwise=rowwise, colwise=colwise,
+                                  fused_amax=True)
+        torch.cuda.synchronize()
+        got = {k: host(v) for k, v in out.items()}
+        a = np.float32(oracle.amax(x))
+    else:
+        got, a = run_q1(x, rowwise, colwise)
+    assert a == np.float32(0.00189208984375)
+    check_q1(x, got, a, rowwise, colwise, False, False)
+
+
 def test_quantize_deterministic():
     x = wl("ragged_grad")
     g1, _ = run_q1(x, True, True, sr=True)
