@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_bf16_kernel(const uint4* __
         uint4 v[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            v[u] = load16(&x[i + u * stride]);
+            v[u] = load16_stream(&x[i + u * stride]);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             pm = pk_max_u16(pm, v[u].x & 0x7FFF7FFFu);
@@ -121,7 +121,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t st
     uint32_t* out = reinterpret_cast<uint32_t*>(amax);
     hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(1), 0, stream, out);
     const int64_t nvec = n >> 3;
-    constexpr int kUnroll = 4;
+    constexpr int kUnroll = 16;
     const int grid = grid_for(nvec, kAmaxThreads * kUnroll, kAmaxMaxBlocks);
     hipLaunchKernelGGL((amax_bf16_kernel<kUnroll>), dim3(grid), dim3(kAmaxThreads), 0, stream,
                        reinterpret_cast<const uint4*>(x), nvec, x + nvec * 8, (int)(n & 7), out);
