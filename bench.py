@@ -224,6 +224,8 @@ def main():
         src.fill_(1.0)
         row_hbm("copy_256MiB_torch", timed(lambda: dst.copy_(src)), 2 * src.numel() * 4, [src.numel()],
                 note="device copy: practical streaming ceiling (read + write)")
+        row_hbm("fill_256MiB_torch", timed(lambda: dst.fill_(2.0)), src.numel() * 4, [src.numel()],
+                note="device fill: practical ceiling for write-only streams")
         del src, dst
         x = xs[0]
         n_x = R * C

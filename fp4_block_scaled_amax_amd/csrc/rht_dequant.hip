@@ -85,8 +85,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 }
 
 // Each thread owns E consecutive elements of a row (E = 4 for binary32
-// output, 8 for bf16: 16 bytes either way) and walks down the rows, so a
-// wave's stores are 1 KB contiguous. Decoding is exact hardware work: the
+// output, 8 for bf16: 16 bytes either way) and walks down the rows, four
+// adjacent rows at a time whose codes and scales are all loaded before
+// decoding, so a wave's stores are 1 KB contiguous and the loads' latency
+// overlaps. Plain stores: the streaming hint measured slower here. Decoding is exact hardware work: the
 // scale byte through the E4M3 convert, two codes per E2M1 convert (unit
 // scale); then (G * s) is exact and one rounding multiplies by S_g. A NaN
 // scale gives NaN with the code's sign (the reconstruction negates the
@@ -99,42 +101,62 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint8_t* __r
                                                                void* __restrict__ out)
 {
     constexpr int E = BF16 ? 8 : 4;
+    constexpr int U = 4;  // adjacent rows whose loads are in flight together
     const int64_t chunk = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     const int64_t c0 = chunk * E;
     if (c0 >= cols)
         return;
     const float sg = *sgp;
     const int64_t bpr = cols >> 4;  // scale blocks per row
-    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-        const uint8_t* cp = codes + ((r * cols + c0) >> 1);
-        const uint32_t w = BF16 ? *reinterpret_cast<const uint32_t*>(cp)
-                                : (uint32_t)*reinterpret_cast<const uint16_t*>(cp);
-        const uint32_t sb = TWO_D ? scales[(r >> 4) * bpr + (c0 >> 4)] : scales[r * bpr + (c0 >> 4)];
-        const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.0f, false)[0];
-        float v[E];
+    const int64_t step = gridDim.y;
+    for (int64_t r0 = (int64_t)blockIdx.y * U; r0 < rows; r0 += step * U) {
+        // All loads of U rows first: each row's codes and scale are a few
+        // bytes, so one row at a time would leave the thread waiting on
+        // load latency for every row.
+        uint32_t w[U], sb[U];
 #pragma unroll
-        for (int j = 0; j < E / 2; ++j) {
-            auto g = j == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
-                   : j == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
-                   : j == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
-                            : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                v[2 * j + h] = (g[h] * s) * sg;
-            if (s != s) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    v[2 * j + h] = __uint_as_float(0x7FC00000u | (__float_as_uint(g[h]) & 0x80000000u));
+        for (int u = 0; u < U; ++u) {
+            const int64_t r = r0 + u;
+            w[u] = 0u;
+            sb[u] = 0u;
+            if (r < rows) {
+                const uint8_t* cp = codes + ((r * cols + c0) >> 1);
+                w[u] = BF16 ? *reinterpret_cast<const uint32_t*>(cp)
+                            : (uint32_t)*reinterpret_cast<const uint16_t*>(cp);
+                sb[u] = TWO_D ? scales[(r >> 4) * bpr + (c0 >> 4)] : scales[r * bpr + (c0 >> 4)];
             }
         }
-        if (BF16) {
-            uint32_t q[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                q[k] = f32_to_bf16_rne(v[2 * k]) | (f32_to_bf16_rne(v[2 * k + 1]) << 16);
-            store16_stream(reinterpret_cast<uint16_t*>(out) + r * cols + c0, make_uint4(q[0], q[1], q[2], q[3]));
-        } else {
-            store16_stream(reinterpret_cast<float*>(out) + r * cols + c0, make_float4(v[0], v[1], v[2], v[3]));
+        for (int u = 0; u < U; ++u) {
+            const int64_t r = r0 + u;
+            if (r >= rows)
+                break;
+            const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb[u], 1.0f, false)[0];
+            float v[E];
+#pragma unroll
+            for (int j = 0; j < E / 2; ++j) {
+                auto g = j == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 0)
+                       : j == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 1)
+                       : j == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 2)
+                                : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 3);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    v[2 * j + h] = (g[h] * s) * sg;
+                if (s != s) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        v[2 * j + h] = __uint_as_float(0x7FC00000u | (__float_as_uint(g[h]) & 0x80000000u));
+                }
+            }
+            if (BF16) {
+                uint32_t q[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    q[k] = f32_to_bf16_rne(v[2 * k]) | (f32_to_bf16_rne(v[2 * k + 1]) << 16);
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + r * cols + c0) = make_uint4(q[0], q[1], q[2], q[3]);
+            } else {
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + r * cols + c0) = make_float4(v[0], v[1], v[2], v[3]);
+            }
         }
     }
 }
@@ -160,13 +182,13 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, bool t
                              const float* global_scale, int64_t rows, int64_t cols, void* out,
                              bool bf16_out, hipStream_t stream)
 {
-    // x: 16-byte column chunks of a row; y: rows, walked with a stride so
-    // that about 2048 workgroups cover the tensor.
+    // x: 16-byte column chunks of a row; y: groups of 4 rows, walked with a
+    // stride so that about 4096 workgroups cover the tensor.
     const int64_t chunks = cols / (bf16_out ? 8 : 4);
     const int64_t gx = (chunks + kThreads - 1) / kThreads;
-    int64_t gy = 2048 / gx;
+    int64_t gy = 4096 / gx;
     gy = gy < 1 ? 1 : gy;
-    gy = gy > rows ? rows : gy;
+    gy = gy > (rows + 3) / 4 ? (rows + 3) / 4 : gy;
     gy = gy > 65535 ? 65535 : gy;
     if (gx > 0x7FFFFFFF)
         return hipErrorInvalidValue;
