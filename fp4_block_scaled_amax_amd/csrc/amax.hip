@@ -35,7 +35,10 @@ __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* out)
     }
 }
 
-// bf16 [n]: 16-byte vectors, UNROLL loads in flight per thread.
+// bf16 [n]: 16-byte vectors, UNROLL loads in flight per thread. Plain
+// (cache-allocating) loads: the quantize pass that follows an amax re-reads
+// the same tensor and then finds it in the Infinity Cache (amax + quantize
+// row+col of 8192x4096: 35.9 us, against 39.7 us with streaming loads).
 template <int UNROLL>
 __global__ __launch_bounds__(kAmaxThreads) void amax_bf16_kernel(const uint4* __restrict__ x,
                                                               int64_t nvec,
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_bf16_kernel(const uint4* __
         uint4 v[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            v[u] = load16_stream(&x[i + u * stride]);
+            v[u] = load16(&x[i + u * stride]);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             pm = pk_max_u16(pm, v[u].x & 0x7FFF7FFFu);
