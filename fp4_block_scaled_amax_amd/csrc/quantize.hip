@@ -48,6 +48,7 @@ struct Params {
     uint8_t* scales_col;
     float* sg_out;
     int tiles_r, tiles_c;
+    int amax_given;  // quantize_fused_kernel: *amax holds the amax, no exchange
 };
 
 // Map the workgroup index to a tile so that each XCD (workgroups are dealt
@@ -656,7 +657,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
 // workgroups fit on the device at once; the waits are bounded by wall-clock
 // time and, should they expire (workgroups not co-resident), a workgroup
 // computes the exact amax directly from the tensor, so the result is always
-// the same and the device can never hang.
+// the same and the device can never hang. With Params::amax_given the
+// kernel takes the amax from memory instead and skips the exchange (then any
+// grid size works): the two-layout quantize with a given amax uses it for
+// its paired tiles.
 //
 // Workspace (32-bit words): [0] amax bits, [1] generation of the last
 // completed call, [2] slow-path counter, then 2 words per workgroup of
@@ -897,7 +901,7 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
     const ItemPos qa = item_pos(tra, tc, p.rows, p.cols);
     const ItemPos qb = item_pos(tra + 1, tc, p.rows, p.cols);
     uint32_t gen = 0u;
-    if (threadIdx.x == 0)
+    if (!p.amax_given && threadIdx.x == 0)
         gen = call_generation(ws);
     uint4 va[16], vb[16];
     load_item(p, qa, va);
@@ -922,7 +926,7 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
             row_maxima(vb, qb.odd, bb);
         m = max(m, item_max(bb));
     }
-    const uint32_t amax_bits = grid_max(m, gen, ws, p);
+    const uint32_t amax_bits = p.amax_given ? __float_as_uint(*p.amax) : grid_max(m, gen, ws, p);
 
     const ScaleCtx sc = scale_ctx(__uint_as_float(amax_bits));
     if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
@@ -982,6 +986,17 @@ hipError_t launch_fused_variant(Params p, uint32_t* ws, hipStream_t stream, bool
     return hipGetLastError();
 }
 
+// The paired-tile kernel with the amax given: no exchange, so any grid size.
+template <bool ROW, bool COL, bool SR>
+hipError_t launch_paired(Params p, hipStream_t stream)
+{
+    p.amax_given = 1;
+    const int64_t grid = (int64_t)((p.tiles_r + 1) / 2) * p.tiles_c;
+    hipLaunchKernelGGL((quantize_fused_kernel<ROW, COL, SR>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       stream, p, nullptr);
+    return hipGetLastError();
+}
+
 template <bool ROW, bool COL, bool TWO_D, bool SR, bool RHT>
 hipError_t launch_variant(const Params& p, hipStream_t stream)
 {
@@ -1011,6 +1026,7 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
         p.sg_out = a.global_scale;
         p.tiles_r = (int)((a.rows + kTileR - 1) / kTileR);
         p.tiles_c = (int)((a.cols + kTileC - 1) / kTileC);
+        p.amax_given = 0;
         bool launched = false;
         hipError_t e;
         if (a.rowwise && a.colwise)
@@ -1049,6 +1065,7 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
     p.sg_out = a.global_scale;
     p.tiles_r = (int)((a.rows + kTileR - 1) / kTileR);
     p.tiles_c = (int)((a.cols + kTileC - 1) / kTileC);
+    p.amax_given = 0;
 
     if (a.two_d) {
         if (a.rowwise && a.colwise)
@@ -1062,9 +1079,12 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
         return a.sr ? launch_variant<false, true, false, true, true>(p, stream)
                     : launch_variant<false, true, false, false, true>(p, stream);
     }
+    // Both layouts: the paired-tile kernel (whole-line columnwise stores),
+    // here without its exchange.
     if (a.rowwise && a.colwise)
-        return a.sr ? launch_variant<true, true, false, true, false>(p, stream)
-                    : launch_variant<true, true, false, false, false>(p, stream);
+        return a.sr ? launch_paired<true, true, true>(p, stream)
+                    : launch_paired<true, true, false>(p, stream);
+    // One layout: one tile per workgroup measured faster than the pairs.
     if (a.rowwise)
         return a.sr ? launch_variant<true, false, false, true, false>(p, stream)
                     : launch_variant<true, false, false, false, false>(p, stream);
