@@ -320,6 +320,25 @@ def main():
                           "frac": round(tf / F16_MFMA_PEAK_TFLOPS, 4)}
             log(f"[bench] {name}: {us:.0f} us {tf:.1f} TFLOP/s")
         gemm_tflops = rows["gemm_fp32_out"]["TFLOP/s"]
+        # Reference only (not a path of this library): the vendor fp16 GEMM
+        # (hipBLASLt through torch.matmul) on the same operand values, decoded
+        # exactly to fp16 by nvfp4_dequantize with unit global scales.
+        one = torch.ones(1, dtype=torch.float32, device=dev)
+        da = F.nvfp4_dequantize(qa["codes_row"], qa["scales_row"], 1, one, M, K, out_dtype=torch.float32).half()
+        db = F.nvfp4_dequantize(qb["codes_row"], qb["scales"], 2, one, N, K, out_dtype=torch.float32).half()
+        ch = torch.empty((M, N), dtype=torch.float16, device=dev)
+        dbt = db.t()
+        for _ in range(50):
+            torch.matmul(da, dbt, out=ch)
+        torch.cuda.synchronize()
+        us = timed(lambda: torch.matmul(da, dbt, out=ch), iters=max(3, args.row_iters // 2))
+        tf = flop / (us * 1e-6) / 1e12
+        rows["reference_hipblaslt_fp16_gemm_same_values"] = {
+            "shape": [M, N, K], "us": round(us, 1), "flop": flop, "TFLOP/s": round(tf, 1),
+            "note": "vendor fp16 GEMM on the decoded operand values (reads 4x the operand bytes, no "
+                    "decode); context for gemm_fp32_out, not part of this library"}
+        log(f"[bench] reference hipBLASLt fp16 GEMM on the same values: {us:.0f} us {tf:.1f} TFLOP/s")
+        del da, db, dbt, ch
         del flush
 
     # -------------------------------------------------- CPU oracle baseline
