@@ -663,10 +663,12 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
 // its paired tiles.
 //
 // Workspace (32-bit words): [0] amax bits, [1] generation of the last
-// completed call, [2] slow-path counter, then 2 words per workgroup of
-// arrival slots and 2 words per workgroup of release slots.
+// completed call, [2] slow-path counter, [3] wait limit in ticks of the
+// 100 MHz counter (0: the default; a tiny value makes every wait expire, so
+// tests can drive the fallback), then 2 words per workgroup of arrival
+// slots and 2 words per workgroup of release slots.
 
-constexpr int kWsAmax = 0, kWsGen = 1, kWsSlow = 2, kWsArrive = 16;
+constexpr int kWsAmax = 0, kWsGen = 1, kWsSlow = 2, kWsWait = 3, kWsArrive = 16;
 constexpr int kMaxFusedBlocks = 2048;                       // slots in the workspace
 constexpr int kWsRelease = kWsArrive + 2 * kMaxFusedBlocks;
 constexpr int kMaxFusedGrid = 1024;                         // largest grid launched
@@ -736,19 +738,22 @@ __device__ __forceinline__ uint32_t call_generation(const uint32_t* ws)
 }
 
 // Grid-wide maximum of one value per workgroup (binary32 bits); every
-// workgroup returns the same result. gen: call_generation(), read by
-// thread 0.
-__device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t* ws, const Params& p)
+// workgroup returns the same result. gen0 and wait0 (workspace word 3: the
+// bound on each wait in 100 MHz ticks, 0 for the default) are read by
+// thread 0 at the start of the kernel.
+__device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t* ws, const Params& p)
 {
     __shared__ uint32_t red[kThreads / 64];
-    __shared__ uint32_t gen_s, result_s, ok_s;
+    __shared__ uint32_t gen_s, wait_s, result_s, ok_s;
     m = workgroup_max(m, red);
     if (threadIdx.x == 0) {
         gen_s = gen0;
+        wait_s = wait0;
         slot_store(&ws[kWsArrive + 2 * blockIdx.x], gen0, m);
     }
     __syncthreads();
     const uint32_t gen = gen_s;
+    const uint64_t wait = wait_s != 0u ? (uint64_t)wait_s : kWaitTicks;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     if (blockIdx.x == 0) {
         // Collect every workgroup's maximum. Each thread watches the slots
@@ -776,7 +781,7 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t* ws, const Para
             }
             if (pending == 0u)
                 break;
-            if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > wait) {
                 ok = false;
                 break;
             }
@@ -811,7 +816,7 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t* ws, const Para
         uint64_t w = slot_load(&ws[kWsRelease + 2 * blockIdx.x]);
         ok_s = 1u;
         while ((uint32_t)w != gen) {
-            if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > wait) {
                 ok_s = 0u;
                 break;
             }
@@ -900,9 +905,11 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
     const bool has_b = tra + 1 < p.tiles_r;  // uniform over the workgroup
     const ItemPos qa = item_pos(tra, tc, p.rows, p.cols);
     const ItemPos qb = item_pos(tra + 1, tc, p.rows, p.cols);
-    uint32_t gen = 0u;
-    if (!p.amax_given && threadIdx.x == 0)
+    uint32_t gen = 0u, wait = 0u;
+    if (!p.amax_given && threadIdx.x == 0) {
         gen = call_generation(ws);
+        wait = ws_load(&ws[kWsWait]);
+    }
     uint4 va[16], vb[16];
     load_item(p, qa, va);
     if (has_b)
@@ -926,7 +933,7 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
             row_maxima(vb, qb.odd, bb);
         m = max(m, item_max(bb));
     }
-    const uint32_t amax_bits = p.amax_given ? __float_as_uint(*p.amax) : grid_max(m, gen, ws, p);
+    const uint32_t amax_bits = p.amax_given ? __float_as_uint(*p.amax) : grid_max(m, gen, wait, ws, p);
 
     const ScaleCtx sc = scale_ctx(__uint_as_float(amax_bits));
     if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)

@@ -125,8 +125,10 @@ int nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags, ui
  * nvfp4_amax would give). The single pass needs all of its workgroups on
  * the device at once; if they are not (another kernel holds the device),
  * a bounded wait expires, the amax is computed from x directly (same
- * result, slower) and 32-bit word 2 of the workspace is incremented. Calls
- * that overlap in time must use different workspaces.
+ * result, slower) and 32-bit word 2 of the workspace is incremented. Word 3
+ * sets that wait in ticks of the 100 MHz real-time counter (0, as after
+ * zero-filling: 2 ms; a tiny value forces the direct computation, for
+ * tests). Calls that overlap in time must use different workspaces.
  */
 int nvfp4_quantize_1d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
                       uint32_t flags, uint16_t rht_mask, uint64_t seed, uint8_t* codes_row,

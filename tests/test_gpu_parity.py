@@ -556,6 +556,36 @@ def test_fused_amax_quantize(name, sr, layouts):
         assert np.array_equal(got[k], two[k]), k
 
 
+@pytest.mark.parametrize("sr,layouts", [(False, (True, True)), (True, (True, True)), (False, (True, False)),
+                                       (False, (False, True))])
+def test_fused_exchange_fallback_forced(sr, layouts):
+    """Word 3 of the workspace set to one tick makes the exchange's waits
+    expire at once, so workgroups take the direct amax: the outputs are
+    still bit-identical to the oracle, the slow-path counter moves, and the
+    same workspace then serves a normal call (word 3 back to 0)."""
+    rowwise, colwise = layouts
+    x = W.activation(1024, 1280, seed=17)  # 4 x 5 workgroups: the release is never there in time
+    log(f"[test_fused_exchange_fallback_forced] sr={sr} layouts={layouts}")
+    xd = dev(x)
+    ws = F.nvfp4_workspace()
+    ws[3] = 1
+    out = F.nvfp4_quantize_1d(xd, ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED, fused_amax=True)
+    torch.cuda.synchronize()
+    wsh = host(ws)
+    assert wsh[2] > 0, "no workgroup took the direct amax"
+    got = {k: host(v) for k, v in out.items()}
+    check_q1(x, got, wsh[:1].view(np.float32)[0], rowwise, colwise, sr, False)
+    slow = int(wsh[2])
+    ws[3] = 0
+    out = F.nvfp4_quantize_1d(xd, ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED, fused_amax=True)
+    torch.cuda.synchronize()
+    wsh = host(ws)
+    assert int(wsh[2]) == slow, "the exchange fell back again with the default wait"
+    got2 = {k: host(v) for k, v in out.items()}
+    for k in got:
+        assert np.array_equal(got[k], got2[k]), k
+
+
 def test_fused_workspace_across_tensors():
     """Consecutive fused calls on different tensors through one workspace."""
     ws = F.nvfp4_workspace()
