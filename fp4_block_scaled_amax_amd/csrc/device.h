@@ -104,27 +104,14 @@ __device__ __forceinline__ float unit_reciprocal(uint32_t byte, float sg)
     return (d == 0.0f) ? 0.0f : 1.0f / d;
 }
 
-// Per-block scale chain. b_bits: binary32 bits of the block's max |x|.
-// sg = amax / 2688, t = 6 * sg. Outputs the scale byte and the element
-// multiplier r = 1 / (s * sg) (0 when that unit is 0).
-struct BlockScale {
-    uint32_t byte;
-    float r;
-};
-
+// Scale byte of a block. b_bits: binary32 bits of the block's max |x|;
+// t = 6 * sg with sg = amax / 2688. The IEEE division, exactly as the rule
+// states it.
 __device__ __forceinline__ uint32_t block_scale_byte(uint32_t b_bits, float t)
 {
     const float b = __uint_as_float(b_bits);
     const float s_f = (t == 0.0f) ? 0.0f : b / t;
     return e4m3_encode(s_f);
-}
-
-__device__ __forceinline__ BlockScale block_scale(uint32_t b_bits, float sg, float t)
-{
-    BlockScale out;
-    out.byte = block_scale_byte(b_bits, t);
-    out.r = unit_reciprocal(out.byte, sg);
-    return out;
 }
 
 // Same byte, cheaper: one multiply by inv_t = fl(1/t) instead of the IEEE
@@ -192,25 +179,14 @@ __device__ __forceinline__ bool reciprocals_finite(float sg)
 
 // ----------------------------------------------------------- E2M1 codes
 //
-// For a scaled magnitude v, the E2M1 grid has spacing 1/2 on [0, 2), 1 on
-// [2, 4) and 2 on [4, 6]. With j = clamp(exponent(v), 1, 3), v * 2^(2-j) is
-// exact and its integer part/rounding counts grid steps; adding
-// 2^23 + 2(j-1) + 8*sign in binary32 rounds to an integer (ties to even, and
-// the even offset keeps the parity) and leaves the 4-bit code in the low
-// bits of the result.
-
-__device__ __forceinline__ uint32_t e2m1_rne_nibble(float v, uint32_t sign8)
-{
-    v = fminf(fmaxf(v, 0.0f), 6.0f);                     // NaN -> 0, saturate at 6
-    int e = __builtin_amdgcn_frexp_expf(v);
-    int j = min(max(e, 1), 3);
-    float vs = __builtin_amdgcn_ldexpf(v, 2 - j);
-    float q = vs + __uint_as_float(0x4B000000u + 2u * (uint32_t)(j - 1) + sign8);
-    return __float_as_uint(q) & 0xFu;
-}
-
-// Stochastic rounding: round up with probability p = (v - lo)/(hi - lo),
-// decided as h < p * 2^16 for the element's 16-bit draw h.
+// Software stochastic rounding (used where a block multiplier is not finite;
+// the hardware converters cover every other case). For a scaled magnitude
+// v, the E2M1 grid has spacing 1/2 on [0, 2), 1 on [2, 4) and 2 on [4, 6].
+// With j = clamp(exponent(v), 1, 3), vs = v * 2^(2-j) is exact: its integer
+// part counts grid steps below v and its fraction is p = (v - lo)/(hi - lo).
+// The element rounds up when h < p * 2^16 for its 16-bit draw h. Adding
+// 2^23 + 2(j-1) + 8*sign in binary32 leaves the 4-bit code (the even offset
+// keeps the parity) in the low bits of the result.
 __device__ __forceinline__ uint32_t e2m1_sr_nibble(float v, uint32_t h16, uint32_t sign8)
 {
     v = fminf(fmaxf(v, 0.0f), 6.0f);

@@ -11,16 +11,22 @@
 //     (2k, 2k+1), which trade maxima and multipliers through DPP;
 //   - a 2D tile is the lane pair's 16 x 16 elements.
 // Rowwise codes are stored straight from registers (128 contiguous bytes per
-// row per half-wave). Columnwise codes are staged in LDS and leave as 64-byte
-// column segments; tiles are walked down the rows per XCD so that the two
-// halves of a 128-byte line are written by the same L2.
+// row per half-wave). Columnwise codes are staged in LDS; quantize_kernel
+// writes them as 64-byte column segments (tiles walked down the rows per
+// XCD, so the two halves of a line meet in one L2), while
+// quantize_fused_kernel holds two vertically adjacent tiles per workgroup
+// and writes whole 128-byte column lines. The fused kernel serves the
+// in-kernel amax (single pass) and, with the amax given, both layouts.
 //
 // Encoding: the element ratio v = x * r (r = 1 / (s * S_g) of its block) is
 // rounded to E2M1 by the gfx950 converter v_cvt_scalef32_pk_fp4_f32 with a
 // unit scale, which rounds to nearest even and saturates at +-6 exactly like
 // the reference rule for every non-NaN input (checked over all 2^32 binary32
 // patterns); a NaN ratio needs a non-finite r, and such blocks first map NaN
-// ratios to a signed zero. Stochastic rounding uses the software encoder.
+// ratios to a signed zero. Stochastic rounding runs on the SR converter
+// v_cvt_scalef32_sr_pk_fp4_f32 through an input mapping that reproduces the
+// rule exactly (see sr_operand); blocks with a non-finite multiplier use the
+// software encoder e2m1_sr_nibble.
 #include <atomic>
 
 #include "device.h"
