@@ -75,7 +75,8 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_bf16_kernel(const uint4* __
 }
 
 // amax of the 16-point Hadamard transform along axis 0. Work item: 16 rows
-// x 8 columns (sixteen 16-byte loads), transformed per column in registers.
+// x 8 columns (sixteen 16-byte loads), transformed per column in registers;
+// the sign diagonal is applied to the packed words, the 1/4 to the maximum.
 __global__ __launch_bounds__(kThreads) void amax_rht_kernel(const uint16_t* __restrict__ x,
                                                              int64_t rows, int64_t cols,
                                                              uint32_t mask,
@@ -90,20 +91,27 @@ __global__ __launch_bounds__(kThreads) void amax_rht_kernel(const uint16_t* __re
         const uint16_t* base = x + (rb * 16) * cols + cg * 8;
         uint4 v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+        for (int i = 0; i < 16; ++i) {
             v[i] = load16(base + i * cols);
+            const uint32_t sg = rht_row_sign(mask, i);
+            v[i] = make_uint4(v[i].x ^ sg, v[i].y ^ sg, v[i].z ^ sg, v[i].w ^ sg);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             float z[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 z[i] = bf16_at(v[i], j);
-            rht16_inplace(z, mask);
+            hadamard16(z);
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 m = max(m, __float_as_uint(z[i]) & 0x7FFFFFFFu);
         }
     }
+    // The 1/4 once, on the maximum: scaling by a power of two is monotone
+    // (also where it rounds, in the subnormal range), so
+    // max |fl(z / 4)| = fl(max |z| / 4), and NaN stays NaN.
+    m = __float_as_uint(0.25f * __uint_as_float(m));
     workgroup_max_to<kThreads>(m, out);
 }
 

@@ -239,14 +239,27 @@ __device__ __forceinline__ uint32_t draw16(const uint4& w, int k)
 
 // ----------------------------------------------- 16-point Hadamard (FWHT)
 //
-// z_j = mask bit j ? -x_j : x_j; butterflies h = 1, 2, 4, 8 in natural
-// (Sylvester) order; y = z / 4.
-__device__ __forceinline__ void rht16_inplace(float (&z)[16], uint32_t mask)
+// y = (1/4) H16 D x: D negates element j of a 16-element segment when bit j
+// of the mask is set, H16 is the natural-order (Sylvester) Hadamard matrix,
+// evaluated as butterflies h = 1, 2, 4, 8 in binary32. D is applied to the
+// packed bf16 words before unpacking (a sign flip is exact), so the
+// butterfly takes already signed values.
+
+// XOR pattern of D for a 16-row segment: row i's packed bf16 words.
+__device__ __forceinline__ uint32_t rht_row_sign(uint32_t mask, int i)
 {
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-        if ((mask >> j) & 1u)
-            z[j] = -z[j];
+    return ((mask >> i) & 1u) ? 0x80008000u : 0u;
+}
+
+// XOR pattern of D for a segment along a row: word k (elements 2k, 2k+1).
+__device__ __forceinline__ uint32_t rht_pair_sign(uint32_t mask, int k)
+{
+    return (((mask >> (2 * k)) & 1u) << 15) | (((mask >> (2 * k + 1)) & 1u) << 31);
+}
+
+// The butterflies alone (H16 z, not yet scaled by 1/4).
+__device__ __forceinline__ void hadamard16(float (&z)[16])
+{
 #pragma unroll
     for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -258,6 +271,12 @@ __device__ __forceinline__ void rht16_inplace(float (&z)[16], uint32_t mask)
             z[j + h] = a - b;
         }
     }
+}
+
+// y = (1/4) H16 z for signed inputs z = D x.
+__device__ __forceinline__ void rht16_signed(float (&z)[16])
+{
+    hadamard16(z);
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         z[j] = 0.25f * z[j];

@@ -442,10 +442,12 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
             float y[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                y[i] = bf16_at(v[i], j);
+                y[i] = RHT ? bf16_at(make_uint4(v[i].x ^ rht_row_sign(p.mask, i), v[i].y ^ rht_row_sign(p.mask, i),
+                                                v[i].z ^ rht_row_sign(p.mask, i), v[i].w ^ rht_row_sign(p.mask, i)), j)
+                           : bf16_at(v[i], j);
             uint32_t m;
             if (RHT) {
-                rht16_inplace(y, p.mask);
+                rht16_signed(y);
                 m = 0u;
 #pragma unroll
                 for (int i = 0; i < 16; ++i)

@@ -36,8 +36,11 @@ __global__ __launch_bounds__(kThreads) void rht16_axis0_kernel(const uint16_t* _
         const int64_t off = (rb * 16) * cols + cg * 4;
         uint2 v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+        for (int i = 0; i < 16; ++i) {
             v[i] = load8_stream(x + off + i * cols);
+            v[i].x ^= rht_row_sign(mask, i);
+            v[i].y ^= rht_row_sign(mask, i);
+        }
         float z[4][16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -48,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void rht16_axis0_kernel(const uint16_t* _
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            rht16_inplace(z[j], mask);
+            rht16_signed(z[j]);
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             *reinterpret_cast<float4*>(y + off + i * cols) = make_float4(z[0][i], z[1][i], z[2][i], z[3][i]);
@@ -62,15 +65,19 @@ __global__ __launch_bounds__(kThreads) void rht16_axis1_kernel(const uint16_t* _
 {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x; s < nseg; s += stride) {
-        const uint4 a = load16_stream(x + s * 16);
-        const uint4 b = load16_stream(x + s * 16 + 8);
+        uint4 a = load16_stream(x + s * 16);
+        uint4 b = load16_stream(x + s * 16 + 8);
+        a = make_uint4(a.x ^ rht_pair_sign(mask, 0), a.y ^ rht_pair_sign(mask, 1), a.z ^ rht_pair_sign(mask, 2),
+                       a.w ^ rht_pair_sign(mask, 3));
+        b = make_uint4(b.x ^ rht_pair_sign(mask, 4), b.y ^ rht_pair_sign(mask, 5), b.z ^ rht_pair_sign(mask, 6),
+                       b.w ^ rht_pair_sign(mask, 7));
         float z[16];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             z[j] = bf16_at(a, j);
             z[j + 8] = bf16_at(b, j);
         }
-        rht16_inplace(z, mask);
+        rht16_signed(z);
         float4* dst = reinterpret_cast<float4*>(y + s * 16);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
