@@ -120,11 +120,12 @@ __device__ __forceinline__ uint32_t sr_random_word(uint32_t w)
     return HALF ? (~w | 0xFFFFu) : ~(w << 16);
 }
 
-// v -> the converter operand (2^23 |v|, rounded up below 2^23, sign of v).
+// v -> the converter operand: 2^23 |v| rounded up to an integer (every
+// binary32 value from 2^23 up already is one, so only |v| < 1 changes),
+// with the sign of v.
 __device__ __forceinline__ float sr_operand(float v)
 {
-    const float t = fabsf(v) * 0x1p23f;
-    const float tc = __builtin_amdgcn_fmed3f(__builtin_ceilf(t), t, 0x1p23f);
+    const float tc = __builtin_ceilf(fabsf(v) * 0x1p23f);
     return __uint_as_float((__float_as_uint(tc) & 0x7FFFFFFFu) | (__float_as_uint(v) & 0x80000000u));
 }
 
