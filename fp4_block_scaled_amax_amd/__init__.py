@@ -23,6 +23,7 @@ FUSED_AMAX = 0x10
 WORKSPACE_BYTES = 32832
 SCALE_1D = 1
 SCALE_2D = 2
+SCALE_2D_T = 3  # 2D tile scales of the transposed operand (GEMM only)
 F32 = 0
 BF16 = 1
 

@@ -192,8 +192,8 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode
     if (a_codes == nullptr || a_scales == nullptr || a_global_scale == nullptr ||
         b_codes == nullptr || b_scales == nullptr || b_global_scale == nullptr || c == nullptr)
         return NVFP4_ERR_NULL;
-    if ((a_scale_mode != NVFP4_SCALE_1D && a_scale_mode != NVFP4_SCALE_2D) ||
-        (b_scale_mode != NVFP4_SCALE_1D && b_scale_mode != NVFP4_SCALE_2D) ||
+    if (a_scale_mode < NVFP4_SCALE_1D || a_scale_mode > NVFP4_SCALE_2D_T ||
+        b_scale_mode < NVFP4_SCALE_1D || b_scale_mode > NVFP4_SCALE_2D_T ||
         (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16))
         return NVFP4_ERR_FLAGS;
     if (M <= 0 || N <= 0 || K <= 0 || M % 16 != 0 || N % 16 != 0 || K % 16 != 0)
@@ -206,11 +206,13 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode
     nvfp4::GemmArgs g{};
     g.a_codes = a_codes;
     g.a_scales = a_scales;
-    g.a_two_d = a_scale_mode == NVFP4_SCALE_2D;
+    g.a_two_d = a_scale_mode != NVFP4_SCALE_1D;
+    g.a_scales_t = a_scale_mode == NVFP4_SCALE_2D_T;
     g.a_sg = a_global_scale;
     g.b_codes = b_codes;
     g.b_scales = b_scales;
-    g.b_two_d = b_scale_mode == NVFP4_SCALE_2D;
+    g.b_two_d = b_scale_mode != NVFP4_SCALE_1D;
+    g.b_scales_t = b_scale_mode == NVFP4_SCALE_2D_T;
     g.b_sg = b_global_scale;
     g.c = c;
     g.c_bf16 = c_dtype == NVFP4_BF16;

@@ -67,27 +67,31 @@ struct RowStage {
 __device__ __attribute__((aligned(16))) const uint8_t kZeroScales[16] = {};
 
 // Fetch stage `stage` of this thread's row: 16 bytes of codes and the two
-// scale bytes at scale_row + stage * sstride (sstride 0 for rows past the
-// end, which read kZeroScales).
+// scale bytes, the first at scale_row + stage * sstride and the second
+// bstride after it (bstride 1: adjacent; transposed 2D scales: one scale row
+// apart; sstride = bstride = 0 for rows past the end, which read
+// kZeroScales).
 template <bool WIDE>
 __device__ __forceinline__ RowStage fetch_stage(const uint8_t* code_row, const uint8_t* scale_row,
-                                                int stage, int sstride, int64_t K)
+                                                int stage, int64_t sstride, int64_t bstride, int64_t K)
 {
     RowStage st;
     const int64_t k0 = (int64_t)stage * kBK;
     const uint8_t* sp = scale_row + (int64_t)stage * sstride;
+    const __attribute__((address_space(1))) uint8_t* gp = (const __attribute__((address_space(1))) uint8_t*)sp;
     if (WIDE) {
         st.codes = load16(code_row + (k0 >> 1));
-        st.scales = *(const __attribute__((address_space(1))) uint16_t*)sp;
+        if (bstride == 1)  // uniform over the wave (its rows are all A or all B)
+            st.scales = *(const __attribute__((address_space(1))) uint16_t*)sp;
+        else
+            st.scales = (uint16_t)(gp[0] | ((uint32_t)gp[bstride] << 8));
     } else {
         // K is an odd multiple of 16: the last stage has one block.
         const bool has2 = k0 + 16 < K;
         const uint2 lo = *reinterpret_cast<const uint2*>(code_row + (k0 >> 1));
         const uint2 hi = has2 ? *reinterpret_cast<const uint2*>(code_row + (k0 >> 1) + 8) : make_uint2(0u, 0u);
         st.codes = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        const __attribute__((address_space(1))) uint8_t* gp =
-            (const __attribute__((address_space(1))) uint8_t*)sp;
-        st.scales = (uint16_t)(gp[0] | (has2 ? (uint32_t)gp[sstride >> 1] << 8 : 0u));
+        st.scales = (uint16_t)(gp[0] | (has2 ? (uint32_t)gp[bstride] << 8 : 0u));
     }
     return st;
 }
@@ -163,6 +167,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     const bool is_b = t >= kBM;
     const int64_t rows = is_b ? g.N : g.M;
     const bool two_d = is_b ? g.b_two_d : g.a_two_d;
+    const bool scales_t = is_b ? g.b_scales_t : g.a_scales_t;
     const uint8_t* codes = is_b ? g.b_codes : g.a_codes;
     const uint8_t* scales = is_b ? g.b_scales : g.a_scales;
     uint8_t* my_row0 = lds + t * kRowBytes;
@@ -190,8 +195,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         const bool valid = row < rows;
         const int64_t rc = valid ? row : 0;
         const uint8_t* code_row = codes + rc * (K >> 1);
-        const uint8_t* scale_row = valid ? scales + (two_d ? (rc >> 4) : rc) * (K >> 4) : kZeroScales;
-        const int sstride = valid ? kBK / 16 : 0;
+        // Scale of (row, K block j): 1D [row][j], 2D [row/16][j], transposed
+        // 2D [j][row/16].
+        const int64_t tile_rows = (rows + 15) >> 4;
+        const uint8_t* scale_row = !valid    ? kZeroScales
+                                   : scales_t ? scales + (rc >> 4)
+                                              : scales + (two_d ? (rc >> 4) : rc) * (K >> 4);
+        const int64_t bstride = !valid ? 0 : scales_t ? tile_rows : 1;
+        const int64_t sstride = 2 * bstride;
 
         floatx16 acc[2][4];
 #pragma unroll
@@ -200,13 +211,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
             for (int b = 0; b < 4; ++b)
                 acc[a][b] = floatx16{};
 
-        decode_stage_to_lds(fetch_stage<WIDE>(code_row, scale_row, 0, sstride, K), my_row0);
+        decode_stage_to_lds(fetch_stage<WIDE>(code_row, scale_row, 0, sstride, bstride, K), my_row0);
         // Two register sets alternate (stage s+1 in one, s+2 in the other)
         // so a fetch lands in registers the decode has just consumed: no
         // copies of in-flight loads, hence no wait on the newest fetch.
-        RowStage sa = fetch_stage<WIDE>(code_row, scale_row, min(1, last), sstride, K);
+        RowStage sa = fetch_stage<WIDE>(code_row, scale_row, min(1, last), sstride, bstride, K);
         __builtin_amdgcn_sched_barrier(0);  // issue order sa, sb as in the loop
-        RowStage sb = fetch_stage<WIDE>(code_row, scale_row, min(2, last), sstride, K);
+        RowStage sb = fetch_stage<WIDE>(code_row, scale_row, min(2, last), sstride, bstride, K);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
 
@@ -214,14 +225,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         for (; s + 1 < nstages; s += 2) {
             stage_mfma(lds, wm, wn, frow, fk, acc);
             decode_stage_to_lds(sa, my_row0 + kStageBytes);
-            sa = fetch_stage<WIDE>(code_row, scale_row, min(s + 3, last), sstride, K);
+            sa = fetch_stage<WIDE>(code_row, scale_row, min(s + 3, last), sstride, bstride, K);
             __syncthreads();
             // keep each half's work in its half: the scheduler would
             // otherwise hoist the next decode and wait on the newest fetch
             __builtin_amdgcn_sched_barrier(0);
             stage_mfma(lds + kStageBytes, wm, wn, frow, fk, acc);
             decode_stage_to_lds(sb, my_row0);
-            sb = fetch_stage<WIDE>(code_row, scale_row, min(s + 4, last), sstride, K);
+            sb = fetch_stage<WIDE>(code_row, scale_row, min(s + 4, last), sstride, bstride, K);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
         }

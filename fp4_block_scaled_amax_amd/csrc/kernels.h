@@ -39,10 +39,12 @@ struct GemmArgs {
     const uint8_t* a_codes;
     const uint8_t* a_scales;
     bool a_two_d;
+    bool a_scales_t;  // 2D tile scales stored transposed ([K/16][M/16])
     const float* a_sg;
     const uint8_t* b_codes;
     const uint8_t* b_scales;
     bool b_two_d;
+    bool b_scales_t;  // 2D tile scales stored transposed ([K/16][N/16])
     const float* b_sg;
     void* c;
     bool c_bf16;

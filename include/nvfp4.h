@@ -62,6 +62,8 @@ extern "C" {
 /* scale_mode values */
 #define NVFP4_SCALE_1D 1 /* one scale per 16 consecutive elements of a row */
 #define NVFP4_SCALE_2D 2 /* one scale per 16x16 tile                       */
+#define NVFP4_SCALE_2D_T 3 /* 16x16 tile scales of the transposed operand:  */
+                           /* row n, K block j at [j][n/16] (GEMM only)     */
 
 /* dtype values */
 #define NVFP4_F32 0
@@ -196,6 +198,10 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int scale_mode
  * results match an exact product to fp32 rounding, not bit for bit.
  *   a_codes [M][K/2], a_scales per a_scale_mode over [M][K]
  *   b_codes [N][K/2], b_scales per b_scale_mode over [N][K]
+ *   Scale modes: NVFP4_SCALE_1D [rows][K/16]; NVFP4_SCALE_2D [rows/16][K/16];
+ *   NVFP4_SCALE_2D_T [K/16][rows/16], the tile scales that
+ *   nvfp4_quantize_2d writes for the tensor whose column layout is the
+ *   operand (a weight's dgrad copy: its codes_col with its scales).
  *   a_global_scale, b_global_scale: device floats
  *   c       [M][N] of c_dtype (fp32 or bf16, round-to-nearest-even)
  * M, N, K multiples of 16.

@@ -1,0 +1,167 @@
+"""GPU: the NVFP4 linear layer composed from the library (fprop, dgrad,
+wgrad), each GEMM against the double-precision product of its exactly
+reconstructed operands (||C - C_ref||_F / ||C_ref||_F <= 1e-5), each
+operand's codes and scales against the oracle bit for bit, and the layer's
+outputs against the unquantized products within the format's error (which
+also shows the Hadamard transform cancelling in dW)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+F = None
+L = None
+
+# tokens, in, out: multiples of 16, ragged against the GEMM's 256 x 256 tiles
+T, N_IN, N_OUT = 272, 528, 784
+SEED = 42
+
+
+def setup_module(module):
+    global F, L
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp4_block_scaled_amax_amd as pkg
+    from fp4_block_scaled_amax_amd import linear
+
+    pkg.lib()  # raises if the HIP library is missing: no fallback
+    F, L = pkg, linear
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x_bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def tensors():
+    x = W.activation(T, N_IN, seed=31, n_outlier_cols=2)
+    w = W.weight(N_OUT, N_IN, seed=32)
+    dy = W.gradient(T, N_OUT, seed=33)
+    return x, w, dy
+
+
+def rel_fro(c, ref):
+    return np.linalg.norm(c.astype(np.float64) - ref) / np.linalg.norm(ref)
+
+
+def recon(codes, scales, mode, sg, R, C):
+    return oracle.dequantize_f64_rows(host(codes), host(scales), mode, host(sg)[0], R, C,
+                                      np.arange(R, dtype=np.int64))
+
+
+def test_fprop():
+    x, w, _ = tensors()
+    log("[test_linear] fprop")
+    xd, wd = dev(x), dev(w)
+    wq = L.quantize_weight(wd)
+    y = host(L.fprop(xd, wq))
+    # the operands are the library's own quantizations, equal to the oracle's
+    xq = F.nvfp4_quantize_1d(xd, F.nvfp4_amax(xd), rowwise=True)
+    sg = oracle.global_scale(oracle.amax(x))
+    c, s = oracle.quantize_1d_rows(x, sg)
+    assert np.array_equal(host(xq["codes_row"]), c) and np.array_equal(host(xq["scales_row"]), s)
+    cr, cc, s2 = oracle.quantize_2d(w, oracle.global_scale(oracle.amax(w)))
+    assert np.array_equal(host(wq["scales"]), s2)
+    assert np.array_equal(host(wq["codes_row"]), cr) and np.array_equal(host(wq["codes_col"]), cc)
+    ref = recon(xq["codes_row"], xq["scales_row"], 1, xq["global_scale"], T, N_IN) @ \
+        recon(wq["codes_row"], wq["scales"], 2, wq["global_scale"], N_OUT, N_IN).T
+    assert rel_fro(y, ref) <= 1e-5
+    exact = W.bf16_bits_to_f32(x).astype(np.float64) @ W.bf16_bits_to_f32(w).astype(np.float64).T
+    assert rel_fro(y, exact) < 0.15  # 4-bit operands
+
+
+def test_dgrad_reads_the_weight_column_copy_with_transposed_scales():
+    x, w, dy = tensors()
+    log("[test_linear] dgrad")
+    wd, dyd = dev(w), dev(dy)
+    wq = L.quantize_weight(wd)
+    dx = host(L.dgrad(dyd, wq, SEED))
+    dyq = F.nvfp4_quantize_1d(dyd, F.nvfp4_amax(dyd), rowwise=True, sr=True, seed=SEED)
+    c, s = oracle.quantize_1d_rows(dy, oracle.global_scale(oracle.amax(dy)), True, SEED)
+    assert np.array_equal(host(dyq["codes_row"]), c) and np.array_equal(host(dyq["scales_row"]), s)
+    w_hat = recon(wq["codes_row"], wq["scales"], 2, wq["global_scale"], N_OUT, N_IN)
+    ref = recon(dyq["codes_row"], dyq["scales_row"], 1, dyq["global_scale"], T, N_OUT) @ w_hat
+    assert rel_fro(dx, ref) <= 1e-5
+    # the column copy holds the same codes, transposed (one code per element)
+    lo_hi = lambda a: np.stack([a & 15, a >> 4], -1).reshape(a.shape[0], -1)
+    assert np.array_equal(lo_hi(host(wq["codes_col"])), lo_hi(host(wq["codes_row"])).T)
+    exact = W.bf16_bits_to_f32(dy).astype(np.float64) @ W.bf16_bits_to_f32(w).astype(np.float64)
+    assert rel_fro(dx, exact) < 0.2
+
+
+def test_gemm_transposed_tile_scales_match_dequantized_reference():
+    """NVFP4_SCALE_2D_T on either operand, with K not a multiple of 32."""
+    w = W.weight(N_OUT, 784, seed=34)  # the operand's K is N_OUT = 784 = 24.5 x 32
+    a = W.activation(T, N_OUT, seed=35, n_outlier_cols=1)
+    wd, ad = dev(w), dev(a)
+    wq = F.nvfp4_quantize_2d(wd, F.nvfp4_amax(wd))   # [784][784]: codes_col is W^T
+    aq = F.nvfp4_quantize_1d(ad, F.nvfp4_amax(ad))
+    w_hat_t = recon(wq["codes_row"], wq["scales"], 2, wq["global_scale"], 784, 784).T
+    a_hat = recon(aq["codes_row"], aq["scales_row"], 1, aq["global_scale"], T, N_OUT)
+    c = host(F.nvfp4_gemm(aq["codes_row"], aq["scales_row"], 1, aq["global_scale"],
+                          wq["codes_col"], wq["scales"], F.SCALE_2D_T, wq["global_scale"], T, 784, 784))
+    assert rel_fro(c, a_hat @ w_hat_t.T) <= 1e-5
+    c2 = host(F.nvfp4_gemm(wq["codes_col"], wq["scales"], F.SCALE_2D_T, wq["global_scale"],
+                           aq["codes_row"], aq["scales_row"], 1, aq["global_scale"], 784, T, 784))
+    assert rel_fro(c2, w_hat_t @ a_hat.T) <= 1e-5
+
+
+@pytest.mark.parametrize("x_sr", [False, True])
+def test_wgrad_hadamard_operands_cancel(x_sr):
+    x, _, dy = tensors()
+    log(f"[test_linear] wgrad x_sr={x_sr}")
+    xd, dyd = dev(x), dev(dy)
+    mask = W.rht_sign_mask()
+    dw = host(L.wgrad(dyd, xd, mask, SEED, x_sr=x_sr))
+    dyq, xq = L.wgrad_operands(dyd, xd, mask, SEED, x_sr=x_sr)
+    for t, q, sr in ((dy, dyq, True), (x, xq, x_sr)):
+        sg = oracle.global_scale(oracle.amax_rht(t, mask))
+        c, s = oracle.quantize_1d_cols(t, sg, sr, SEED, True, mask)
+        assert np.array_equal(host(q["codes_col"]), c) and np.array_equal(host(q["scales_col"]), s)
+    ref = recon(dyq["codes_col"], dyq["scales_col"], 1, dyq["global_scale"], N_OUT, T) @ \
+        recon(xq["codes_col"], xq["scales_col"], 1, xq["global_scale"], N_IN, T).T
+    assert rel_fro(dw, ref) <= 1e-5
+    # (H D dY)^T (H D X) / 16 = dY^T X: the transform cancels
+    exact = W.bf16_bits_to_f32(dy).astype(np.float64).T @ W.bf16_bits_to_f32(x).astype(np.float64)
+    assert rel_fro(dw, exact) < 0.2
+
+
+def test_wgrad_with_mismatched_masks_does_not_cancel():
+    """Control for the cancellation check: different sign masks on the two
+    operands leave a product far from dY^T X."""
+    x, _, dy = tensors()
+    xd, dyd = dev(x), dev(dy)
+    mask = W.rht_sign_mask()
+    a_dy = F.nvfp4_amax(dyd, rht=True, rht_mask=mask)
+    dyq = F.nvfp4_quantize_1d(dyd, a_dy, rowwise=False, colwise=True, sr=True, rht=True, rht_mask=mask, seed=SEED)
+    a_x = F.nvfp4_amax(xd, rht=True, rht_mask=mask ^ 0x0F0F)
+    xq = F.nvfp4_quantize_1d(xd, a_x, rowwise=False, colwise=True, rht=True, rht_mask=mask ^ 0x0F0F)
+    dw = host(F.nvfp4_gemm(dyq["codes_col"], dyq["scales_col"], 1, dyq["global_scale"],
+                           xq["codes_col"], xq["scales_col"], 1, xq["global_scale"], N_OUT, N_IN, T))
+    exact = W.bf16_bits_to_f32(dy).astype(np.float64).T @ W.bf16_bits_to_f32(x).astype(np.float64)
+    assert rel_fro(dw, exact) > 0.5
+
+
+def test_training_step_outputs():
+    x, w, dy = tensors()
+    out = L.training_step(dev(x), dev(w), dev(dy), W.rht_sign_mask(), SEED, out_dtype=torch.bfloat16)
+    assert tuple(out["y"].shape) == (T, N_OUT) and out["y"].dtype == torch.bfloat16
+    assert tuple(out["dx"].shape) == (T, N_IN)
+    assert tuple(out["dw"].shape) == (N_OUT, N_IN)
+    for k in ("y", "dx", "dw"):
+        assert torch.isfinite(out[k].float()).all()
