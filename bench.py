@@ -281,7 +281,7 @@ def main():
         y = torch.empty((GR, GC), dtype=torch.float32, device=dev)
         row_hbm("rht16_axis0_gradient", timed(lambda: F.nvfp4_rht16(g, axis=0, rht_mask=mask, out=y)),
                 n_g * 6, [GR, GC])
-        del y, og, g
+        del y, og
 
         log("[bench] generating the 14336x4096 weight")
         w = to_dev(W.weight())
@@ -339,6 +339,29 @@ def main():
                     "decode); context for gemm_fp32_out, not part of this library"}
         log(f"[bench] reference hipBLASLt fp16 GEMM on the same values: {us:.0f} us {tf:.1f} TFLOP/s")
         del da, db, dbt, ch
+
+        # A linear layer's three GEMMs with their quantizations, composed
+        # from the library (fp4_block_scaled_amax_amd.linear): the activation
+        # (8192 tokens x 4096), the weight (14336 x 4096), the gradient
+        # (8192 x 14336).
+        from fp4_block_scaled_amax_amd import linear as L
+        log("[bench] NVFP4 linear layer 8192 tokens, 4096 -> 14336: fprop, dgrad, wgrad")
+        ws_l = F.nvfp4_workspace(dev)
+        wq = L.quantize_weight(w)
+        lin_flop = 3 * 2.0 * R * C * WR
+        parts = (("linear_weight_quantize_2d", lambda: L.quantize_weight(w), None),
+                 ("linear_fprop", lambda: L.fprop(x, wq, ws=ws_l), 2.0 * R * C * WR),
+                 ("linear_dgrad", lambda: L.dgrad(g, wq, W.SR_SEED, ws=ws_l), 2.0 * R * C * WR),
+                 ("linear_wgrad", lambda: L.wgrad(g, x, mask, W.SR_SEED), 2.0 * R * C * WR),
+                 ("linear_layer_step", lambda: L.training_step(x, w, g, mask, W.SR_SEED), lin_flop))
+        for name, fn, fl in parts:
+            us = timed(fn, iters=3)
+            rows[name] = {"shape": {"tokens": R, "in": C, "out": WR}, "us": round(us, 1)}
+            if fl is not None:
+                rows[name].update({"flop": fl, "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1),
+                                   "note": "GEMM flop only; the time includes the operands' quantization"})
+            log(f"[bench] {name}: {us:.0f} us" + (f" {fl / (us * 1e-6) / 1e12:.1f} TFLOP/s" if fl else ""))
+        del wq, g
         del flush
 
     # -------------------------------------------------- CPU oracle baseline
