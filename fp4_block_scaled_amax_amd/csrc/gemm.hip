@@ -20,6 +20,10 @@
 //     one's decode overlaps the other's MFMAs. Stages are double-buffered in
 //     LDS, and the packed codes are fetched two stages ahead into two
 //     alternating register sets.
+//   - A 2D-scaled operand's tile scales (16 row groups x K/16 bytes) are
+//     staged in LDS once per tile with coalesced loads (transposed storage,
+//     NVFP4_SCALE_2D_T, transposed on the way in), so its rows fetch only
+//     codes per stage; K above kLdsScaleK falls back to per-row scale loads.
 //   - The grid is persistent (one workgroup per CU); a tile's output stores
 //     drain while the next tile starts.
 #include <atomic>
@@ -43,6 +47,7 @@ constexpr int kBK = 32;
 constexpr int kRowBytes = kBK * 2 + 16;          // 80: padded LDS row of fp16
 constexpr int kStageBytes = (kBM + kBN) * kRowBytes;  // A rows then B rows
 constexpr int kGroupM = 4;  // tile rows per group of the tile order
+constexpr int kLdsScaleK = 16384;  // largest K whose 2D tile scales a tile stages in LDS
 
 // Byte SEL of `w` (two codes) -> two fp16, times the packed pair `s2`
 // (both halves the block's scale). Both converts are exact: E2M1 and E4M3
@@ -73,10 +78,26 @@ __device__ __attribute__((aligned(16))) const uint8_t kZeroScales[16] = {};
 // kZeroScales).
 template <bool WIDE>
 __device__ __forceinline__ RowStage fetch_stage(const uint8_t* code_row, const uint8_t* scale_row,
-                                                int stage, int64_t sstride, int64_t bstride, int64_t K)
+                                                int stage, int64_t sstride, int64_t bstride, int64_t K,
+                                                const uint8_t* lds_scales)
 {
     RowStage st;
     const int64_t k0 = (int64_t)stage * kBK;
+    if (lds_scales != nullptr) {
+        // 2D tile scales staged in LDS: this row group's K/16 bytes
+        const uint8_t* q = lds_scales + 2 * stage;
+        if (WIDE) {
+            st.codes = load16(code_row + (k0 >> 1));
+            st.scales = *reinterpret_cast<const uint16_t*>(q);
+        } else {
+            const bool has2 = k0 + 16 < K;
+            const uint2 lo = *reinterpret_cast<const uint2*>(code_row + (k0 >> 1));
+            const uint2 hi = has2 ? *reinterpret_cast<const uint2*>(code_row + (k0 >> 1) + 8) : make_uint2(0u, 0u);
+            st.codes = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            st.scales = (uint16_t)(q[0] | (has2 ? (uint32_t)q[1] << 8 : 0u));
+        }
+        return st;
+    }
     const uint8_t* sp = scale_row + (int64_t)stage * sstride;
     const __attribute__((address_space(1))) uint8_t* gp = (const __attribute__((address_space(1))) uint8_t*)sp;
     if (WIDE) {
@@ -151,10 +172,57 @@ __device__ __forceinline__ int gemm_tile_index(int round)
     return round * G + w;
 }
 
+// Stage one operand's 2D tile scales for a tile (its 16 row groups, from
+// group g0 on) into LDS as [group][K/16], group-major; groups past the last
+// (tile_rows of them) read as 0. t: 0..255, this operand's threads.
+// Transposed storage ([K/16][tile_rows]) is transposed on the way in.
+__device__ __forceinline__ void stage_tile_scales(uint8_t* dst, const uint8_t* scales, bool transposed,
+                                                  int64_t g0, int64_t tile_rows, int64_t K, int t)
+{
+    const int64_t kb = K >> 4;  // scale blocks per row
+    if (!transposed) {
+        // The 16 groups' rows are one contiguous span of 16 * kb bytes.
+        const uint8_t* src = scales + g0 * kb;
+        const int64_t avail = (tile_rows - g0) * kb;  // bytes inside the matrix
+        for (int64_t off = (int64_t)t * 16; off < 16 * kb; off += 256 * 16) {
+            if (off + 16 <= avail) {
+                *reinterpret_cast<uint4*>(dst + off) = load16(src + off);
+            } else {
+                for (int i = 0; i < 16; ++i)
+                    dst[off + i] = off + i < avail ? src[off + i] : (uint8_t)0;
+            }
+        }
+    } else {
+        // Row j holds the scales of every group for K block j: 16 bytes of
+        // this tile's groups at j * tile_rows + g0.
+        const int ng = (int)min((int64_t)16, tile_rows - g0);
+        const bool vec = ng == 16 && ((tile_rows & 15) == 0);
+        for (int64_t j = t; j < kb; j += 256) {
+            const uint8_t* src = scales + j * tile_rows + g0;
+            uint8_t b[16];
+            if (vec) {
+                const uint4 v = load16(src);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    b[i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    b[i] = i < ng ? src[i] : (uint8_t)0;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                dst[i * kb + j] = b[i];
+        }
+    }
+}
+
 template <bool BF16_OUT, bool WIDE>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2][kLdsScaleK];  // A, B tile scales
 
     const int64_t K = g.K;
     const int t = threadIdx.x;
@@ -172,6 +240,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     const uint8_t* scales = is_b ? g.b_scales : g.a_scales;
     uint8_t* my_row0 = lds + t * kRowBytes;
     const float scale = (*g.a_sg) * (*g.b_sg);
+    // 2D operands read their tile scales from LDS (K small enough, 16-byte
+    // aligned scale arrays); the flags are uniform over the workgroup.
+    const bool a_stage = g.a_two_d && K <= kLdsScaleK && ((reinterpret_cast<uintptr_t>(g.a_scales) & 15) == 0);
+    const bool b_stage = g.b_two_d && K <= kLdsScaleK && ((reinterpret_cast<uintptr_t>(g.b_scales) & 15) == 0);
+    const bool my_stage = is_b ? b_stage : a_stage;
 
     // Persistent: each workgroup walks tiles; a tile's output stores drain
     // while the next tile's first stages load and decode.
@@ -203,6 +276,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
                                               : scales + (two_d ? (rc >> 4) : rc) * (K >> 4);
         const int64_t bstride = !valid ? 0 : scales_t ? tile_rows : 1;
         const int64_t sstride = 2 * bstride;
+        const int lt = is_b ? t - kBM : t;  // this thread's index among its operand's 256
+        const uint8_t* my_lds_scales = my_stage ? lds_sc[is_b ? 1 : 0] + (lt >> 4) * (K >> 4) : nullptr;
+        if (my_stage)
+            stage_tile_scales(lds_sc[is_b ? 1 : 0], scales, scales_t, (is_b ? n0 : m0) >> 4, tile_rows, K, lt);
+        if (a_stage || b_stage)
+            __syncthreads();
 
         floatx16 acc[2][4];
 #pragma unroll
@@ -211,13 +290,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
             for (int b = 0; b < 4; ++b)
                 acc[a][b] = floatx16{};
 
-        decode_stage_to_lds(fetch_stage<WIDE>(code_row, scale_row, 0, sstride, bstride, K), my_row0);
+        decode_stage_to_lds(fetch_stage<WIDE>(code_row, scale_row, 0, sstride, bstride, K, my_lds_scales), my_row0);
         // Two register sets alternate (stage s+1 in one, s+2 in the other)
         // so a fetch lands in registers the decode has just consumed: no
         // copies of in-flight loads, hence no wait on the newest fetch.
-        RowStage sa = fetch_stage<WIDE>(code_row, scale_row, min(1, last), sstride, bstride, K);
+        RowStage sa = fetch_stage<WIDE>(code_row, scale_row, min(1, last), sstride, bstride, K, my_lds_scales);
         __builtin_amdgcn_sched_barrier(0);  // issue order sa, sb as in the loop
-        RowStage sb = fetch_stage<WIDE>(code_row, scale_row, min(2, last), sstride, bstride, K);
+        RowStage sb = fetch_stage<WIDE>(code_row, scale_row, min(2, last), sstride, bstride, K, my_lds_scales);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
 
@@ -225,14 +304,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         for (; s + 1 < nstages; s += 2) {
             stage_mfma(lds, wm, wn, frow, fk, acc);
             decode_stage_to_lds(sa, my_row0 + kStageBytes);
-            sa = fetch_stage<WIDE>(code_row, scale_row, min(s + 3, last), sstride, bstride, K);
+            sa = fetch_stage<WIDE>(code_row, scale_row, min(s + 3, last), sstride, bstride, K, my_lds_scales);
             __syncthreads();
             // keep each half's work in its half: the scheduler would
             // otherwise hoist the next decode and wait on the newest fetch
             __builtin_amdgcn_sched_barrier(0);
             stage_mfma(lds + kStageBytes, wm, wn, frow, fk, acc);
             decode_stage_to_lds(sb, my_row0);
-            sb = fetch_stage<WIDE>(code_row, scale_row, min(s + 4, last), sstride, bstride, K);
+            sb = fetch_stage<WIDE>(code_row, scale_row, min(s + 4, last), sstride, bstride, K, my_lds_scales);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
         }

@@ -165,3 +165,28 @@ def test_training_step_outputs():
     assert tuple(out["dw"].shape) == (N_OUT, N_IN)
     for k in ("y", "dx", "dw"):
         assert torch.isfinite(out[k].float()).all()
+
+
+@pytest.mark.parametrize("mode", [2, 3])
+def test_gemm_2d_scales_beyond_the_lds_staged_k(mode):
+    """K = 16400 is past the K whose tile scales a workgroup stages in LDS:
+    the per-row scale loads serve 2D and transposed 2D operands."""
+    M, N, K = 48, 64, 16400
+    a = W.activation(M, K, seed=36, n_outlier_cols=1)
+    ad = dev(a)
+    aq = F.nvfp4_quantize_1d(ad, F.nvfp4_amax(ad))
+    a_hat = recon(aq["codes_row"], aq["scales_row"], 1, aq["global_scale"], M, K)
+    if mode == 2:
+        w = W.weight(N, K, seed=37)                     # B = W [N][K], 2D scales [N/16][K/16]
+        wq = F.nvfp4_quantize_2d(dev(w), F.nvfp4_amax(dev(w)), colwise=False)
+        b_codes = wq["codes_row"]
+        b_hat = recon(wq["codes_row"], wq["scales"], 2, wq["global_scale"], N, K)
+    else:
+        w = W.weight(K, N, seed=38)                     # B = W^T: W's column copy, scales [K/16][N/16]
+        wq = F.nvfp4_quantize_2d(dev(w), F.nvfp4_amax(dev(w)), rowwise=False)
+        b_codes = wq["codes_col"]
+        wq_rows = F.nvfp4_quantize_2d(dev(w), F.nvfp4_amax(dev(w)), colwise=False)
+        b_hat = recon(wq_rows["codes_row"], wq_rows["scales"], 2, wq_rows["global_scale"], K, N).T
+    c = host(F.nvfp4_gemm(aq["codes_row"], aq["scales_row"], 1, aq["global_scale"],
+                          b_codes, wq["scales"], mode, wq["global_scale"], M, N, K))
+    assert rel_fro(c, a_hat @ b_hat.T) <= 1e-5
