@@ -74,6 +74,12 @@ def _load():
         "nvfp4_oracle_e2m1_sr_array": (None, [P, P, I64, P]),
         "nvfp4_oracle_e4m3_encode_array": (None, [P, I64, P]),
         "nvfp4_oracle_sr_draw_array": (None, [U64, P, I64, P]),
+        "mxfp4_oracle_e8m0_decode": (ctypes.c_double, [ctypes.c_uint8]),
+        "mxfp4_oracle_scale_byte": (ctypes.c_uint8, [F]),
+        "mxfp4_oracle_quantize_rows": (None, [P, I64, I64, I64, I64, P, P]),
+        "mxfp4_oracle_quantize_cols": (None, [P, I64, I64, ctypes.c_int, ctypes.c_uint16, I64, I64, P, P]),
+        "mxfp4_oracle_dequantize": (None, [P, P, I64, I64, I64, I64, P]),
+        "mxfp4_oracle_dequantize_f64_rows": (None, [P, P, I64, I64, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -290,3 +296,65 @@ def quantize_1d(x: np.ndarray, rowwise=True, colwise=False, sr=False, seed=0, rh
     if colwise:
         out["codes_col"], out["scales_col"] = quantize_1d_cols(x, sg, sr, seed, rht, mask)
     return out
+
+
+# ------------------------------------------ MXFP4, the comparator format
+
+def e8m0_decode(b: int) -> float:
+    return _load().mxfp4_oracle_e8m0_decode(b)
+
+
+def mx_scale_byte(amax: float) -> int:
+    return int(_load().mxfp4_oracle_scale_byte(float(amax)))
+
+
+def mx_quantize_rows(x: np.ndarray, r0: int = 0, r1=None):
+    """MXFP4 rowwise codes [r1-r0][C/2] and E8M0 scales [r1-r0][C/32]."""
+    x = _c(x, np.uint16)
+    R, C = x.shape
+    r1 = R if r1 is None else r1
+    codes = np.empty((r1 - r0, C // 2), np.uint8)
+    scales = np.empty((r1 - r0, C // 32), np.uint8)
+    _load().mxfp4_oracle_quantize_rows(_ptr(x), R, C, r0, r1, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def mx_quantize_cols(x: np.ndarray, rht: bool = False, mask: int = 0, c0: int = 0, c1=None):
+    """MXFP4 columnwise codes [c1-c0][R/2] and scales [c1-c0][R/32]."""
+    x = _c(x, np.uint16)
+    R, C = x.shape
+    c1 = C if c1 is None else c1
+    codes = np.empty((c1 - c0, R // 2), np.uint8)
+    scales = np.empty((c1 - c0, R // 32), np.uint8)
+    _load().mxfp4_oracle_quantize_cols(_ptr(x), R, C, int(bool(rht)), mask, c0, c1, _ptr(codes),
+                                       _ptr(scales))
+    return codes, scales
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray, R: int, C: int, r0: int = 0,
+                  r1=None) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    r1 = R if r1 is None else r1
+    out = np.empty((r1 - r0, C), np.float32)
+    _load().mxfp4_oracle_dequantize(_ptr(codes), _ptr(scales), R, C, r0, r1, _ptr(out))
+    return out
+
+
+def mx_dequantize_f64_rows(codes: np.ndarray, scales: np.ndarray, R: int, C: int,
+                           rows) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    rows = _c(rows, np.int64)
+    out = np.empty((rows.size, C), np.float64)
+    _load().mxfp4_oracle_dequantize_f64_rows(_ptr(codes), _ptr(scales), R, C, _ptr(rows), rows.size,
+                                             _ptr(out))
+    return out
+
+
+def mx_gemm_rows(a_codes, a_scales, b_codes, b_scales, M, N, K, rows):
+    """MXFP4 reference product rows: C[m][n] = sum_k A^[m][k] B^[n][k] in
+    double from the exact reconstructions (TN layout)."""
+    a = mx_dequantize_f64_rows(a_codes, a_scales, M, K, rows)
+    b = mx_dequantize_f64_rows(b_codes, b_scales, N, K, np.arange(N, dtype=np.int64))
+    return a @ b.T

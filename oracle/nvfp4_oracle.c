@@ -23,6 +23,12 @@
  *  [FP4]    "how numbers are stored in computers" (number.rest, FP4 page).
  *  [PHILOX] Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
  *           1, 2, 3", SC'11 -- the Philox4x32-10 counter-based generator.
+ *  [MX]     "NVFP4 Is a Scaling System, Not Just a 4-Bit Number", section
+ *           "Generic FP4, MXFP4, and NVFP4" (MXFP4: E2M1 payload, one E8M0
+ *           power-of-two scale per 32 values, no tensor scale); [ZH] section
+ *           "MXFP4:开放标准,但精度较粗"; the shared-exponent rule of the OCP
+ *           Microscaling Formats (MX) v1.0 specification, which the pages
+ *           name as MXFP4's definition but do not spell out.
  *
  * Readings where the pages are silent (each is also listed in the design doc):
  *  - global scale S_g = amax / (448*6) is the decode multiplier; encoding
@@ -34,7 +40,13 @@
  *  - stochastic rounding rounds up with probability (v-lo)/(hi-lo), drawing
  *    16 bits per element from Philox4x32-10 (one call per 8 elements);
  *  - the Hadamard transform is the natural-order Sylvester H16 applied by
- *    the butterfly in binary32, scaled by 1/4, after a 16-bit sign mask.
+ *    the butterfly in binary32, scaled by 1/4, after a 16-bit sign mask;
+ *  - MXFP4 (the comparator format): the block scale is X = 2^(floor(log2
+ *    amax) - 2), 2 being E2M1's largest exponent, clamped to E8M0's range
+ *    2^-127..2^127 (an all-zero block gets 2^-127); a block holding a NaN
+ *    or an infinity gets the E8M0 NaN byte 0xFF; elements are x / X
+ *    rounded to E2M1 by the same rule as NVFP4's (so a NaN ratio has
+ *    magnitude 0 and the sign bit is kept).
  *
  * Parity status: every function here is pinned by a CPU test
  * (tests/test_oracle_pins.py) except where a function's comment says
@@ -558,4 +570,130 @@ void nvfp4_oracle_sr_draw_array(uint64_t seed, const uint64_t* idx, int64_t n, u
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = nvfp4_oracle_sr_draw(seed, idx[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP4, the comparator format ([MX])                                 */
+/* ------------------------------------------------------------------ */
+
+/* E8M0: eight exponent bits, no sign, no mantissa, bias 127; 0xFF is NaN. */
+double mxfp4_oracle_e8m0_decode(uint8_t b)
+{
+    if (b == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* The block's E8M0 byte from its maximum magnitude: the shared exponent
+ * floor(log2 amax) minus E2M1's largest exponent (2), clamped to the
+ * format's range. log2 of a binary32 value in double is exact enough for
+ * the floor: a binary32 value below a power of two is at least 2^-24 below
+ * it in relative terms, far above double's rounding. amax = 0 gives
+ * -infinity and so the lowest byte; a non-finite amax gives NaN. */
+uint8_t mxfp4_oracle_scale_byte(float amax)
+{
+    if (!isfinite(amax))
+        return 0xFF;
+    double e = floor(log2((double)amax)) - 2.0;
+    if (e < -127.0)
+        e = -127.0;
+    if (e > 127.0)
+        e = 127.0;
+    return (uint8_t)(e + 127.0);
+}
+
+/* One block of 32 values: scale from the block maximum, each element x / X
+ * rounded to E2M1 (round-to-nearest-even, saturating at 6), sign kept.
+ * X is a power of two, so the division is exact wherever the quotient is a
+ * binary32 normal; below that it only decides quotients far under 0.25,
+ * which round to 0 either way. */
+static void mx_quantize_block(const float* x, uint8_t* codes, uint8_t* scale_byte)
+{
+    float b = 0.0f;
+    int bad = 0;
+    for (int k = 0; k < 32; ++k) {
+        float a = fabsf(x[k]);
+        if (!isfinite(a))
+            bad = 1;
+        else if (a > b)
+            b = a;
+    }
+    uint8_t sb = mxfp4_oracle_scale_byte(bad ? NAN : b);
+    float X = (float)mxfp4_oracle_e8m0_decode(sb);
+    for (int k = 0; k < 32; ++k) {
+        float v = fabsf(x[k]) / X;
+        int sign = signbit(x[k]) ? 1 : 0;
+        codes[k] = (uint8_t)((sign << 3) | nvfp4_oracle_e2m1_rne(v));
+    }
+    *scale_byte = sb;
+}
+
+/* Rowwise: blocks of 32 consecutive elements along C. Rows [r0, r1) of the
+ * bf16 [R][C] tensor; codes [r1-r0][C/2], scales [r1-r0][C/32]. */
+void mxfp4_oracle_quantize_rows(const uint16_t* x, int64_t R, int64_t C, int64_t r0, int64_t r1,
+                                uint8_t* codes, uint8_t* scales)
+{
+    (void)R;
+    float blk[32];
+    uint8_t q[32];
+    for (int64_t r = r0; r < r1; ++r)
+        for (int64_t c0 = 0; c0 < C; c0 += 32) {
+            for (int j = 0; j < 32; ++j)
+                blk[j] = bf16_bits_to_float(x[r * C + c0 + j]);
+            mx_quantize_block(blk, q, &scales[(r - r0) * (C / 32) + c0 / 32]);
+            pack_codes(q, 32, &codes[(r - r0) * (C / 2) + c0 / 2]);
+        }
+}
+
+/* Columnwise: blocks of 32 consecutive rows of one column, optionally after
+ * the 16-point Hadamard transform along the rows (each block is two
+ * transformed 16-row segments). Columns [c0, c1); codes [c1-c0][R/2],
+ * scales [c1-c0][R/32]. */
+void mxfp4_oracle_quantize_cols(const uint16_t* x, int64_t R, int64_t C, int rht, uint16_t mask,
+                                int64_t c0, int64_t c1, uint8_t* codes, uint8_t* scales)
+{
+    float seg[16], blk[32];
+    uint8_t q[32];
+    for (int64_t c = c0; c < c1; ++c)
+        for (int64_t rb = 0; rb < R; rb += 32) {
+            for (int half = 0; half < 2; ++half) {
+                for (int j = 0; j < 16; ++j)
+                    seg[j] = bf16_bits_to_float(x[(rb + half * 16 + j) * C + c]);
+                if (rht)
+                    nvfp4_oracle_rht16(seg, mask, &blk[half * 16]);
+                else
+                    memcpy(&blk[half * 16], seg, sizeof seg);
+            }
+            mx_quantize_block(blk, q, &scales[(c - c0) * (R / 32) + rb / 32]);
+            pack_codes(q, 32, &codes[(c - c0) * (R / 2) + rb / 2]);
+        }
+}
+
+/* x = e2m1(code) * X, rows [r0, r1) of [R][C] (scales [R][C/32]), in
+ * binary32. Exact for every byte a bf16 input can produce (at most 252):
+ * two significant bits times a power of two from 2^-128 up. */
+void mxfp4_oracle_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t C,
+                             int64_t r0, int64_t r1, float* out)
+{
+    (void)R;
+    for (int64_t r = r0; r < r1; ++r)
+        for (int64_t c = 0; c < C; ++c) {
+            uint8_t q = nibble(codes, r * C + c);
+            double X = mxfp4_oracle_e8m0_decode(scales[r * (C / 32) + c / 32]);
+            out[(r - r0) * C + c] = (float)(nvfp4_oracle_e2m1_decode(q) * X);
+        }
+}
+
+/* The same reconstruction in double for the listed rows (the GEMM
+ * reference's operands). */
+void mxfp4_oracle_dequantize_f64_rows(const uint8_t* codes, const uint8_t* scales, int64_t R,
+                                      int64_t C, const int64_t* rows, int64_t nrows, double* out)
+{
+    (void)R;
+    for (int64_t t = 0; t < nrows; ++t) {
+        int64_t r = rows[t];
+        for (int64_t c = 0; c < C; ++c)
+            out[t * C + c] = nvfp4_oracle_e2m1_decode(nibble(codes, r * C + c)) *
+                             mxfp4_oracle_e8m0_decode(scales[r * (C / 32) + c / 32]);
+    }
 }
