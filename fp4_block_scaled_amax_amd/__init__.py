@@ -6,7 +6,9 @@ tensors are allocated here with torch.empty) and the current stream. There
 is no fallback: if the library is missing, every call raises.
 
 Names follow the C ABI: nvfp4_amax, nvfp4_quantize_1d, nvfp4_quantize_2d,
-nvfp4_rht16, nvfp4_dequantize, nvfp4_gemm, nvfp4_status_string.
+nvfp4_rht16, nvfp4_dequantize, nvfp4_gemm, nvfp4_status_string, and the
+MXFP4 comparator format's mxfp4_quantize, mxfp4_dequantize, mxfp4_gemm
+(include/mxfp4.h).
 """
 from __future__ import annotations
 
@@ -45,6 +47,9 @@ EXPORTS = (
     "nvfp4_rht16",
     "nvfp4_dequantize",
     "nvfp4_gemm",
+    "mxfp4_quantize",
+    "mxfp4_dequantize",
+    "mxfp4_gemm",
 )
 
 
@@ -84,6 +89,12 @@ def lib():
     L.nvfp4_dequantize.argtypes = [P, P, I, P, I64, I64, P, I, P]
     L.nvfp4_gemm.restype = I
     L.nvfp4_gemm.argtypes = [P, P, I, P, P, P, I, P, P, I, I64, I64, I64, P]
+    L.mxfp4_quantize.restype = I
+    L.mxfp4_quantize.argtypes = [P, I64, I64, U32, U16, P, P, P, P, P]
+    L.mxfp4_dequantize.restype = I
+    L.mxfp4_dequantize.argtypes = [P, P, I64, I64, P, I, P]
+    L.mxfp4_gemm.restype = I
+    L.mxfp4_gemm.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
     _lib = L
     return L
 
@@ -264,4 +275,59 @@ def nvfp4_gemm(a_codes, a_scales, a_scale_mode: int, a_global_scale, b_codes, b_
     _check(lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), a_scale_mode, _ptr(a_global_scale),
                             _ptr(b_codes), _ptr(b_scales), b_scale_mode, _ptr(b_global_scale),
                             _ptr(out), dt, M, N, K, _stream(stream)))
+    return out
+
+
+# ------------------------------------------------- MXFP4 comparator format
+
+def mxfp4_quantize(x, rowwise: bool = True, colwise: bool = False, rht: bool = False,
+                   rht_mask: int = 0, out: dict | None = None, stream=None):
+    """MXFP4 quantization (E8M0 scale per 32 elements) -> dict with codes_row
+    [R][C/2], scales_row [R][C/32], codes_col [C][R/2], scales_col [C][R/32]
+    (the requested layouts). rht: columnwise only, after the axis-0
+    Hadamard transform with sign mask rht_mask."""
+    torch = _torch()
+    _bits16(x)
+    R, C = x.shape
+    out = dict(out or {})
+    dev = x.device
+    if rowwise:
+        out["codes_row"] = _empty((R, C // 2), torch.uint8, dev, out.get("codes_row"))
+        out["scales_row"] = _empty((R, C // 32), torch.uint8, dev, out.get("scales_row"))
+    if colwise:
+        out["codes_col"] = _empty((C, R // 2), torch.uint8, dev, out.get("codes_col"))
+        out["scales_col"] = _empty((C, R // 32), torch.uint8, dev, out.get("scales_col"))
+    flags = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0) | (RHT if rht else 0)
+    _check(lib().mxfp4_quantize(
+        _ptr(x), R, C, flags, rht_mask & 0xFFFF, _ptr(out.get("codes_row")), _ptr(out.get("scales_row")),
+        _ptr(out.get("codes_col")), _ptr(out.get("scales_col")), _stream(stream)))
+    return out
+
+
+def mxfp4_dequantize(codes, scales, rows: int, cols: int, out_dtype=None, out=None, stream=None):
+    """Reconstruct [rows][cols] (float32 or bfloat16) from MXFP4 codes and
+    E8M0 scales [rows][cols/32]."""
+    torch = _torch()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    _dev_tensor(codes, "codes", torch.uint8)
+    _dev_tensor(scales, "scales", torch.uint8)
+    dt = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
+    out = _empty((rows, cols), out_dtype, codes.device, out)
+    _check(lib().mxfp4_dequantize(_ptr(codes), _ptr(scales), rows, cols, _ptr(out), dt, _stream(stream)))
+    return out
+
+
+def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int, out_dtype=None, out=None,
+               stream=None):
+    """C [M][N] = A * B^T from MXFP4 operands (TN) on the block-scaled
+    matrix cores."""
+    torch = _torch()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    for name, t in (("a_codes", a_codes), ("a_scales", a_scales), ("b_codes", b_codes),
+                    ("b_scales", b_scales)):
+        _dev_tensor(t, name, torch.uint8)
+    dt = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
+    out = _empty((M, N), out_dtype, a_codes.device, out)
+    _check(lib().mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), _ptr(out), dt,
+                            M, N, K, _stream(stream)))
     return out

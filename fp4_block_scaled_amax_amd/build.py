@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libnvfp4.so")
 
-SOURCES = ["api.hip", "amax.hip", "quantize.hip", "rht_dequant.hip", "gemm.hip"]
+SOURCES = ["api.hip", "amax.hip", "quantize.hip", "rht_dequant.hip", "gemm.hip", "mx_quantize.hip",
+           "mx_gemm.hip"]
 HEADERS = ["device.h", "kernels.h"]
 
 ARCH = "gfx950"
@@ -62,7 +63,7 @@ def is_stale() -> bool:
     if not os.path.exists(LIB_PATH):
         return True
     t = os.path.getmtime(LIB_PATH)
-    deps = sources() + [os.path.join(CSRC, h) for h in HEADERS] + [os.path.join(ROOT, "include", "nvfp4.h")]
+    deps = sources() + [os.path.join(CSRC, h) for h in HEADERS] + [os.path.join(ROOT, "include", h) for h in ("nvfp4.h", "mxfp4.h")]
     return any(os.path.getmtime(d) > t for d in deps)
 
 

@@ -1,5 +1,6 @@
 // C ABI entry points: argument validation (before any HIP call), then the
 // launch. See include/nvfp4.h for the contract of each call.
+#include "../../include/mxfp4.h"
 #include "../../include/nvfp4.h"
 #include "kernels.h"
 
@@ -220,6 +221,89 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode
     g.N = N;
     g.K = K;
     return status_of(nvfp4::launch_gemm(g, stream));
+}
+
+int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
+                   uint16_t rht_mask, uint8_t* codes_row, uint8_t* scales_row,
+                   uint8_t* codes_col, uint8_t* scales_col, hipStream_t stream)
+{
+    if ((flags & ~(NVFP4_ROWWISE | NVFP4_COLWISE | NVFP4_RHT)) != 0 ||
+        (flags & (NVFP4_ROWWISE | NVFP4_COLWISE)) == 0)
+        return NVFP4_ERR_FLAGS;
+    if ((flags & NVFP4_RHT) && ((flags & NVFP4_ROWWISE) || !(flags & NVFP4_COLWISE)))
+        return NVFP4_ERR_FLAGS;
+    const bool row = (flags & NVFP4_ROWWISE) != 0, col = (flags & NVFP4_COLWISE) != 0;
+    if (x == nullptr || (row && (codes_row == nullptr || scales_row == nullptr)) ||
+        (col && (codes_col == nullptr || scales_col == nullptr)))
+        return NVFP4_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || (row && cols % 32 != 0) || (col && (rows % 32 != 0 || cols % 8 != 0)))
+        return NVFP4_ERR_SHAPE;
+    if (!dims_ok(rows, cols) || rows / 128 >= (1 << 15) || cols / 128 >= (1 << 15) ||
+        (rows / 128 + 1) * (cols / 128 + 1) >= (int64_t)1 << 31)
+        return NVFP4_ERR_SIZE;
+    if (!aligned16(x) || (row && !aligned16(codes_row)) || (col && !aligned16(codes_col)))
+        return NVFP4_ERR_ALIGN;
+    nvfp4::MxQuantizeArgs a{};
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.mask = rht_mask;
+    a.rowwise = row;
+    a.colwise = col;
+    a.rht = (flags & NVFP4_RHT) != 0;
+    a.codes_row = codes_row;
+    a.scales_row = scales_row;
+    a.codes_col = codes_col;
+    a.scales_col = scales_col;
+    return status_of(nvfp4::launch_mx_quantize(a, stream));
+}
+
+int mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                     void* out, int out_dtype, hipStream_t stream)
+{
+    if (codes == nullptr || scales == nullptr || out == nullptr)
+        return NVFP4_ERR_NULL;
+    if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16)
+        return NVFP4_ERR_FLAGS;
+    if (rows <= 0 || cols <= 0 || cols % 32 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!dims_ok(rows, cols))
+        return NVFP4_ERR_SIZE;
+    if (!aligned16(codes) || !aligned16(out))
+        return NVFP4_ERR_ALIGN;
+    return status_of(nvfp4::launch_mx_dequantize(codes, scales, rows, cols, out,
+                                                 out_dtype == NVFP4_BF16, stream));
+}
+
+int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+               const uint8_t* b_scales, void* c, int c_dtype, int64_t M, int64_t N, int64_t K,
+               hipStream_t stream)
+{
+    if (a_codes == nullptr || a_scales == nullptr || b_codes == nullptr || b_scales == nullptr ||
+        c == nullptr)
+        return NVFP4_ERR_NULL;
+    if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16)
+        return NVFP4_ERR_FLAGS;
+    if (M <= 0 || N <= 0 || K <= 0 || K % 32 != 0)
+        return NVFP4_ERR_SHAPE;
+    // 32-bit offsets inside a 256-row panel (256 * K / 2 bytes) and an
+    // output sub-tile (128 * N elements).
+    if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N) || M / 256 >= (1 << 15) ||
+        N / 256 >= (1 << 15) || K > (1 << 24))
+        return NVFP4_ERR_SIZE;
+    if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(c))
+        return NVFP4_ERR_ALIGN;
+    nvfp4::MxGemmArgs g{};
+    g.a_codes = a_codes;
+    g.a_scales = a_scales;
+    g.b_codes = b_codes;
+    g.b_scales = b_scales;
+    g.c = c;
+    g.c_bf16 = c_dtype == NVFP4_BF16;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    return status_of(nvfp4::launch_mx_gemm(g, stream));
 }
 
 }  // extern "C"

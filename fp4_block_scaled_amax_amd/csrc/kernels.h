@@ -52,4 +52,31 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
+// MXFP4 (E8M0 scale per 32 elements): quantize, dequantize, GEMM.
+struct MxQuantizeArgs {
+    const uint16_t* x;
+    int64_t rows, cols;  // rowwise: cols % 32 == 0; colwise: rows % 32 == 0, cols % 8 == 0
+    uint32_t mask;
+    bool rowwise, colwise, rht;
+    uint8_t* codes_row;   // [rows][cols/2]
+    uint8_t* scales_row;  // [rows][cols/32]
+    uint8_t* codes_col;   // [cols][rows/2]
+    uint8_t* scales_col;  // [cols][rows/32]
+};
+hipError_t launch_mx_quantize(const MxQuantizeArgs& a, hipStream_t stream);
+
+hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                                void* out, bool bf16_out, hipStream_t stream);
+
+struct MxGemmArgs {
+    const uint8_t* a_codes;   // [M][K/2]
+    const uint8_t* a_scales;  // [M][K/32]
+    const uint8_t* b_codes;   // [N][K/2]
+    const uint8_t* b_scales;  // [N][K/32]
+    void* c;
+    bool c_bf16;
+    int64_t M, N, K;
+};
+hipError_t launch_mx_gemm(const MxGemmArgs& a, hipStream_t stream);
+
 }  // namespace nvfp4

@@ -1,6 +1,6 @@
 """Host-side checks of the C ABI (no GPU needed).
 
-The library must load, export every entry point include/nvfp4.h declares,
+The library must load, export every entry point include/*.h declares,
 and reject bad arguments with the documented status codes before making any
 HIP call (so these run on a machine without a GPU).
 """
@@ -28,9 +28,13 @@ def L():
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b((?:nvfp4|mxfp4)_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(L):
@@ -104,6 +108,36 @@ def test_rht_dequant_gemm_validation(L):
     assert g(K=24) == -2
     assert g(M=0) == -2
     assert g(c=MIS) == -3
+
+
+def test_mxfp4_validation(L):
+    q = lambda **k: L.mxfp4_quantize(k.get("x", A), k.get("R", 64), k.get("C", 64), k.get("f", F.ROWWISE), 0,
+                                     k.get("cr", A), k.get("sr", A), k.get("cc", A), k.get("sc", A), NULL)
+    assert q(f=0) == -4
+    assert q(f=F.ROWWISE | F.SR) == -4                    # no stochastic rounding
+    assert q(f=F.ROWWISE | F.RHT) == -4                   # the transform is columnwise only
+    assert q(f=F.ROWWISE | F.COLWISE | F.RHT) == -4
+    assert q(x=NULL) == -1
+    assert q(cr=NULL) == -1
+    assert q(f=F.COLWISE, sc=NULL) == -1
+    assert q(f=F.COLWISE, R=48) == -2                     # columnwise: rows a multiple of 32
+    assert q(f=F.COLWISE, C=12) == -2                     # ... and cols of 8
+    assert q(C=16) == -2                                  # rowwise: cols a multiple of 32
+    assert q(x=MIS) == -3
+    assert q(R=1 << 40, C=1 << 40) == -6
+    assert L.mxfp4_dequantize(NULL, A, 32, 32, A, 0, NULL) == -1
+    assert L.mxfp4_dequantize(A, A, 32, 32, A, 2, NULL) == -4
+    assert L.mxfp4_dequantize(A, A, 32, 48, A, 0, NULL) == -2
+    assert L.mxfp4_dequantize(A, A, 32, 32, MIS, 0, NULL) == -3
+    g = lambda **k: L.mxfp4_gemm(k.get("ac", A), A, A, k.get("bs", A), k.get("c", A), k.get("dt", 0),
+                                 k.get("M", 32), k.get("N", 32), k.get("K", 64), NULL)
+    assert g(ac=NULL) == -1
+    assert g(bs=NULL) == -1
+    assert g(dt=5) == -4
+    assert g(K=48) == -2
+    assert g(M=0) == -2
+    assert g(c=MIS) == -3
+    assert g(M=1 << 40, N=1 << 40, K=1 << 20) == -6
 
 
 def test_oracle_is_not_reachable_from_product():
