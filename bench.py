@@ -42,6 +42,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 ALU_NOTE = ("vector-ALU bound, not HBM: Philox (two 32x32->64 multiplies per round, 10 rounds per "
             "8 elements), the 16-point butterfly and the SR encode; the HBM fraction is context")
 F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 (= bf16) matrix peak, TFLOP/s
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 (block-scaled) matrix peak, TFLOP/s
 # Plain vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one op per lane
 # per clock, no packed math).
 VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
@@ -93,6 +94,45 @@ def recorded_traffic():
     if not m_sha or not m_b or m_sha.group(1) != sources_digest(DOMINANT_SOURCES):
         return None
     return float(m_b.group(1))
+
+
+def error_study(F, tensors, mask, dev):
+    """||x - x^||_F / ||x||_F of NVFP4 and MXFP4 (round-to-nearest-even) on
+    each tensor: rowwise, and columnwise after the 16-point Hadamard
+    transform (measured against the transformed tensor); the weight also
+    with NVFP4's 16x16 tiles. Every step runs in the library's kernels; the
+    norms are torch reductions in double precision."""
+    torch = F._torch()
+    out = {}
+
+    def rel(ref, deq):
+        ref = ref.double()
+        return round(float(torch.linalg.vector_norm(deq.double() - ref) / torch.linalg.vector_norm(ref)), 5)
+
+    for name, t in tensors.items():
+        R, C = t.shape
+        ref = t.view(torch.bfloat16).float()
+        e = {}
+        q = F.nvfp4_quantize_1d(t, F.nvfp4_amax(t), rowwise=True)
+        e["nvfp4_1d_rowwise"] = rel(ref, F.nvfp4_dequantize(q["codes_row"], q["scales_row"], 1, q["global_scale"],
+                                                             R, C))
+        m = F.mxfp4_quantize(t)
+        e["mxfp4_rowwise"] = rel(ref, F.mxfp4_dequantize(m["codes_row"], m["scales_row"], R, C))
+        if name == "weight":
+            q2 = F.nvfp4_quantize_2d(t, F.nvfp4_amax(t), colwise=False)
+            e["nvfp4_2d"] = rel(ref, F.nvfp4_dequantize(q2["codes_row"], q2["scales"], 2, q2["global_scale"], R, C))
+        del ref
+        y = F.nvfp4_rht16(t, axis=0, rht_mask=mask).t()
+        q = F.nvfp4_quantize_1d(t, F.nvfp4_amax(t, rht=True, rht_mask=mask), rowwise=False, colwise=True, rht=True,
+                                rht_mask=mask)
+        e["nvfp4_1d_colwise_rht"] = rel(y, F.nvfp4_dequantize(q["codes_col"], q["scales_col"], 1, q["global_scale"],
+                                                               C, R))
+        m = F.mxfp4_quantize(t, rowwise=False, colwise=True, rht=True, rht_mask=mask)
+        e["mxfp4_colwise_rht"] = rel(y, F.mxfp4_dequantize(m["codes_col"], m["scales_col"], C, R))
+        del y, q, m
+        out[name] = e
+        log(f"[bench] error {name}: " + ", ".join(f"{k} {v:.4f}" for k, v in e.items()))
+    return out
 
 
 def main():
@@ -361,7 +401,44 @@ def main():
                 rows[name].update({"flop": fl, "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1),
                                    "note": "GEMM flop only; the time includes the operands' quantization"})
             log(f"[bench] {name}: {us:.0f} us" + (f" {fl / (us * 1e-6) / 1e12:.1f} TFLOP/s" if fl else ""))
-        del wq, g
+        del wq
+
+        # MXFP4, the comparator format (E8M0 scale per 32 elements, no tensor
+        # scale): its quantizer on the same tensors, its GEMM on the gfx950
+        # block-scaled matrix cores with operands from the same values, and
+        # the representation error of both formats.
+        log("[bench] MXFP4 comparator")
+        mo = F.mxfp4_quantize(x, rowwise=True, colwise=True)
+        row_hbm("mx_quantize_rowwise_activation", timed(lambda: F.mxfp4_quantize(x, out=mo)),
+                n_x * (2 + 0.5 + 1 / 32), [R, C])
+        row_hbm("mx_quantize_row_and_col_activation",
+                timed(lambda: F.mxfp4_quantize(x, rowwise=True, colwise=True, out=mo)),
+                n_x * (2 + 2 * (0.5 + 1 / 32)), [R, C])
+        mg = F.mxfp4_quantize(g, rowwise=False, colwise=True, rht=True, rht_mask=mask)
+        row_hbm("mx_quantize_colwise_rht_gradient",
+                timed(lambda: F.mxfp4_quantize(g, rowwise=False, colwise=True, rht=True, rht_mask=mask, out=mg)),
+                n_g * (2 + 0.5 + 1 / 32), [GR, GC])
+        mdq = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+        row_hbm("mx_dequantize_bf16_activation",
+                timed(lambda: F.mxfp4_dequantize(mo["codes_row"], mo["scales_row"], R, C, out_dtype=torch.bfloat16,
+                                                 out=mdq)), n_x * (0.5 + 1 / 32 + 2), [R, C])
+        del mdq
+        ma = F.mxfp4_quantize(A)
+        mb = F.mxfp4_quantize(Bm)
+        for _ in range(50):
+            F.mxfp4_gemm(ma["codes_row"], ma["scales_row"], mb["codes_row"], mb["scales_row"], M, N, K, out=c32)
+        torch.cuda.synchronize()
+        for name, cc, dt in (("mx_gemm_fp32_out", c32, torch.float32), ("mx_gemm_bf16_out", c16, torch.bfloat16)):
+            us = timed(lambda: F.mxfp4_gemm(ma["codes_row"], ma["scales_row"], mb["codes_row"], mb["scales_row"],
+                                            M, N, K, out_dtype=dt, out=cc), iters=max(3, args.row_iters // 2))
+            tf = flop / (us * 1e-6) / 1e12
+            rows[name] = {"shape": [M, N, K], "us": round(us, 1), "flop": flop, "TFLOP/s": round(tf, 1),
+                          "bound": "mfma", "peak": FP4_MFMA_PEAK_TFLOPS,
+                          "frac": round(tf / FP4_MFMA_PEAK_TFLOPS, 4)}
+            log(f"[bench] {name}: {us:.0f} us {tf:.1f} TFLOP/s")
+        del ma, mb, mo, mg
+        rows["error_study"] = error_study(F, {"activation": x, "weight": w, "gradient": g}, mask, dev)
+        del g
         del flush
 
     # -------------------------------------------------- CPU oracle baseline
