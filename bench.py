@@ -321,7 +321,21 @@ def main():
         y = torch.empty((GR, GC), dtype=torch.float32, device=dev)
         row_hbm("rht16_axis0_gradient", timed(lambda: F.nvfp4_rht16(g, axis=0, rht_mask=mask, out=y)),
                 n_g * 6, [GR, GC])
-        del y, og
+        del y
+        # What the fused transform costs: the same calls without it, and both
+        # amaxes of the gradient (plain for dgrad, transformed for wgrad)
+        # from one read.
+        a_g = torch.empty(1, dtype=torch.float32, device=dev)
+        a_both = torch.empty(2, dtype=torch.float32, device=dev)
+        row_hbm("amax_gradient", timed(lambda: F.nvfp4_amax(g, out=a_g)), 2 * n_g, [GR, GC])
+        row_hbm("amax_plain_and_rht_gradient_one_read",
+                timed(lambda: F.nvfp4_amax(g, rht=True, rht_mask=mask, both=True, out=a_both)), 2 * n_g, [GR, GC],
+                note="nvfp4_amax(NVFP4_RHT | NVFP4_AMAX_BOTH): replaces amax_gradient + amax_rht_gradient")
+        row_hbm("quantize_colwise_sr_gradient_no_rht",
+                timed(lambda: F.nvfp4_quantize_1d(g, a_g, rowwise=False, colwise=True, sr=True, seed=W.SR_SEED,
+                                                  out=og)),
+                n_g * 2.5625, [GR, GC], note="the RHT row's call without the transform")
+        del og
 
         log("[bench] generating the 14336x4096 weight")
         w = to_dev(W.weight())
@@ -394,6 +408,14 @@ def main():
                  ("linear_dgrad", lambda: L.dgrad(g, wq, W.SR_SEED, ws=ws_l), 2.0 * R * C * WR),
                  ("linear_wgrad", lambda: L.wgrad(g, x, mask, W.SR_SEED), 2.0 * R * C * WR),
                  ("linear_layer_step", lambda: L.training_step(x, w, g, mask, W.SR_SEED), lin_flop))
+        def unfused_forward():
+            yy = L.fprop(x, wq, ws=ws_l, out_dtype=torch.bfloat16)
+            return F.nvfp4_quantize_1d(yy, F.nvfp4_amax(yy), rowwise=True, colwise=True)
+
+        parts = parts + (
+            ("linear_forward_quantized_output_fused", lambda: L.forward_quantized(x, wq, ws=ws_l),
+             2.0 * R * C * WR),
+            ("linear_forward_quantized_output_unfused", unfused_forward, 2.0 * R * C * WR))
         for name, fn, fl in parts:
             us = timed(fn, iters=3)
             rows[name] = {"shape": {"tokens": R, "in": C, "out": WR}, "us": round(us, 1)}

@@ -22,6 +22,7 @@ COLWISE = 0x2
 SR = 0x4
 RHT = 0x8
 FUSED_AMAX = 0x10
+AMAX_BOTH = 0x20
 WORKSPACE_BYTES = 32832
 SCALE_1D = 1
 SCALE_2D = 2
@@ -47,6 +48,7 @@ EXPORTS = (
     "nvfp4_rht16",
     "nvfp4_dequantize",
     "nvfp4_gemm",
+    "nvfp4_gemm_amax",
     "mxfp4_quantize",
     "mxfp4_dequantize",
     "mxfp4_gemm",
@@ -89,6 +91,8 @@ def lib():
     L.nvfp4_dequantize.argtypes = [P, P, I, P, I64, I64, P, I, P]
     L.nvfp4_gemm.restype = I
     L.nvfp4_gemm.argtypes = [P, P, I, P, P, P, I, P, P, I, I64, I64, I64, P]
+    L.nvfp4_gemm_amax.restype = I
+    L.nvfp4_gemm_amax.argtypes = [P, P, I, P, P, P, I, P, P, I, I64, I64, I64, P, P]
     L.mxfp4_quantize.restype = I
     L.mxfp4_quantize.argtypes = [P, I64, I64, U32, U16, P, P, P, P, P]
     L.mxfp4_dequantize.restype = I
@@ -158,12 +162,15 @@ def _empty(shape, dtype, device, out=None):
 
 # ------------------------------------------------------------------ the API
 
-def nvfp4_amax(x, rht: bool = False, rht_mask: int = 0, out=None, stream=None):
-    """Tensor amax (of the axis-0 Hadamard transform when rht) -> float32 [1]."""
+def nvfp4_amax(x, rht: bool = False, rht_mask: int = 0, out=None, stream=None, both: bool = False):
+    """Tensor amax (of the axis-0 Hadamard transform when rht) -> float32 [1];
+    with both=True (and rht), float32 [2]: the plain amax and the
+    transform's, from one read of x."""
     torch = _torch()
     _bits16(x)
-    out = _empty((1,), torch.float32, x.device, out)
-    _check(lib().nvfp4_amax(_ptr(x), x.shape[0], x.shape[1], RHT if rht else 0, rht_mask & 0xFFFF,
+    out = _empty((2 if both else 1,), torch.float32, x.device, out)
+    flags = (RHT if rht else 0) | (AMAX_BOTH if both else 0)
+    _check(lib().nvfp4_amax(_ptr(x), x.shape[0], x.shape[1], flags, rht_mask & 0xFFFF,
                             _ptr(out), _stream(stream)))
     return out
 
@@ -261,8 +268,11 @@ def nvfp4_dequantize(codes, scales, scale_mode: int, global_scale, rows: int, co
 
 def nvfp4_gemm(a_codes, a_scales, a_scale_mode: int, a_global_scale, b_codes, b_scales,
                b_scale_mode: int, b_global_scale, M: int, N: int, K: int, out_dtype=None, out=None,
-               stream=None):
-    """C [M][N] = A * B^T from packed NVFP4 operands (TN)."""
+               stream=None, out_amax=None):
+    """C [M][N] = A * B^T from packed NVFP4 operands (TN). out_amax: a
+    float32 [1] tensor that also receives max |C| of the stored values
+    (nvfp4_gemm_amax: the amax pass of C's own quantization, fused into the
+    epilogue)."""
     torch = _torch()
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     for name, t in (("a_codes", a_codes), ("a_scales", a_scales), ("b_codes", b_codes),
@@ -272,6 +282,12 @@ def nvfp4_gemm(a_codes, a_scales, a_scale_mode: int, a_global_scale, b_codes, b_
     _dev_tensor(b_global_scale, "b_global_scale", torch.float32)
     dt = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
     out = _empty((M, N), out_dtype, a_codes.device, out)
+    if out_amax is not None:
+        _dev_tensor(out_amax, "out_amax", torch.float32)
+        _check(lib().nvfp4_gemm_amax(_ptr(a_codes), _ptr(a_scales), a_scale_mode, _ptr(a_global_scale),
+                                     _ptr(b_codes), _ptr(b_scales), b_scale_mode, _ptr(b_global_scale),
+                                     _ptr(out), dt, M, N, K, _ptr(out_amax), _stream(stream)))
+        return out
     _check(lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), a_scale_mode, _ptr(a_global_scale),
                             _ptr(b_codes), _ptr(b_scales), b_scale_mode, _ptr(b_global_scale),
                             _ptr(out), dt, M, N, K, _stream(stream)))

@@ -13,7 +13,11 @@ constexpr int kThreads = 256;
 constexpr int kAmaxThreads = 1024;
 constexpr int kAmaxMaxBlocks = 256;
 
-__global__ void amax_reset_kernel(uint32_t* out) { *out = 0u; }
+__global__ void amax_reset_kernel(uint32_t* out, int n)
+{
+    if ((int)threadIdx.x < n)
+        out[threadIdx.x] = 0u;
+}
 
 // Reduce a per-thread maximum (binary32 bits) over the workgroup and merge
 // it into *out.
@@ -77,11 +81,15 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_bf16_kernel(const uint4* __
 // amax of the 16-point Hadamard transform along axis 0. Work item: 16 rows
 // x 8 columns (sixteen 16-byte loads), transformed per column in registers;
 // the sign diagonal is applied to the packed words, the 1/4 to the maximum.
+// BOTH: the same read also gives the plain amax (into out[0]; the
+// transform's into out[1]), half an integer max per element more.
+template <bool BOTH>
 __global__ __launch_bounds__(kThreads) void amax_rht_kernel(const uint16_t* __restrict__ x,
                                                              int64_t rows, int64_t cols,
                                                              uint32_t mask,
                                                              uint32_t* __restrict__ out)
 {
+    uint32_t pm = 0u;  // BOTH: two u16 maxima of |bf16| patterns
     const int64_t groups = cols >> 3;
     const int64_t items = (rows >> 4) * groups;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -93,6 +101,12 @@ __global__ __launch_bounds__(kThreads) void amax_rht_kernel(const uint16_t* __re
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             v[i] = load16(base + i * cols);
+            if (BOTH) {
+                pm = pk_max_u16(pm, v[i].x & 0x7FFF7FFFu);
+                pm = pk_max_u16(pm, v[i].y & 0x7FFF7FFFu);
+                pm = pk_max_u16(pm, v[i].z & 0x7FFF7FFFu);
+                pm = pk_max_u16(pm, v[i].w & 0x7FFF7FFFu);
+            }
             const uint32_t sg = rht_row_sign(mask, i);
             v[i] = make_uint4(v[i].x ^ sg, v[i].y ^ sg, v[i].z ^ sg, v[i].w ^ sg);
         }
@@ -112,7 +126,13 @@ __global__ __launch_bounds__(kThreads) void amax_rht_kernel(const uint16_t* __re
     // (also where it rounds, in the subnormal range), so
     // max |fl(z / 4)| = fl(max |z| / 4), and NaN stays NaN.
     m = __float_as_uint(0.25f * __uint_as_float(m));
-    workgroup_max_to<kThreads>(m, out);
+    if (BOTH) {
+        workgroup_max_to<kThreads>(max(pm & 0xFFFFu, pm >> 16) << 16, out);
+        __syncthreads();  // the partials array is reused
+        workgroup_max_to<kThreads>(m, out + 1);
+    } else {
+        workgroup_max_to<kThreads>(m, out);
+    }
 }
 
 int grid_for(int64_t work_items, int per_block, int max_blocks)
@@ -130,7 +150,7 @@ int grid_for(int64_t work_items, int per_block, int max_blocks)
 hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t stream)
 {
     uint32_t* out = reinterpret_cast<uint32_t*>(amax);
-    hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(1), 0, stream, out);
+    hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(64), 0, stream, out, 1);
     const int64_t nvec = n >> 3;
     constexpr int kUnroll = 16;
     const int grid = grid_for(nvec, kAmaxThreads * kUnroll, kAmaxMaxBlocks);
@@ -140,14 +160,18 @@ hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t st
 }
 
 hipError_t launch_amax_rht(const uint16_t* x, int64_t rows, int64_t cols, uint32_t mask, float* amax,
-                           hipStream_t stream)
+                           bool both, hipStream_t stream)
 {
     uint32_t* out = reinterpret_cast<uint32_t*>(amax);
-    hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(1), 0, stream, out);
+    hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(64), 0, stream, out, both ? 2 : 1);
     const int64_t items = (rows >> 4) * (cols >> 3);
     const int grid = grid_for(items, kThreads, 1024);
-    hipLaunchKernelGGL(amax_rht_kernel, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, mask,
-                       out);
+    if (both)
+        hipLaunchKernelGGL(amax_rht_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, mask,
+                           out);
+    else
+        hipLaunchKernelGGL(amax_rht_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, mask,
+                           out);
     return hipGetLastError();
 }
 

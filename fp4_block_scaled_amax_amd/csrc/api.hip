@@ -51,7 +51,8 @@ int nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags, ui
 {
     if (x == nullptr || amax == nullptr)
         return NVFP4_ERR_NULL;
-    if ((flags & ~NVFP4_RHT) != 0)
+    if ((flags & ~(NVFP4_RHT | NVFP4_AMAX_BOTH)) != 0 ||
+        ((flags & NVFP4_AMAX_BOTH) && !(flags & NVFP4_RHT)))
         return NVFP4_ERR_FLAGS;
     if (rows <= 0 || cols <= 0)
         return NVFP4_ERR_SHAPE;
@@ -62,7 +63,8 @@ int nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags, ui
     if (flags & NVFP4_RHT) {
         if (rows % 16 != 0 || cols % 8 != 0)
             return NVFP4_ERR_SHAPE;
-        return status_of(nvfp4::launch_amax_rht(x, rows, cols, rht_mask, amax, stream));
+        return status_of(nvfp4::launch_amax_rht(x, rows, cols, rht_mask, amax,
+                                                (flags & NVFP4_AMAX_BOTH) != 0, stream));
     }
     return status_of(nvfp4::launch_amax(x, rows * cols, amax, stream));
 }
@@ -185,10 +187,12 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int scale_mode
                                               out_dtype == NVFP4_BF16, stream));
 }
 
-int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode,
-               const float* a_global_scale, const uint8_t* b_codes, const uint8_t* b_scales,
-               int b_scale_mode, const float* b_global_scale, void* c, int c_dtype, int64_t M,
-               int64_t N, int64_t K, hipStream_t stream)
+namespace {
+
+int gemm_common(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode,
+                const float* a_global_scale, const uint8_t* b_codes, const uint8_t* b_scales,
+                int b_scale_mode, const float* b_global_scale, void* c, int c_dtype, int64_t M,
+                int64_t N, int64_t K, float* c_amax, hipStream_t stream)
 {
     if (a_codes == nullptr || a_scales == nullptr || a_global_scale == nullptr ||
         b_codes == nullptr || b_scales == nullptr || b_global_scale == nullptr || c == nullptr)
@@ -220,7 +224,32 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode
     g.M = M;
     g.N = N;
     g.K = K;
+    g.c_amax = c_amax;
     return status_of(nvfp4::launch_gemm(g, stream));
+}
+
+}  // namespace
+
+int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode,
+               const float* a_global_scale, const uint8_t* b_codes, const uint8_t* b_scales,
+               int b_scale_mode, const float* b_global_scale, void* c, int c_dtype, int64_t M,
+               int64_t N, int64_t K, hipStream_t stream)
+{
+    return gemm_common(a_codes, a_scales, a_scale_mode, a_global_scale, b_codes, b_scales, b_scale_mode,
+                       b_global_scale, c, c_dtype, M, N, K, nullptr, stream);
+}
+
+int nvfp4_gemm_amax(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode,
+                    const float* a_global_scale, const uint8_t* b_codes, const uint8_t* b_scales,
+                    int b_scale_mode, const float* b_global_scale, void* c, int c_dtype, int64_t M,
+                    int64_t N, int64_t K, float* c_amax, hipStream_t stream)
+{
+    if (c_amax == nullptr)
+        return NVFP4_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(c_amax) & 3u) != 0)
+        return NVFP4_ERR_ALIGN;
+    return gemm_common(a_codes, a_scales, a_scale_mode, a_global_scale, b_codes, b_scales, b_scale_mode,
+                       b_global_scale, c, c_dtype, M, N, K, c_amax, stream);
 }
 
 int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,

@@ -26,6 +26,9 @@
 //     codes per stage; K above kLdsScaleK falls back to per-row scale loads.
 //   - The grid is persistent (one workgroup per CU); a tile's output stores
 //     drain while the next tile starts.
+//   - Optionally the epilogue also reduces max |C| of the stored values (the
+//     tensor amax a following NVFP4 quantization of C needs), so that
+//     quantization reads C once instead of twice.
 #include <atomic>
 
 #include "device.h"
@@ -218,9 +221,14 @@ __device__ __forceinline__ void stage_tile_scales(uint8_t* dst, const uint8_t* s
     }
 }
 
-template <bool BF16_OUT, bool WIDE>
+// AMAX: also reduce max |C| over the values as stored (bf16 or fp32 bit
+// patterns, an integer maximum like nvfp4_amax's) into *g.c_amax, which the
+// launch has reset: a running maximum per lane over its tiles, one atomic
+// per wave at the end.
+template <bool BF16_OUT, bool WIDE, bool AMAX>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n)
 {
+    uint32_t cmax = 0u;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2][kLdsScaleK];  // A, B tile scales
 
@@ -335,19 +343,30 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
                     const float v = acc[a][b][i] * scale;
                     if (BF16_OUT) {
                         const uint32_t u = __float_as_uint(v);
-                        reinterpret_cast<uint16_t*>(g.c)[r * g.N + col] =
-                            (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                        const uint16_t h = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                        reinterpret_cast<uint16_t*>(g.c)[r * g.N + col] = h;
+                        if (AMAX)
+                            cmax = max(cmax, (uint32_t)(h & 0x7FFFu) << 16);
                     } else {
                         reinterpret_cast<float*>(g.c)[r * g.N + col] = v;
+                        if (AMAX)
+                            cmax = max(cmax, __float_as_uint(v) & 0x7FFFFFFFu);
                     }
                 }
             }
     }
+    if (AMAX) {
+        cmax = wave_max_u32(cmax);
+        if ((threadIdx.x & 63) == 0)
+            atomicMax(reinterpret_cast<uint32_t*>(g.c_amax), cmax);
+    }
 }
+
+__global__ void gemm_amax_reset_kernel(float* a) { *reinterpret_cast<uint32_t*>(a) = 0u; }
 
 // Workgroups resident at once on the current device (one per CU at this
 // tile size), cached per device.
-template <bool BF16_OUT, bool WIDE>
+template <bool BF16_OUT, bool WIDE, bool AMAX>
 int gemm_capacity()
 {
     static std::atomic<int> cache[64];
@@ -359,7 +378,7 @@ int gemm_capacity()
         return c;
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(gemm_kernel<BF16_OUT, WIDE>), kThreads, 0) !=
+            &per_cu, reinterpret_cast<const void*>(gemm_kernel<BF16_OUT, WIDE, AMAX>), kThreads, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
@@ -369,16 +388,25 @@ int gemm_capacity()
     return c;
 }
 
-template <bool BF16_OUT, bool WIDE>
+template <bool BF16_OUT, bool WIDE, bool AMAX>
 hipError_t launch_variant(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t stream)
 {
-    const int cap = gemm_capacity<BF16_OUT, WIDE>();
+    const int cap = gemm_capacity<BF16_OUT, WIDE, AMAX>();
     if (cap <= 0)
         return hipErrorInvalidDevice;
     const int nt = tiles_m * tiles_n;
     const dim3 grid((unsigned)(nt < cap ? nt : cap));
-    hipLaunchKernelGGL((gemm_kernel<BF16_OUT, WIDE>), grid, dim3(kThreads), 0, stream, a, tiles_m, tiles_n);
+    if (AMAX)
+        hipLaunchKernelGGL(gemm_amax_reset_kernel, dim3(1), dim3(1), 0, stream, a.c_amax);
+    hipLaunchKernelGGL((gemm_kernel<BF16_OUT, WIDE, AMAX>), grid, dim3(kThreads), 0, stream, a, tiles_m, tiles_n);
     return hipGetLastError();
+}
+
+template <bool BF16_OUT, bool WIDE>
+hipError_t launch_amax_or_not(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t stream)
+{
+    return a.c_amax != nullptr ? launch_variant<BF16_OUT, WIDE, true>(a, tiles_m, tiles_n, stream)
+                               : launch_variant<BF16_OUT, WIDE, false>(a, tiles_m, tiles_n, stream);
 }
 
 }  // namespace
@@ -389,10 +417,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream)
     const int tiles_n = (int)((a.N + kBN - 1) / kBN);
     const bool wide = (a.K % kBK) == 0;
     if (a.c_bf16)
-        return wide ? launch_variant<true, true>(a, tiles_m, tiles_n, stream)
-                    : launch_variant<true, false>(a, tiles_m, tiles_n, stream);
-    return wide ? launch_variant<false, true>(a, tiles_m, tiles_n, stream)
-                : launch_variant<false, false>(a, tiles_m, tiles_n, stream);
+        return wide ? launch_amax_or_not<true, true>(a, tiles_m, tiles_n, stream)
+                    : launch_amax_or_not<true, false>(a, tiles_m, tiles_n, stream);
+    return wide ? launch_amax_or_not<false, true>(a, tiles_m, tiles_n, stream)
+                : launch_amax_or_not<false, false>(a, tiles_m, tiles_n, stream);
 }
 
 }  // namespace nvfp4

@@ -8,8 +8,9 @@
 namespace nvfp4 {
 
 hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t stream);
+// both: amax[0] = plain amax, amax[1] = amax of the transform (one read).
 hipError_t launch_amax_rht(const uint16_t* x, int64_t rows, int64_t cols, uint32_t mask, float* amax,
-                           hipStream_t stream);
+                           bool both, hipStream_t stream);
 
 struct QuantizeArgs {
     const uint16_t* x;
@@ -49,6 +50,7 @@ struct GemmArgs {
     void* c;
     bool c_bf16;
     int64_t M, N, K;
+    float* c_amax;  // optional: max |C| of the stored values
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 

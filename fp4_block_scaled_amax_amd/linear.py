@@ -17,6 +17,12 @@ a^T b, since H^T H = 16 I and D^2 = I. The weight is quantized once with
 2D tiles, so its two copies hold identical codes and the same tile scales
 (read transposed by the dgrad GEMM, NVFP4_SCALE_2D_T).
 
+Fused passes: dY's two amaxes (plain, for its rowwise dgrad operand, and of
+its Hadamard transform, for its columnwise wgrad operand) come from one read
+of dY (nvfp4_amax with both=True), and the forward can hand its output to
+the next layer already quantized, the output's amax reduced in the GEMM's
+epilogue (forward_quantized) so the quantization reads Y once.
+
 Every step runs in the library's kernels; this module only sequences calls
 on one stream. Shapes: x [tokens][in], w [out][in], dy [tokens][out], all
 bf16 bit patterns (int16/uint16 tensors), every dimension a multiple of 16.
@@ -46,24 +52,55 @@ def fprop(x, wq: dict, ws=None, out_dtype=None, stream=None):
                       tokens, n, k, out_dtype=out_dtype, stream=stream)
 
 
-def dgrad(dy, wq: dict, seed: int, ws=None, out_dtype=None, stream=None):
+def forward_quantized(x, wq: dict, ws=None, stream=None):
+    """Y = X W^T in bf16 and Y's own NVFP4 quantization for the next layer
+    (rowwise and columnwise 1D, round-to-nearest-even): the GEMM's epilogue
+    reduces max |Y| of the stored bf16 values, so the quantization takes it
+    as its amax and reads Y once. Returns (y, yq)."""
+    torch = _torch()
+    tokens, k = x.shape
+    n = wq["codes_row"].shape[0]
+    ws = nvfp4_workspace(x.device) if ws is None else ws
+    xq = nvfp4_quantize_1d(x, ws, rowwise=True, fused_amax=True, stream=stream)
+    y_amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    y = nvfp4_gemm(xq["codes_row"], xq["scales_row"], SCALE_1D, xq["global_scale"],
+                   wq["codes_row"], wq["scales"], SCALE_2D, wq["global_scale"],
+                   tokens, n, k, out_dtype=torch.bfloat16, stream=stream, out_amax=y_amax)
+    yq = nvfp4_quantize_1d(y, y_amax, rowwise=True, colwise=True, stream=stream)
+    return y, yq
+
+
+def gradient_amaxes(dy, rht_mask: int, stream=None):
+    """dY's plain amax and its Hadamard transform's, from one read: float32
+    [2] (views [0:1] and [1:2] serve dgrad and wgrad)."""
+    return nvfp4_amax(dy, rht=True, rht_mask=rht_mask, both=True, stream=stream)
+
+
+def dgrad(dy, wq: dict, seed: int, ws=None, out_dtype=None, stream=None, dy_amax=None):
     """dX [tokens][in] = dY W: dY rowwise 1D stochastic (seed), W's
-    columnwise copy with its tile scales read transposed."""
+    columnwise copy with its tile scales read transposed. dy_amax: dY's
+    amax if already known (gradient_amaxes(...)[0:1]); otherwise the call
+    computes it."""
     tokens, k = dy.shape
     n = wq["codes_col"].shape[0]
-    ws = nvfp4_workspace(dy.device) if ws is None else ws
-    dyq = nvfp4_quantize_1d(dy, ws, rowwise=True, sr=True, seed=seed, fused_amax=True,
-                            stream=stream)
+    if dy_amax is not None:
+        dyq = nvfp4_quantize_1d(dy, dy_amax, rowwise=True, sr=True, seed=seed, stream=stream)
+    else:
+        ws = nvfp4_workspace(dy.device) if ws is None else ws
+        dyq = nvfp4_quantize_1d(dy, ws, rowwise=True, sr=True, seed=seed, fused_amax=True,
+                                stream=stream)
     return nvfp4_gemm(dyq["codes_row"], dyq["scales_row"], SCALE_1D, dyq["global_scale"],
                       wq["codes_col"], wq["scales"], SCALE_2D_T, wq["global_scale"],
                       tokens, n, k, out_dtype=out_dtype, stream=stream)
 
 
-def wgrad_operands(dy, x, rht_mask: int, seed: int, x_sr: bool = False, stream=None):
+def wgrad_operands(dy, x, rht_mask: int, seed: int, x_sr: bool = False, stream=None,
+                   dy_amax_rht=None):
     """The two columnwise operands of dW = dY^T X, blocks along the tokens,
     after the Hadamard transform with the shared sign mask: dY stochastic,
-    X round-to-nearest-even (or stochastic with x_sr)."""
-    a_dy = nvfp4_amax(dy, rht=True, rht_mask=rht_mask, stream=stream)
+    X round-to-nearest-even (or stochastic with x_sr). dy_amax_rht: the
+    transform's amax of dY if already known (gradient_amaxes(...)[1:2])."""
+    a_dy = nvfp4_amax(dy, rht=True, rht_mask=rht_mask, stream=stream) if dy_amax_rht is None else dy_amax_rht
     dyq = nvfp4_quantize_1d(dy, a_dy, rowwise=False, colwise=True, sr=True, rht=True,
                             rht_mask=rht_mask, seed=seed, stream=stream)
     a_x = nvfp4_amax(x, rht=True, rht_mask=rht_mask, stream=stream)
@@ -72,12 +109,13 @@ def wgrad_operands(dy, x, rht_mask: int, seed: int, x_sr: bool = False, stream=N
     return dyq, xq
 
 
-def wgrad(dy, x, rht_mask: int, seed: int, x_sr: bool = False, out_dtype=None, stream=None):
+def wgrad(dy, x, rht_mask: int, seed: int, x_sr: bool = False, out_dtype=None, stream=None,
+          dy_amax_rht=None):
     """dW [out][in] = dY^T X from the Hadamard-transformed columnwise
     operands (the transform cancels in the product)."""
     tokens, n_out = dy.shape
     n_in = x.shape[1]
-    dyq, xq = wgrad_operands(dy, x, rht_mask, seed, x_sr, stream)
+    dyq, xq = wgrad_operands(dy, x, rht_mask, seed, x_sr, stream, dy_amax_rht)
     return nvfp4_gemm(dyq["codes_col"], dyq["scales_col"], SCALE_1D, dyq["global_scale"],
                       xq["codes_col"], xq["scales_col"], SCALE_1D, xq["global_scale"],
                       n_out, n_in, tokens, out_dtype=out_dtype, stream=stream)
@@ -85,12 +123,14 @@ def wgrad(dy, x, rht_mask: int, seed: int, x_sr: bool = False, out_dtype=None, s
 
 def training_step(x, w, dy, rht_mask: int, seed: int, out_dtype=None, stream=None) -> dict:
     """One linear layer's forward and backward GEMMs with their
-    quantizations: {"y", "dx", "dw", "wq"}."""
+    quantizations: {"y", "dx", "dw", "wq"}. dY is read once for both of its
+    amaxes."""
     torch = _torch()
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     wq = quantize_weight(w, stream=stream)
     ws = nvfp4_workspace(x.device)
     y = fprop(x, wq, ws=ws, out_dtype=out_dtype, stream=stream)
-    dx = dgrad(dy, wq, seed, ws=ws, out_dtype=out_dtype, stream=stream)
-    dw = wgrad(dy, x, rht_mask, seed, out_dtype=out_dtype, stream=stream)
+    a_dy = gradient_amaxes(dy, rht_mask, stream=stream)
+    dx = dgrad(dy, wq, seed, out_dtype=out_dtype, stream=stream, dy_amax=a_dy[0:1])
+    dw = wgrad(dy, x, rht_mask, seed, out_dtype=out_dtype, stream=stream, dy_amax_rht=a_dy[1:2])
     return {"y": y, "dx": dx, "dw": dw, "wq": wq}

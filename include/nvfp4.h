@@ -55,6 +55,7 @@ extern "C" {
 #define NVFP4_SR 0x4u      /* stochastic rounding (gradients) instead of RNE */
 #define NVFP4_RHT 0x8u     /* random-sign 16-point Hadamard along rows first */
 #define NVFP4_FUSED_AMAX 0x10u /* compute the amax inside nvfp4_quantize_1d  */
+#define NVFP4_AMAX_BOTH 0x20u  /* nvfp4_amax with NVFP4_RHT: plain amax too    */
 
 /* Size of the workspace nvfp4_quantize_1d takes with NVFP4_FUSED_AMAX. */
 #define NVFP4_WORKSPACE_BYTES 32832
@@ -80,9 +81,13 @@ const char* nvfp4_status_string(int status);
  *   x        bf16 [rows][cols]
  *   flags    0, or NVFP4_RHT: the amax of the Hadamard-transformed tensor
  *            (16-row segments of every column, sign mask `rht_mask`), i.e.
- *            of what nvfp4_rht16(axis 0) would produce.
- *   amax     one float, written with the result (the call first resets it,
- *            stream-ordered, then reduces into it).
+ *            of what nvfp4_rht16(axis 0) would produce; or
+ *            NVFP4_RHT | NVFP4_AMAX_BOTH: both amaxes from one read of x
+ *            (a gradient needs the plain one for its rowwise dgrad operand
+ *            and the transformed one for its columnwise wgrad operand).
+ *   amax     one float (two with NVFP4_AMAX_BOTH: [0] plain, [1] of the
+ *            transform), written with the result (the call first resets
+ *            it, stream-ordered, then reduces into it).
  * Shapes: rows, cols >= 1; with NVFP4_RHT rows must be a multiple of 16.
  * The maximum is an integer maximum of |x| bit patterns, so it is exact and
  * independent of launch geometry; a NaN input yields a NaN amax.
@@ -210,6 +215,22 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode
                const float* a_global_scale, const uint8_t* b_codes, const uint8_t* b_scales,
                int b_scale_mode, const float* b_global_scale, void* c, int c_dtype, int64_t M,
                int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * nvfp4_gemm_amax -- nvfp4_gemm whose epilogue also reduces the tensor amax
+ * of the output it stores: *c_amax = max |C| over the stored values (for a
+ * bf16 C, of the bf16 values; the integer maximum of their magnitude bit
+ * patterns, so it equals what nvfp4_amax of C returns, NaN included). A
+ * following NVFP4 quantization of C (the next layer's input) can take it as
+ * its amax and read C once instead of twice: the amax pass is fused into
+ * the producer's epilogue. The call resets *c_amax (stream-ordered) before
+ * the GEMM. c_amax: one device float, 4-byte aligned. Other arguments,
+ * validation and results as nvfp4_gemm.
+ */
+int nvfp4_gemm_amax(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode,
+                    const float* a_global_scale, const uint8_t* b_codes, const uint8_t* b_scales,
+                    int b_scale_mode, const float* b_global_scale, void* c, int c_dtype, int64_t M,
+                    int64_t N, int64_t K, float* c_amax, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,155 @@
+"""GPU: the fused passes of the linear layer, against the oracle and
+against the unfused calls.
+
+- nvfp4_amax with NVFP4_RHT | NVFP4_AMAX_BOTH: the plain amax and the
+  Hadamard transform's from one read, each bit-equal to the oracle's.
+- nvfp4_gemm_amax: the GEMM's epilogue reduces max |C| of the stored values;
+  C is bit-identical to nvfp4_gemm's and the amax bit-equal to nvfp4_amax of
+  C (bf16) or the host maximum (fp32).
+- linear.forward_quantized: Y's quantization from the epilogue amax equals
+  the oracle's quantization of Y; linear.training_step (one read of dY for
+  both amaxes) equals the calls composed without the fusion, bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+F = None
+L = None
+MASK = W.rht_sign_mask()
+
+
+def setup_module(module):
+    global F, L
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp4_block_scaled_amax_amd as pkg
+    from fp4_block_scaled_amax_amd import linear
+
+    pkg.lib()  # raises if the HIP library is missing: no fallback
+    F, L = pkg, linear
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x_bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def host16(t: torch.Tensor) -> np.ndarray:
+    return host(t.view(torch.int16)).view(np.uint16)
+
+
+def bits(v) -> int:
+    return int(np.float32(v).view(np.uint32))
+
+
+def special(R, C, seed, what):
+    x = W.gradient(R, C, seed=seed)
+    if what == "nan":
+        x[R // 2, C // 3] = 0x7FC0
+    if what == "inf":
+        x[3, 5] = 0xFF80
+    if what == "zeros":
+        x[:] = 0
+    return x
+
+
+AMAX_CASES = {
+    "activation": lambda: W.activation(512, 1024, seed=80, n_outlier_cols=4),
+    "gradient_ragged": lambda: W.gradient(304, 400, seed=81),
+    "gradient_full": lambda: W.gradient(),
+    "nan": lambda: special(64, 96, 82, "nan"),
+    "inf": lambda: special(64, 96, 83, "inf"),
+    "zeros": lambda: special(32, 48, 84, "zeros"),
+}
+
+
+@pytest.mark.parametrize("name", list(AMAX_CASES))
+def test_amax_both_from_one_read(name):
+    x = AMAX_CASES[name]()
+    log(f"[test_amax_both] {name} {x.shape}")
+    a = host(F.nvfp4_amax(dev(x), rht=True, rht_mask=MASK, both=True))
+    plain, rht = oracle.amax(x), oracle.amax_rht(x, MASK)
+    if np.isnan(plain):
+        assert np.isnan(a[0]) and np.isnan(a[1])
+        return
+    assert bits(a[0]) == bits(plain)
+    if np.isnan(rht):
+        assert np.isnan(a[1])
+    else:
+        assert bits(a[1]) == bits(rht)
+    # the single-amax calls agree
+    assert bits(host(F.nvfp4_amax(dev(x)))[0]) == bits(a[0])
+
+
+@pytest.mark.parametrize("M,N,K", [(272, 400, 528), (2064, 8208, 48), (8192, 14336, 4096)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gemm_amax_epilogue(M, N, K, dtype):
+    log(f"[test_gemm_amax] {M}x{N}x{K} {dtype}")
+    a = W.normal_tensor(M, K, seed=85)
+    b = W.normal_tensor(N, K, seed=86, std=0.02)
+    ad, bd = dev(a), dev(b)
+    qa = F.nvfp4_quantize_1d(ad, F.nvfp4_amax(ad))
+    qb = F.nvfp4_quantize_2d(bd, F.nvfp4_amax(bd), colwise=False)
+    args = (qa["codes_row"], qa["scales_row"], 1, qa["global_scale"], qb["codes_row"], qb["scales"], 2,
+            qb["global_scale"], M, N, K)
+    ref = F.nvfp4_gemm(*args, out_dtype=dtype)
+    amax = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")  # reset by the call
+    c = F.nvfp4_gemm(*args, out_dtype=dtype, out_amax=amax)
+    if dtype == torch.bfloat16:
+        cb, rb = host16(c), host16(ref)
+        assert np.array_equal(cb, rb)
+        assert bits(host(amax)[0]) == bits(host(F.nvfp4_amax(c))[0])
+        assert bits(host(amax)[0]) == bits(oracle.amax(cb))
+    else:
+        cf, rf = host(c), host(ref)
+        assert np.array_equal(cf.view(np.uint32), rf.view(np.uint32))
+        assert bits(host(amax)[0]) == int((cf.view(np.uint32) & 0x7FFFFFFF).max())
+
+
+def test_forward_quantized_matches_oracle_quantization_of_y():
+    T, N_IN, N_OUT = 272, 528, 784
+    x = W.activation(T, N_IN, seed=87, n_outlier_cols=2)
+    w = W.weight(N_OUT, N_IN, seed=88)
+    wq = L.quantize_weight(dev(w))
+    y, yq = L.forward_quantized(dev(x), wq)
+    yb = host16(y)
+    # Y itself is the plain fprop's output
+    assert np.array_equal(yb, host16(L.fprop(dev(x), wq, out_dtype=torch.bfloat16)))
+    sg = oracle.global_scale(oracle.amax(yb))
+    assert bits(host(yq["global_scale"])[0]) == bits(sg)
+    c, s = oracle.quantize_1d_rows(yb, sg)
+    assert np.array_equal(host(yq["codes_row"]), c) and np.array_equal(host(yq["scales_row"]), s)
+    c, s = oracle.quantize_1d_cols(yb, sg)
+    assert np.array_equal(host(yq["codes_col"]), c) and np.array_equal(host(yq["scales_col"]), s)
+
+
+def test_training_step_equals_unfused_calls():
+    T, N_IN, N_OUT = 272, 528, 784
+    x = W.activation(T, N_IN, seed=89, n_outlier_cols=2)
+    w = W.weight(N_OUT, N_IN, seed=90)
+    dy = W.gradient(T, N_OUT, seed=91)
+    xd, wd, dyd = dev(x), dev(w), dev(dy)
+    out = L.training_step(xd, wd, dyd, MASK, 42)
+    wq = L.quantize_weight(wd)
+    y = L.fprop(xd, wq)
+    dx = L.dgrad(dyd, wq, 42)                    # its own amax (fused single-pass quantize)
+    dw = L.wgrad(dyd, xd, MASK, 42)              # its own transform amax
+    for k, ref in (("y", y), ("dx", dx), ("dw", dw)):
+        assert np.array_equal(host(out[k]).view(np.uint32), host(ref).view(np.uint32)), k

@@ -60,6 +60,7 @@ def test_amax_validation(L):
     assert L.nvfp4_amax(MIS, 16, 16, 0, 0, A, NULL) == -3
     assert L.nvfp4_amax(A, 24, 16, F.RHT, 0, A, NULL) == -2  # rows not a multiple of 16
     assert L.nvfp4_amax(A, 1 << 40, 1 << 40, 0, 0, A, NULL) == -6
+    assert L.nvfp4_amax(A, 16, 16, F.AMAX_BOTH, 0, A, NULL) == -4  # both amaxes need the transform
 
 
 def q1(L, x=A, rows=64, cols=64, amax=A, flags=F.ROWWISE, cr=A, sr_=A, cc=A, sc=A):
@@ -108,6 +109,9 @@ def test_rht_dequant_gemm_validation(L):
     assert g(K=24) == -2
     assert g(M=0) == -2
     assert g(c=MIS) == -3
+    ga = lambda amax: L.nvfp4_gemm_amax(A, A, 1, A, A, A, 2, A, A, 0, 32, 32, 32, amax, NULL)
+    assert ga(NULL) == -1
+    assert ga(P(4098)) == -3
 
 
 def test_mxfp4_validation(L):
