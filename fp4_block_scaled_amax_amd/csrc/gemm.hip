@@ -7,14 +7,16 @@
 // NVFP4 scale block.
 //
 // Structure (one workgroup = 8 waves, a 256 x 256 tile of C at a time):
-//   - K advances 32 at a time. Each of the 512 threads owns one row (256 of
-//     A, then 256 of B) for the stage: it loads 16 bytes of packed codes and
-//     the two scale bytes and decodes the 32 codes into LDS. Decoding is
+//   - K advances 64 at a time (32 when K is not a multiple of 64). Each of
+//     the 512 threads owns one row (256 of A, then 256 of B) for the stage:
+//     it loads 32 bytes of packed codes and the four scale bytes and decodes
+//     the 64 codes into LDS. Deeper stages halve the barriers per MFMA. Decoding is
 //     three exact hardware steps: both scale bytes to fp16 in one E4M3
 //     convert, two codes to fp16 per E2M1 convert, one packed fp16 multiply
 //     per two codes. Each element is decoded once per workgroup.
-//   - LDS rows are 80 bytes apart (32 fp16 + 16 bytes of padding) so the
-//     16-byte operand reads of 8 consecutive rows hit distinct banks.
+//   - LDS rows are 144 bytes apart (64 fp16 + 16 bytes of padding; 80 for
+//     32-element stages) so the 16-byte operand reads of 8 consecutive rows
+//     hit distinct banks.
 //   - Waves form a 4 x 2 grid; each computes a 64 x 128 sub-tile (2 x 4 MFMA
 //     tiles, 128 fp32 accumulators per lane), so two waves share a SIMD and
 //     one's decode overlaps the other's MFMAs. Stages are double-buffered in
@@ -46,11 +48,19 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 constexpr int kThreads = 512;
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBK = 32;
-constexpr int kRowBytes = kBK * 2 + 16;          // 80: padded LDS row of fp16
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;  // A rows then B rows
 constexpr int kGroupM = 4;  // tile rows per group of the tile order
-constexpr int kLdsScaleK = 16384;  // largest K whose 2D tile scales a tile stages in LDS
+
+// Stage geometry for a stage of KS = 32 or 64 K-elements: padded LDS rows
+// of fp16 (80 or 144 bytes: the 16-byte reads of 8 consecutive rows hit
+// distinct banks), two stages of A rows then B rows, and the largest K whose
+// 2D tile scales a tile stages in LDS next to them (160 KB in all).
+template <int KS>
+struct Geo {
+    static constexpr int kRowBytes = KS * 2 + 16;
+    static constexpr int kStageBytes = (kBM + kBN) * kRowBytes;
+    static constexpr int kLdsScaleK = KS == 32 ? 16384 : 4096;
+    static_assert(2 * kStageBytes + 2 * kLdsScaleK <= 160 * 1024, "LDS");
+};
 
 // Byte SEL of `w` (two codes) -> two fp16, times the packed pair `s2`
 // (both halves the block's scale). Both converts are exact: E2M1 and E4M3
@@ -63,40 +73,59 @@ __device__ __forceinline__ uint32_t decode_pair(uint32_t w, f16x2 s2)
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, g) * s2);
 }
 
-// One row's packed codes for a K stage: 16 bytes (32 codes) and the two
-// scale bytes (low byte: first 16 codes).
+// One row's packed codes for a K stage: KS / 2 bytes and the KS / 16 scale
+// bytes (low byte: first 16 codes).
+template <int KS>
 struct RowStage {
-    uint4 codes;
-    uint16_t scales;
+    uint4 codes[KS / 32];
+    uint32_t scales;
 };
 
 // Scale bytes read by rows past the end of an operand: scale 0 makes every
 // code of such a row decode to zero without touching the loaded values.
 __device__ __attribute__((aligned(16))) const uint8_t kZeroScales[16] = {};
 
-// Fetch stage `stage` of this thread's row: 16 bytes of codes and the two
-// scale bytes, the first at scale_row + stage * sstride and the second
-// bstride after it (bstride 1: adjacent; transposed 2D scales: one scale row
-// apart; sstride = bstride = 0 for rows past the end, which read
+// Fetch stage `stage` of this thread's row: KS / 2 bytes of codes and the
+// KS / 16 scale bytes, the first at scale_row + stage * sstride and the
+// next ones bstride apart (bstride 1: adjacent; transposed 2D scales: one
+// scale row apart; sstride = bstride = 0 for rows past the end, which read
 // kZeroScales).
-template <bool WIDE>
-__device__ __forceinline__ RowStage fetch_stage(const uint8_t* code_row, const uint8_t* scale_row,
-                                                int stage, int64_t sstride, int64_t bstride, int64_t K,
-                                                const uint8_t* lds_scales)
+template <int KS, bool WIDE>
+__device__ __forceinline__ RowStage<KS> fetch_stage(const uint8_t* code_row, const uint8_t* scale_row,
+                                                    int stage, int64_t sstride, int64_t bstride, int64_t K,
+                                                    const uint8_t* lds_scales)
 {
-    RowStage st;
-    const int64_t k0 = (int64_t)stage * kBK;
+    RowStage<KS> st;
+    const int64_t k0 = (int64_t)stage * KS;
+    if constexpr (KS == 64) {
+        // K is a multiple of 64 and the scale arrays are 4-byte aligned.
+        st.codes[0] = load16(code_row + (k0 >> 1));
+        st.codes[1] = load16(code_row + (k0 >> 1) + 16);
+        if (lds_scales != nullptr) {
+            st.scales = *reinterpret_cast<const uint32_t*>(lds_scales + 4 * stage);
+        } else {
+            const uint8_t* sp = scale_row + (int64_t)stage * sstride;
+            const __attribute__((address_space(1))) uint8_t* gp =
+                (const __attribute__((address_space(1))) uint8_t*)sp;
+            if (bstride == 1)  // uniform over the wave (its rows are all A or all B)
+                st.scales = *(const __attribute__((address_space(1))) uint32_t*)sp;
+            else
+                st.scales = (uint32_t)gp[0] | ((uint32_t)gp[bstride] << 8) | ((uint32_t)gp[2 * bstride] << 16) |
+                            ((uint32_t)gp[3 * bstride] << 24);
+        }
+        return st;
+    }
     if (lds_scales != nullptr) {
         // 2D tile scales staged in LDS: this row group's K/16 bytes
         const uint8_t* q = lds_scales + 2 * stage;
         if (WIDE) {
-            st.codes = load16(code_row + (k0 >> 1));
+            st.codes[0] = load16(code_row + (k0 >> 1));
             st.scales = *reinterpret_cast<const uint16_t*>(q);
         } else {
             const bool has2 = k0 + 16 < K;
             const uint2 lo = *reinterpret_cast<const uint2*>(code_row + (k0 >> 1));
             const uint2 hi = has2 ? *reinterpret_cast<const uint2*>(code_row + (k0 >> 1) + 8) : make_uint2(0u, 0u);
-            st.codes = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            st.codes[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
             st.scales = (uint16_t)(q[0] | (has2 ? (uint32_t)q[1] << 8 : 0u));
         }
         return st;
@@ -104,7 +133,7 @@ __device__ __forceinline__ RowStage fetch_stage(const uint8_t* code_row, const u
     const uint8_t* sp = scale_row + (int64_t)stage * sstride;
     const __attribute__((address_space(1))) uint8_t* gp = (const __attribute__((address_space(1))) uint8_t*)sp;
     if (WIDE) {
-        st.codes = load16(code_row + (k0 >> 1));
+        st.codes[0] = load16(code_row + (k0 >> 1));
         if (bstride == 1)  // uniform over the wave (its rows are all A or all B)
             st.scales = *(const __attribute__((address_space(1))) uint16_t*)sp;
         else
@@ -114,47 +143,57 @@ __device__ __forceinline__ RowStage fetch_stage(const uint8_t* code_row, const u
         const bool has2 = k0 + 16 < K;
         const uint2 lo = *reinterpret_cast<const uint2*>(code_row + (k0 >> 1));
         const uint2 hi = has2 ? *reinterpret_cast<const uint2*>(code_row + (k0 >> 1) + 8) : make_uint2(0u, 0u);
-        st.codes = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        st.codes[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         st.scales = (uint16_t)(gp[0] | (has2 ? (uint32_t)gp[bstride] << 8 : 0u));
     }
     return st;
 }
 
-// Decode one row's stage and write its 32 fp16 (64 bytes) to LDS.
-__device__ __forceinline__ void decode_stage_to_lds(const RowStage& st, uint8_t* lds_row)
+// Decode one row's stage and write its KS fp16 (2 KS bytes) to LDS.
+template <int KS>
+__device__ __forceinline__ void decode_stage_to_lds(const RowStage<KS>& st, uint8_t* lds_row)
 {
-    // Both scale bytes to fp16 in one convert.
-    const auto sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.scales, 1.0f, false);
-    const f16x2 s = __builtin_bit_cast(f16x2, sc);
-    const f16x2 s0 = {s[0], s[0]}, s1 = {s[1], s[1]};
-    const uint32_t w[4] = {st.codes.x, st.codes.y, st.codes.z, st.codes.w};
+    // Two scale bytes to fp16 per convert.
+    const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.scales, 1.0f, false));
+    f16x2 sc[4] = {{lo[0], lo[0]}, {lo[1], lo[1]}, {}, {}};
+    if constexpr (KS == 64) {
+        const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.scales, 1.0f, true));
+        sc[2] = f16x2{hi[0], hi[0]};
+        sc[3] = f16x2{hi[1], hi[1]};
+    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const f16x2 sq = q < 2 ? s0 : s1;
-        const u32x4 o = {decode_pair<0>(w[q], sq), decode_pair<1>(w[q], sq), decode_pair<2>(w[q], sq),
-                         decode_pair<3>(w[q], sq)};
-        *reinterpret_cast<u32x4*>(lds_row + 16 * q) = o;
+    for (int h = 0; h < KS / 32; ++h) {
+        const uint32_t w[4] = {st.codes[h].x, st.codes[h].y, st.codes[h].z, st.codes[h].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f16x2 sq = sc[2 * h + (q >> 1)];
+            const u32x4 o = {decode_pair<0>(w[q], sq), decode_pair<1>(w[q], sq), decode_pair<2>(w[q], sq),
+                             decode_pair<3>(w[q], sq)};
+            *reinterpret_cast<u32x4*>(lds_row + 64 * h + 16 * q) = o;
+        }
     }
 }
 
+template <int KS>
 __device__ __forceinline__ f16x8 lds_fragment(const uint8_t* lds, int row, int kbyte)
 {
-    return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(lds + row * kRowBytes + kbyte));
+    return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(lds + row * Geo<KS>::kRowBytes + kbyte));
 }
 
 // The MFMAs of one stage for this wave's 64 x 128 sub-tile.
+template <int KS>
 __device__ __forceinline__ void stage_mfma(const uint8_t* buf, int wm, int wn, int frow, int fk,
                                            floatx16 (&acc)[2][4])
 {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KS / 16; ++ks) {
         f16x8 fa[2], fb[4];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
-            fa[a] = lds_fragment(buf, wm + a * 32 + frow, ks * 32 + fk);
+            fa[a] = lds_fragment<KS>(buf, wm + a * 32 + frow, ks * 32 + fk);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-            fb[b] = lds_fragment(buf + kBM * kRowBytes, wn + b * 32 + frow, ks * 32 + fk);
+            fb[b] = lds_fragment<KS>(buf + kBM * Geo<KS>::kRowBytes, wn + b * 32 + frow, ks * 32 + fk);
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -225,9 +264,12 @@ __device__ __forceinline__ void stage_tile_scales(uint8_t* dst, const uint8_t* s
 // patterns, an integer maximum like nvfp4_amax's) into *g.c_amax, which the
 // launch has reset: a running maximum per lane over its tiles, one atomic
 // per wave at the end.
-template <bool BF16_OUT, bool WIDE, bool AMAX>
+template <bool BF16_OUT, bool WIDE, bool AMAX, int KS>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n)
 {
+    constexpr int kRowBytes = Geo<KS>::kRowBytes;
+    constexpr int kStageBytes = Geo<KS>::kStageBytes;
+    constexpr int kLdsScaleK = Geo<KS>::kLdsScaleK;
     uint32_t cmax = 0u;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2][kLdsScaleK];  // A, B tile scales
@@ -236,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
-    const int nstages = (int)((K + kBK - 1) / kBK);
+    const int nstages = (int)((K + KS - 1) / KS);
     const int last = nstages - 1;
     const int frow = lane & 31;
     const int fk = (lane >> 5) * 16;  // byte offset of the lane's 8 K-elements
@@ -283,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
                                    : scales_t ? scales + (rc >> 4)
                                               : scales + (two_d ? (rc >> 4) : rc) * (K >> 4);
         const int64_t bstride = !valid ? 0 : scales_t ? tile_rows : 1;
-        const int64_t sstride = 2 * bstride;
+        const int64_t sstride = (KS / 16) * bstride;
         const int lt = is_b ? t - kBM : t;  // this thread's index among its operand's 256
         const uint8_t* my_lds_scales = my_stage ? lds_sc[is_b ? 1 : 0] + (lt >> 4) * (K >> 4) : nullptr;
         if (my_stage)
@@ -298,33 +340,33 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
             for (int b = 0; b < 4; ++b)
                 acc[a][b] = floatx16{};
 
-        decode_stage_to_lds(fetch_stage<WIDE>(code_row, scale_row, 0, sstride, bstride, K, my_lds_scales), my_row0);
+        decode_stage_to_lds<KS>(fetch_stage<KS, WIDE>(code_row, scale_row, 0, sstride, bstride, K, my_lds_scales), my_row0);
         // Two register sets alternate (stage s+1 in one, s+2 in the other)
         // so a fetch lands in registers the decode has just consumed: no
         // copies of in-flight loads, hence no wait on the newest fetch.
-        RowStage sa = fetch_stage<WIDE>(code_row, scale_row, min(1, last), sstride, bstride, K, my_lds_scales);
+        RowStage<KS> sa = fetch_stage<KS, WIDE>(code_row, scale_row, min(1, last), sstride, bstride, K, my_lds_scales);
         __builtin_amdgcn_sched_barrier(0);  // issue order sa, sb as in the loop
-        RowStage sb = fetch_stage<WIDE>(code_row, scale_row, min(2, last), sstride, bstride, K, my_lds_scales);
+        RowStage<KS> sb = fetch_stage<KS, WIDE>(code_row, scale_row, min(2, last), sstride, bstride, K, my_lds_scales);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
 
         int s = 0;
         for (; s + 1 < nstages; s += 2) {
-            stage_mfma(lds, wm, wn, frow, fk, acc);
-            decode_stage_to_lds(sa, my_row0 + kStageBytes);
-            sa = fetch_stage<WIDE>(code_row, scale_row, min(s + 3, last), sstride, bstride, K, my_lds_scales);
+            stage_mfma<KS>(lds, wm, wn, frow, fk, acc);
+            decode_stage_to_lds<KS>(sa, my_row0 + kStageBytes);
+            sa = fetch_stage<KS, WIDE>(code_row, scale_row, min(s + 3, last), sstride, bstride, K, my_lds_scales);
             __syncthreads();
             // keep each half's work in its half: the scheduler would
             // otherwise hoist the next decode and wait on the newest fetch
             __builtin_amdgcn_sched_barrier(0);
-            stage_mfma(lds + kStageBytes, wm, wn, frow, fk, acc);
-            decode_stage_to_lds(sb, my_row0);
-            sb = fetch_stage<WIDE>(code_row, scale_row, min(s + 4, last), sstride, bstride, K, my_lds_scales);
+            stage_mfma<KS>(lds + kStageBytes, wm, wn, frow, fk, acc);
+            decode_stage_to_lds<KS>(sb, my_row0);
+            sb = fetch_stage<KS, WIDE>(code_row, scale_row, min(s + 4, last), sstride, bstride, K, my_lds_scales);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
         }
         if (s < nstages) {
-            stage_mfma(lds, wm, wn, frow, fk, acc);
+            stage_mfma<KS>(lds, wm, wn, frow, fk, acc);
             __syncthreads();  // buffer 0 is rewritten by the next tile
         }
 
@@ -366,7 +408,7 @@ __global__ void gemm_amax_reset_kernel(float* a) { *reinterpret_cast<uint32_t*>(
 
 // Workgroups resident at once on the current device (one per CU at this
 // tile size), cached per device.
-template <bool BF16_OUT, bool WIDE, bool AMAX>
+template <bool BF16_OUT, bool WIDE, bool AMAX, int KS>
 int gemm_capacity()
 {
     static std::atomic<int> cache[64];
@@ -378,7 +420,7 @@ int gemm_capacity()
         return c;
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(gemm_kernel<BF16_OUT, WIDE, AMAX>), kThreads, 0) !=
+            &per_cu, reinterpret_cast<const void*>(gemm_kernel<BF16_OUT, WIDE, AMAX, KS>), kThreads, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
@@ -388,25 +430,25 @@ int gemm_capacity()
     return c;
 }
 
-template <bool BF16_OUT, bool WIDE, bool AMAX>
+template <bool BF16_OUT, bool WIDE, bool AMAX, int KS>
 hipError_t launch_variant(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t stream)
 {
-    const int cap = gemm_capacity<BF16_OUT, WIDE, AMAX>();
+    const int cap = gemm_capacity<BF16_OUT, WIDE, AMAX, KS>();
     if (cap <= 0)
         return hipErrorInvalidDevice;
     const int nt = tiles_m * tiles_n;
     const dim3 grid((unsigned)(nt < cap ? nt : cap));
     if (AMAX)
         hipLaunchKernelGGL(gemm_amax_reset_kernel, dim3(1), dim3(1), 0, stream, a.c_amax);
-    hipLaunchKernelGGL((gemm_kernel<BF16_OUT, WIDE, AMAX>), grid, dim3(kThreads), 0, stream, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_kernel<BF16_OUT, WIDE, AMAX, KS>), grid, dim3(kThreads), 0, stream, a, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
-template <bool BF16_OUT, bool WIDE>
+template <bool BF16_OUT, bool WIDE, int KS>
 hipError_t launch_amax_or_not(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t stream)
 {
-    return a.c_amax != nullptr ? launch_variant<BF16_OUT, WIDE, true>(a, tiles_m, tiles_n, stream)
-                               : launch_variant<BF16_OUT, WIDE, false>(a, tiles_m, tiles_n, stream);
+    return a.c_amax != nullptr ? launch_variant<BF16_OUT, WIDE, true, KS>(a, tiles_m, tiles_n, stream)
+                               : launch_variant<BF16_OUT, WIDE, false, KS>(a, tiles_m, tiles_n, stream);
 }
 
 }  // namespace
@@ -415,12 +457,20 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream)
 {
     const int tiles_m = (int)((a.M + kBM - 1) / kBM);
     const int tiles_n = (int)((a.N + kBN - 1) / kBN);
-    const bool wide = (a.K % kBK) == 0;
+    // 64-element stages when K allows them and a stage's four scale bytes of
+    // a row are one aligned load; else 32-element stages (K a multiple of
+    // 32, or an odd multiple of 16).
+    const bool k64 = (a.K % 64) == 0 && ((reinterpret_cast<uintptr_t>(a.a_scales) & 3) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(a.b_scales) & 3) == 0);
+    const bool wide = (a.K % 32) == 0;
+    if (k64)
+        return a.c_bf16 ? launch_amax_or_not<true, true, 64>(a, tiles_m, tiles_n, stream)
+                        : launch_amax_or_not<false, true, 64>(a, tiles_m, tiles_n, stream);
     if (a.c_bf16)
-        return wide ? launch_amax_or_not<true, true>(a, tiles_m, tiles_n, stream)
-                    : launch_amax_or_not<true, false>(a, tiles_m, tiles_n, stream);
-    return wide ? launch_amax_or_not<false, true>(a, tiles_m, tiles_n, stream)
-                : launch_amax_or_not<false, false>(a, tiles_m, tiles_n, stream);
+        return wide ? launch_amax_or_not<true, true, 32>(a, tiles_m, tiles_n, stream)
+                    : launch_amax_or_not<true, false, 32>(a, tiles_m, tiles_n, stream);
+    return wide ? launch_amax_or_not<false, true, 32>(a, tiles_m, tiles_n, stream)
+                : launch_amax_or_not<false, false, 32>(a, tiles_m, tiles_n, stream);
 }
 
 }  // namespace nvfp4

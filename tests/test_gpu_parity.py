@@ -517,6 +517,65 @@ def test_gemm_more_tiles_than_workgroups(a_mode, b_mode):
     assert row_err.max() <= 1e-5
 
 
+def quant_operand(xd, mode):
+    """NVFP4 operand of a TN GEMM: 1D rowwise, 2D tiles, or (mode 3) the
+    column copy of the transposed tensor with its tile scales."""
+    if mode == 1:
+        q = F.nvfp4_quantize_1d(xd, F.nvfp4_amax(xd))
+        return q["codes_row"], q["scales_row"], q["global_scale"]
+    if mode == 2:
+        q = F.nvfp4_quantize_2d(xd, F.nvfp4_amax(xd), colwise=False)
+        return q["codes_row"], q["scales"], q["global_scale"]
+    xt = xd.t().contiguous()                      # the operand is the column copy of x^T
+    q = F.nvfp4_quantize_2d(xt, F.nvfp4_amax(xt), rowwise=False)
+    return q["codes_col"], q["scales"], q["global_scale"]
+
+
+def reference_rows(codes, scales, mode, sg, R, C):
+    """Double reconstruction of an operand in any scale mode: mode 3 is
+    decoded as the 2D rowwise layout of the transposed tensor's tiles."""
+    if mode != 3:
+        return oracle.dequantize_f64_rows(host(codes), host(scales), mode, host(sg)[0], R, C, np.arange(R))
+    # codes_col [R][C/2] of x^T [C][R] with scales [C/16][R/16]: element (r, c) has scale [c/16][r/16]
+    st = np.ascontiguousarray(host(scales).T)      # [R/16][C/16]
+    return oracle.dequantize_f64_rows(host(codes), st, 2, host(sg)[0], R, C, np.arange(R))
+
+
+@pytest.mark.parametrize("K", [1024, 4160])
+@pytest.mark.parametrize("a_mode,b_mode", [(1, 2), (2, 1), (1, 3), (3, 1), (1, 1)])
+def test_gemm_64_element_stages(K, a_mode, b_mode):
+    """K a multiple of 64: 64-element stages, tile scales staged in LDS up to
+    K = 4096 and read per row beyond it; ragged M and N."""
+    M, N = 304, 560
+    log(f"[test_gemm_64] K={K} modes=({a_mode},{b_mode})")
+    a = W.normal_tensor(M, K, seed=46)
+    b = W.normal_tensor(N, K, seed=47, std=0.02)
+    ac, as_, ag = quant_operand(dev(a), a_mode)
+    bc, bs, bg = quant_operand(dev(b), b_mode)
+    c = host(F.nvfp4_gemm(ac, as_, a_mode, ag, bc, bs, b_mode, bg, M, N, K))
+    ref = reference_rows(ac, as_, a_mode, ag, M, K) @ reference_rows(bc, bs, b_mode, bg, N, K).T
+    err = np.linalg.norm(c.astype(np.float64) - ref) / np.linalg.norm(ref)
+    row_err = np.linalg.norm(c.astype(np.float64) - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    assert err <= 1e-5 and row_err.max() <= 1e-5
+
+
+def test_gemm_unaligned_scales_take_the_32_element_stages():
+    """Scale arrays that are not 4-byte aligned (here a view one byte into a
+    buffer) run the 32-element-stage kernel; same product."""
+    M, N, K = 272, 400, 1024
+    a = W.normal_tensor(M, K, seed=48)
+    b = W.normal_tensor(N, K, seed=49, std=0.02)
+    ac, as_, ag = quant_operand(dev(a), 1)
+    bc, bs, bg = quant_operand(dev(b), 2)
+    shifted = torch.empty(as_.numel() + 1, dtype=torch.uint8, device="cuda")[1:].view(as_.shape)
+    shifted.copy_(as_)
+    c_ref = host(F.nvfp4_gemm(ac, as_, 1, ag, bc, bs, 2, bg, M, N, K))
+    c = host(F.nvfp4_gemm(ac, shifted, 1, ag, bc, bs, 2, bg, M, N, K))
+    ref = reference_rows(ac, as_, 1, ag, M, K) @ reference_rows(bc, bs, 2, bg, N, K).T
+    for cc in (c, c_ref):
+        assert np.linalg.norm(cc.astype(np.float64) - ref) / np.linalg.norm(ref) <= 1e-5
+
+
 def test_gemm_bf16_output_is_rounded_fp32():
     a = W.normal_tensor(272, 528, seed=42)
     b = W.normal_tensor(400, 528, seed=43, std=0.02)
