@@ -98,9 +98,9 @@ def recorded_traffic():
 
 def error_study(F, tensors, mask, dev):
     """||x - x^||_F / ||x||_F of NVFP4 and MXFP4 (round-to-nearest-even) on
-    each tensor: rowwise, and columnwise after the 16-point Hadamard
-    transform (measured against the transformed tensor); the weight also
-    with NVFP4's 16x16 tiles. Every step runs in the library's kernels; the
+    each tensor: rowwise, columnwise, and columnwise after the 16-point
+    Hadamard transform (measured against the transformed tensor, whose norm
+    is the tensor's); the weight also with NVFP4's 16x16 tiles. Every step runs in the library's kernels; the
     norms are torch reductions in double precision."""
     torch = F._torch()
     out = {}
@@ -121,7 +121,15 @@ def error_study(F, tensors, mask, dev):
         if name == "weight":
             q2 = F.nvfp4_quantize_2d(t, F.nvfp4_amax(t), colwise=False)
             e["nvfp4_2d"] = rel(ref, F.nvfp4_dequantize(q2["codes_row"], q2["scales"], 2, q2["global_scale"], R, C))
-        del ref
+        # columnwise without the transform (blocks along the same axis as the
+        # transformed layout), against the tensor itself
+        tt = ref.t()
+        q = F.nvfp4_quantize_1d(t, F.nvfp4_amax(t), rowwise=False, colwise=True)
+        e["nvfp4_1d_colwise"] = rel(tt, F.nvfp4_dequantize(q["codes_col"], q["scales_col"], 1, q["global_scale"],
+                                                           C, R))
+        m = F.mxfp4_quantize(t, rowwise=False, colwise=True)
+        e["mxfp4_colwise"] = rel(tt, F.mxfp4_dequantize(m["codes_col"], m["scales_col"], C, R))
+        del ref, tt
         y = F.nvfp4_rht16(t, axis=0, rht_mask=mask).t()
         q = F.nvfp4_quantize_1d(t, F.nvfp4_amax(t, rht=True, rht_mask=mask), rowwise=False, colwise=True, rht=True,
                                 rht_mask=mask)
@@ -132,7 +140,37 @@ def error_study(F, tensors, mask, dev):
         del y, q, m
         out[name] = e
         log(f"[bench] error {name}: " + ", ".join(f"{k} {v:.4f}" for k, v in e.items()))
+    out["wgrad_product"] = wgrad_product_error(F, tensors["gradient"], tensors["activation"], mask)
     return out
+
+
+def wgrad_product_error(F, dy, x, mask):
+    """||dW - dY^T X||_F / ||dY^T X||_F for the weight gradient computed from
+    columnwise operands (blocks along the tokens, round-to-nearest-even):
+    NVFP4 and MXFP4, each without and with the shared Hadamard transform.
+    The reference is a double-precision product on the GPU."""
+    torch = F._torch()
+    T, NO = dy.shape
+    NI = x.shape[1]
+    ref = torch.matmul(dy.view(torch.bfloat16).double().t().contiguous(),
+                       x.view(torch.bfloat16).double().contiguous())
+    nref = torch.linalg.vector_norm(ref)
+    res = {}
+    for rht in (False, True):
+        tag = "rht" if rht else "no_rht"
+        qs = []
+        for t in (dy, x):
+            a = F.nvfp4_amax(t, rht=rht, rht_mask=mask)
+            qs.append(F.nvfp4_quantize_1d(t, a, rowwise=False, colwise=True, rht=rht, rht_mask=mask))
+        c = F.nvfp4_gemm(qs[0]["codes_col"], qs[0]["scales_col"], 1, qs[0]["global_scale"], qs[1]["codes_col"],
+                         qs[1]["scales_col"], 1, qs[1]["global_scale"], NO, NI, T)
+        res[f"nvfp4_{tag}"] = round(float(torch.linalg.vector_norm(c.double() - ref) / nref), 5)
+        ms = [F.mxfp4_quantize(t, rowwise=False, colwise=True, rht=rht, rht_mask=mask) for t in (dy, x)]
+        c = F.mxfp4_gemm(ms[0]["codes_col"], ms[0]["scales_col"], ms[1]["codes_col"], ms[1]["scales_col"], NO, NI, T)
+        res[f"mxfp4_{tag}"] = round(float(torch.linalg.vector_norm(c.double() - ref) / nref), 5)
+        del qs, ms, c
+    log("[bench] error wgrad product dY^T X: " + ", ".join(f"{k} {v:.4f}" for k, v in res.items()))
+    return res
 
 
 def main():
