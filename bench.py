@@ -177,7 +177,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path; see DESIGN.md for how it would shard)",
+              "(there is no multi-GPU path: every block is independent, and only the tensor amax "
+              "would need an all-reduce across GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -30,7 +30,7 @@
  *           Microscaling Formats (MX) v1.0 specification, which the pages
  *           name as MXFP4's definition but do not spell out.
  *
- * Readings where the pages are silent (each is also listed in the design doc):
+ * Readings where the pages are silent:
  *  - global scale S_g = amax / (448*6) is the decode multiplier; encoding
  *    uses reciprocals of it;
  *  - block scale = E4M3 round-to-nearest-even (satfinite) of b / (6*S_g);
