@@ -45,6 +45,7 @@ EXPORTS = (
     "nvfp4_amax",
     "nvfp4_quantize_1d",
     "nvfp4_quantize_2d",
+    "nvfp4_quantize_2d_tscales",
     "nvfp4_rht16",
     "nvfp4_dequantize",
     "nvfp4_gemm",
@@ -85,6 +86,8 @@ def lib():
     L.nvfp4_quantize_1d.argtypes = [P, I64, I64, P, U32, U16, U64, P, P, P, P, P, P]
     L.nvfp4_quantize_2d.restype = I
     L.nvfp4_quantize_2d.argtypes = [P, I64, I64, P, P, P, P, P, P]
+    L.nvfp4_quantize_2d_tscales.restype = I
+    L.nvfp4_quantize_2d_tscales.argtypes = [P, I64, I64, P, P, P, P, P, P, P]
     L.nvfp4_rht16.restype = I
     L.nvfp4_rht16.argtypes = [P, I64, I64, I, U16, P, P]
     L.nvfp4_dequantize.restype = I
@@ -220,9 +223,11 @@ def nvfp4_quantize_1d(x, amax, rowwise: bool = True, colwise: bool = False, sr: 
 
 
 def nvfp4_quantize_2d(x, amax, rowwise: bool = True, colwise: bool = True, out: dict | None = None,
-                      stream=None):
+                      stream=None, transposed_scales: bool = False):
     """2D (16x16 tile) NVFP4 weight quantization -> dict with codes_row,
-    codes_col (requested layouts), scales [R/16][C/16], global_scale."""
+    codes_col (requested layouts), scales [R/16][C/16], global_scale; with
+    transposed_scales also scales_t [C/16][R/16] (nvfp4_quantize_2d_tscales:
+    the scales under which codes_col is a plain 2D-scaled operand)."""
     torch = _torch()
     _bits16(x)
     _dev_tensor(amax, "amax", torch.float32)
@@ -235,6 +240,12 @@ def nvfp4_quantize_2d(x, amax, rowwise: bool = True, colwise: bool = True, out: 
         out["codes_col"] = _empty((C, R // 2), torch.uint8, dev, out.get("codes_col"))
     out["scales"] = _empty((R // 16, C // 16), torch.uint8, dev, out.get("scales"))
     out["global_scale"] = _empty((1,), torch.float32, dev, out.get("global_scale"))
+    if transposed_scales:
+        out["scales_t"] = _empty((C // 16, R // 16), torch.uint8, dev, out.get("scales_t"))
+        _check(lib().nvfp4_quantize_2d_tscales(
+            _ptr(x), R, C, _ptr(amax), _ptr(out.get("codes_row")), _ptr(out.get("codes_col")),
+            _ptr(out["scales"]), _ptr(out["scales_t"]), _ptr(out["global_scale"]), _stream(stream)))
+        return out
     _check(lib().nvfp4_quantize_2d(
         _ptr(x), R, C, _ptr(amax), _ptr(out.get("codes_row")), _ptr(out.get("codes_col")),
         _ptr(out["scales"]), _ptr(out["global_scale"]), _stream(stream)))

@@ -118,9 +118,11 @@ int nvfp4_quantize_1d(const uint16_t* x, int64_t rows, int64_t cols, const float
     return status_of(nvfp4::launch_quantize(a, stream));
 }
 
-int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
-                      uint8_t* codes_row, uint8_t* codes_col, uint8_t* scales,
-                      float* global_scale, hipStream_t stream)
+namespace {
+
+int quantize_2d_common(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                       uint8_t* codes_row, uint8_t* codes_col, uint8_t* scales, uint8_t* scales_t,
+                       float* global_scale, hipStream_t stream)
 {
     if (x == nullptr || amax == nullptr || scales == nullptr ||
         (codes_row == nullptr && codes_col == nullptr))
@@ -143,8 +145,29 @@ int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float
     a.codes_row = codes_row;
     a.scales_row = scales;
     a.codes_col = codes_col;
+    a.scales_col = scales_t;
     a.global_scale = global_scale;
     return status_of(nvfp4::launch_quantize(a, stream));
+}
+
+}  // namespace
+
+int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                      uint8_t* codes_row, uint8_t* codes_col, uint8_t* scales,
+                      float* global_scale, hipStream_t stream)
+{
+    return quantize_2d_common(x, rows, cols, amax, codes_row, codes_col, scales, nullptr, global_scale,
+                              stream);
+}
+
+int nvfp4_quantize_2d_tscales(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                              uint8_t* codes_row, uint8_t* codes_col, uint8_t* scales,
+                              uint8_t* scales_t, float* global_scale, hipStream_t stream)
+{
+    if (scales_t == nullptr)
+        return NVFP4_ERR_NULL;
+    return quantize_2d_common(x, rows, cols, amax, codes_row, codes_col, scales, scales_t, global_scale,
+                              stream);
 }
 
 int nvfp4_rht16(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint16_t rht_mask,

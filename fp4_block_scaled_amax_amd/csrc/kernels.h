@@ -22,7 +22,7 @@ struct QuantizeArgs {
     uint8_t* codes_row;
     uint8_t* scales_row;  // 1D rowwise scales, or the 2D tile scales
     uint8_t* codes_col;
-    uint8_t* scales_col;
+    uint8_t* scales_col;  // 1D columnwise scales; 2D: the transposed tile grid (optional)
     float* global_scale;  // optional
     bool fused_amax;      // compute the amax in the same call (workspace)
     uint32_t* workspace;  // fused_amax: amax bits in word 0, scratch after

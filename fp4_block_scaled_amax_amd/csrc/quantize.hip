@@ -490,8 +490,11 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
         for (int i = 0; i < 16; ++i)
             rr[i] = r;
         fin = finite_bits(r);
-        if (!odd)
+        if (!odd) {
             p.scales_row[(r0 >> 4) * (cols >> 4) + (c0 >> 4)] = (uint8_t)byte;
+            if (p.scales_col != nullptr)  // the transposed tile grid, if asked for
+                p.scales_col[(c0 >> 4) * (p.rows >> 4) + (r0 >> 4)] = (uint8_t)byte;
+        }
     } else {
         // All of the item's scale bytes by the branch-free approximate
         // chain, checked once for the wave; a wave holding any block it

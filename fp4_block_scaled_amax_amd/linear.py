@@ -14,8 +14,10 @@ training recipe"):
 
 The shared mask makes the transform cancel in dW: (H D a)^T (H D b) / 16 =
 a^T b, since H^T H = 16 I and D^2 = I. The weight is quantized once with
-2D tiles, so its two copies hold identical codes and the same tile scales
-(read transposed by the dgrad GEMM, NVFP4_SCALE_2D_T).
+2D tiles, so its two copies hold identical codes and the same tile scales;
+the quantizer also writes the tile grid transposed, under which the
+columnwise copy is a plain 2D-scaled dgrad operand with contiguous scale
+reads (NVFP4_SCALE_2D_T on the untransposed grid gives the same product).
 
 Fused passes: dY's two amaxes (plain, for its rowwise dgrad operand, and of
 its Hadamard transform, for its columnwise wgrad operand) come from one read
@@ -35,9 +37,10 @@ from . import (SCALE_1D, SCALE_2D, SCALE_2D_T, _torch, nvfp4_amax, nvfp4_gemm,
 
 def quantize_weight(w, stream=None) -> dict:
     """W [out][in] -> 2D-tiled NVFP4 in both layouts: codes_row [out][in/2],
-    codes_col [in][out/2], scales [out/16][in/16], global_scale."""
+    codes_col [in][out/2], scales [out/16][in/16], the same grid transposed
+    scales_t [in/16][out/16], global_scale."""
     return nvfp4_quantize_2d(w, nvfp4_amax(w, stream=stream), rowwise=True, colwise=True,
-                             stream=stream)
+                             stream=stream, transposed_scales=True)
 
 
 def fprop(x, wq: dict, ws=None, out_dtype=None, stream=None):
@@ -78,9 +81,10 @@ def gradient_amaxes(dy, rht_mask: int, stream=None):
 
 def dgrad(dy, wq: dict, seed: int, ws=None, out_dtype=None, stream=None, dy_amax=None):
     """dX [tokens][in] = dY W: dY rowwise 1D stochastic (seed), W's
-    columnwise copy with its tile scales read transposed. dy_amax: dY's
-    amax if already known (gradient_amaxes(...)[0:1]); otherwise the call
-    computes it."""
+    columnwise copy with the transposed tile grid (a plain 2D operand; a wq
+    without scales_t is read with NVFP4_SCALE_2D_T, same product). dy_amax:
+    dY's amax if already known (gradient_amaxes(...)[0:1]); otherwise the
+    call computes it."""
     tokens, k = dy.shape
     n = wq["codes_col"].shape[0]
     if dy_amax is not None:
@@ -89,8 +93,12 @@ def dgrad(dy, wq: dict, seed: int, ws=None, out_dtype=None, stream=None, dy_amax
         ws = nvfp4_workspace(dy.device) if ws is None else ws
         dyq = nvfp4_quantize_1d(dy, ws, rowwise=True, sr=True, seed=seed, fused_amax=True,
                                 stream=stream)
+    if "scales_t" in wq:
+        b_scales, b_mode = wq["scales_t"], SCALE_2D
+    else:
+        b_scales, b_mode = wq["scales"], SCALE_2D_T
     return nvfp4_gemm(dyq["codes_row"], dyq["scales_row"], SCALE_1D, dyq["global_scale"],
-                      wq["codes_col"], wq["scales"], SCALE_2D_T, wq["global_scale"],
+                      wq["codes_col"], b_scales, b_mode, wq["global_scale"],
                       tokens, n, k, out_dtype=out_dtype, stream=stream)
 
 

@@ -160,6 +160,21 @@ int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float
                       float* global_scale, hipStream_t stream);
 
 /*
+ * nvfp4_quantize_2d_tscales -- nvfp4_quantize_2d that also writes the tile
+ * scales transposed: scales_t [cols/16][rows/16], scales_t[j][i] =
+ * scales[i][j], in the same pass. With it, the columnwise copy codes_col
+ * ([cols][rows/2]) is a plain 2D-scaled GEMM operand (NVFP4_SCALE_2D with
+ * scales_t) whose scale reads are contiguous per row, where
+ * NVFP4_SCALE_2D_T on the untransposed grid reads bytes a scale row apart
+ * (page "Melatih model dalam 4 bit", section "Empat pengaman": the dgrad
+ * GEMM reads the weight's columnwise copy). scales_t: device, any
+ * alignment, required. Everything else as nvfp4_quantize_2d.
+ */
+int nvfp4_quantize_2d_tscales(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                              uint8_t* codes_row, uint8_t* codes_col, uint8_t* scales,
+                              uint8_t* scales_t, float* global_scale, hipStream_t stream);
+
+/*
  * nvfp4_rht16 -- standalone random-sign 16-point Hadamard transform
  * y = (1/4) * H16 * D * x on every 16-element segment along `axis`
  * (0: 16 consecutive rows of a column; 1: 16 consecutive elements of a

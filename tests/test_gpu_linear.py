@@ -85,7 +85,7 @@ def test_fprop():
     assert rel_fro(y, exact) < 0.15  # 4-bit operands
 
 
-def test_dgrad_reads_the_weight_column_copy_with_transposed_scales():
+def test_dgrad_reads_the_weight_column_copy():
     x, w, dy = tensors()
     log("[test_linear] dgrad")
     wd, dyd = dev(w), dev(dy)
@@ -102,6 +102,25 @@ def test_dgrad_reads_the_weight_column_copy_with_transposed_scales():
     assert np.array_equal(lo_hi(host(wq["codes_col"])), lo_hi(host(wq["codes_row"])).T)
     exact = W.bf16_bits_to_f32(dy).astype(np.float64) @ W.bf16_bits_to_f32(w).astype(np.float64)
     assert rel_fro(dx, exact) < 0.2
+
+
+def test_transposed_tile_grid_and_dgrad_operand_modes_agree():
+    """nvfp4_quantize_2d_tscales writes the oracle's tile scales transposed;
+    the column copy read as a 2D operand with them gives the product of the
+    NVFP4_SCALE_2D_T reading bit for bit (K = 14336 past the LDS-staged K,
+    and a small K that stages)."""
+    for (tok, n_out, n_in) in ((256, 14336, 512), (T, N_OUT, N_IN)):
+        w = W.weight(n_out, n_in, seed=39)
+        dy = W.gradient(tok, n_out, seed=40)
+        wq = L.quantize_weight(dev(w))
+        cr, cc, s2 = oracle.quantize_2d(w, oracle.global_scale(oracle.amax(w)))
+        assert np.array_equal(host(wq["scales"]), s2)
+        assert np.array_equal(host(wq["scales_t"]), np.ascontiguousarray(s2.T))
+        dyq = F.nvfp4_quantize_1d(dev(dy), F.nvfp4_amax(dev(dy)), sr=True, seed=SEED)
+        args = (dyq["codes_row"], dyq["scales_row"], 1, dyq["global_scale"], wq["codes_col"])
+        c2 = host(F.nvfp4_gemm(*args, wq["scales_t"], F.SCALE_2D, wq["global_scale"], tok, n_in, n_out))
+        c3 = host(F.nvfp4_gemm(*args, wq["scales"], F.SCALE_2D_T, wq["global_scale"], tok, n_in, n_out))
+        assert np.array_equal(c2.view(np.uint32), c3.view(np.uint32))
 
 
 def test_gemm_transposed_tile_scales_match_dequantized_reference():
