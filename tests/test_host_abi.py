@@ -89,6 +89,8 @@ def test_quantize_2d_validation(L):
     assert L.nvfp4_quantize_2d(A, 32, 32, A, A, A, NULL, NULL, NULL) == -1
     assert L.nvfp4_quantize_2d(A, 40, 32, A, A, A, A, NULL, NULL) == -2
     assert L.nvfp4_quantize_2d(A, 32, 32, A, MIS, A, A, NULL, NULL) == -3
+    assert L.nvfp4_quantize_2d_tscales(A, 32, 32, A, A, A, A, NULL, NULL, NULL) == -1  # scales_t required
+    assert L.nvfp4_quantize_2d_tscales(A, 40, 32, A, A, A, A, A, NULL, NULL) == -2
 
 
 def test_rht_dequant_gemm_validation(L):
