@@ -13,7 +13,8 @@
 // scale (nearest even, saturating at 6). In a NaN-scale block only the
 // elements' sign bits are kept, so every code has magnitude 0.
 //
-// One workgroup (256 threads) stages a 128 x 128 bf16 tile in LDS with
+// Rowwise alone runs without LDS (mx_quantize_rows_kernel). Otherwise one
+// workgroup (256 threads) stages a 128 x 128 bf16 tile in LDS with
 // full-line loads, then:
 //   - rowwise: a thread takes one 32-element block of a row per pass (two
 //     passes); lanes 0..15 of a wave take 16 consecutive rows, so each
@@ -230,6 +231,53 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(MxQuantizeArgs p,
     }
 }
 
+// Rowwise only, without LDS: a rowwise block is 32 consecutive elements of
+// the row-major tensor (cols is a multiple of 32), so a lane takes 16 bytes
+// (8 elements) and a quad of consecutive lanes holds one block; the block
+// maximum is two DPP steps within the quad. Codes leave as one 32-bit store
+// per lane (256 contiguous bytes per wave), the scale byte from the quad's
+// first lane. U vectors in flight per thread.
+template <int U>
+__global__ __launch_bounds__(kThreads) void mx_quantize_rows_kernel(const uint16_t* __restrict__ x, int64_t nvec,
+                                                                   uint8_t* __restrict__ codes,
+                                                                   uint8_t* __restrict__ scales)
+{
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const bool first = (threadIdx.x & 3) == 0;
+    for (int64_t v0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; v0 < nvec; v0 += U * stride) {
+        uint4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + u * stride;
+            w[u] = load16(x + 8 * (v < nvec ? v : 0));  // a quad is all in or all out
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + u * stride;
+            uint32_t pm = pk_max_u16(pk_max_u16(w[u].x & 0x7FFF7FFFu, w[u].y & 0x7FFF7FFFu),
+                                     pk_max_u16(w[u].z & 0x7FFF7FFFu, w[u].w & 0x7FFF7FFFu));
+            uint32_t m = max(pm & 0xFFFFu, pm >> 16);
+            m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));  // lane ^ 1
+            m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));  // lane ^ 2
+            const uint32_t byte = mx_scale_byte(m << 16);
+            const float inv = mx_inverse_scale(byte);
+            const uint32_t keep = byte == 0xFFu ? 0x80008000u : 0xFFFFFFFFu;
+            const uint32_t q[4] = {w[u].x & keep, w[u].y & keep, w[u].z & keep, w[u].w & keep};
+            float f[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                f[2 * k] = bf16_lo(q[k]) * inv;
+                f[2 * k + 1] = bf16_hi(q[k]) * inv;
+            }
+            if (v < nvec) {
+                reinterpret_cast<uint32_t*>(codes)[v] = mx_word(f);
+                if (first)
+                    scales[v >> 2] = (uint8_t)byte;
+            }
+        }
+    }
+}
+
 // Dequantize: one thread per 32-element block (16 code bytes, one scale).
 // Every reconstruction e2m1 * 2^(byte - 127) is exact in binary32 and in
 // bf16 (two significant bits; 2^-128 and up), so the bf16 output is the
@@ -297,6 +345,16 @@ hipError_t launch_mx_variant(const MxQuantizeArgs& a, hipStream_t stream)
 
 hipError_t launch_mx_quantize(const MxQuantizeArgs& a, hipStream_t stream)
 {
+    if (a.rowwise && !a.colwise && !a.rht) {
+        constexpr int kU = 4;
+        const int64_t nvec = a.rows * (a.cols >> 3);
+        int64_t g = (nvec + kThreads * kU - 1) / (kThreads * kU);
+        if (g > 8192)
+            g = 8192;
+        hipLaunchKernelGGL(mx_quantize_rows_kernel<kU>, dim3((unsigned)g), dim3(kThreads), 0, stream, a.x, nvec,
+                           a.codes_row, a.scales_row);
+        return hipGetLastError();
+    }
     if (a.rowwise && a.colwise)
         return a.rht ? hipErrorInvalidValue : launch_mx_variant<true, true, false>(a, stream);
     if (a.rowwise)
