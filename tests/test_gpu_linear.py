@@ -60,8 +60,20 @@ def rel_fro(c, ref):
 
 
 def recon(codes, scales, mode, sg, R, C):
-    return oracle.dequantize_f64_rows(host(codes), host(scales), mode, host(sg)[0], R, C,
-                                      np.arange(R, dtype=np.int64))
+    """Double reconstruction by the oracle of oracle-made codes and scales."""
+    return oracle.dequantize_f64_rows(codes, scales, mode, sg, R, C, np.arange(R, dtype=np.int64))
+
+
+def to_gpu(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def sg_gpu(sg) -> torch.Tensor:
+    return torch.tensor([float(np.float32(sg))], dtype=torch.float32, device="cuda")
+
+
+def f32_bits(a) -> int:
+    return int(np.float32(a).view(np.uint32))
 
 
 def test_fprop():
@@ -75,11 +87,14 @@ def test_fprop():
     sg = oracle.global_scale(oracle.amax(x))
     c, s = oracle.quantize_1d_rows(x, sg)
     assert np.array_equal(host(xq["codes_row"]), c) and np.array_equal(host(xq["scales_row"]), s)
-    cr, cc, s2 = oracle.quantize_2d(w, oracle.global_scale(oracle.amax(w)))
+    assert f32_bits(host(xq["global_scale"])[0]) == f32_bits(sg)
+    sgw = oracle.global_scale(oracle.amax(w))
+    cr, cc, s2 = oracle.quantize_2d(w, sgw)
     assert np.array_equal(host(wq["scales"]), s2)
     assert np.array_equal(host(wq["codes_row"]), cr) and np.array_equal(host(wq["codes_col"]), cc)
-    ref = recon(xq["codes_row"], xq["scales_row"], 1, xq["global_scale"], T, N_IN) @ \
-        recon(wq["codes_row"], wq["scales"], 2, wq["global_scale"], N_OUT, N_IN).T
+    assert f32_bits(host(wq["global_scale"])[0]) == f32_bits(sgw)
+    # so the reference is the oracle's product of the oracle's operands
+    ref = recon(c, s, 1, sg, T, N_IN) @ recon(cr, s2, 2, sgw, N_OUT, N_IN).T
     assert rel_fro(y, ref) <= 1e-5
     exact = W.bf16_bits_to_f32(x).astype(np.float64) @ W.bf16_bits_to_f32(w).astype(np.float64).T
     assert rel_fro(y, exact) < 0.15  # 4-bit operands
@@ -92,10 +107,15 @@ def test_dgrad_reads_the_weight_column_copy():
     wq = L.quantize_weight(wd)
     dx = host(L.dgrad(dyd, wq, SEED))
     dyq = F.nvfp4_quantize_1d(dyd, F.nvfp4_amax(dyd), rowwise=True, sr=True, seed=SEED)
-    c, s = oracle.quantize_1d_rows(dy, oracle.global_scale(oracle.amax(dy)), True, SEED)
+    sg = oracle.global_scale(oracle.amax(dy))
+    c, s = oracle.quantize_1d_rows(dy, sg, True, SEED)
     assert np.array_equal(host(dyq["codes_row"]), c) and np.array_equal(host(dyq["scales_row"]), s)
-    w_hat = recon(wq["codes_row"], wq["scales"], 2, wq["global_scale"], N_OUT, N_IN)
-    ref = recon(dyq["codes_row"], dyq["scales_row"], 1, dyq["global_scale"], T, N_OUT) @ w_hat
+    assert f32_bits(host(dyq["global_scale"])[0]) == f32_bits(sg)
+    sgw = oracle.global_scale(oracle.amax(w))
+    cr, _, s2 = oracle.quantize_2d(w, sgw)
+    assert np.array_equal(host(wq["codes_row"]), cr) and np.array_equal(host(wq["scales"]), s2)
+    assert f32_bits(host(wq["global_scale"])[0]) == f32_bits(sgw)
+    ref = recon(c, s, 1, sg, T, N_OUT) @ recon(cr, s2, 2, sgw, N_OUT, N_IN)
     assert rel_fro(dx, ref) <= 1e-5
     # the column copy holds the same codes, transposed (one code per element)
     lo_hi = lambda a: np.stack([a & 15, a >> 4], -1).reshape(a.shape[0], -1)
@@ -127,16 +147,17 @@ def test_gemm_transposed_tile_scales_match_dequantized_reference():
     """NVFP4_SCALE_2D_T on either operand, with K not a multiple of 32."""
     w = W.weight(N_OUT, 784, seed=34)  # the operand's K is N_OUT = 784 = 24.5 x 32
     a = W.activation(T, N_OUT, seed=35, n_outlier_cols=1)
-    wd, ad = dev(w), dev(a)
-    wq = F.nvfp4_quantize_2d(wd, F.nvfp4_amax(wd))   # [784][784]: codes_col is W^T
-    aq = F.nvfp4_quantize_1d(ad, F.nvfp4_amax(ad))
-    w_hat_t = recon(wq["codes_row"], wq["scales"], 2, wq["global_scale"], 784, 784).T
-    a_hat = recon(aq["codes_row"], aq["scales_row"], 1, aq["global_scale"], T, N_OUT)
-    c = host(F.nvfp4_gemm(aq["codes_row"], aq["scales_row"], 1, aq["global_scale"],
-                          wq["codes_col"], wq["scales"], F.SCALE_2D_T, wq["global_scale"], T, 784, 784))
+    sgw = oracle.global_scale(oracle.amax(w))
+    wr, wc, ws = oracle.quantize_2d(w, sgw)         # [784][784]: the column copy is W^T
+    sga = oracle.global_scale(oracle.amax(a))
+    ac, as_ = oracle.quantize_1d_rows(a, sga)
+    w_hat_t = recon(wr, ws, 2, sgw, 784, 784).T
+    a_hat = recon(ac, as_, 1, sga, T, N_OUT)
+    wcd, wsd, wgd = to_gpu(wc), to_gpu(ws), sg_gpu(sgw)
+    acd, asd, agd = to_gpu(ac), to_gpu(as_), sg_gpu(sga)
+    c = host(F.nvfp4_gemm(acd, asd, 1, agd, wcd, wsd, F.SCALE_2D_T, wgd, T, 784, 784))
     assert rel_fro(c, a_hat @ w_hat_t.T) <= 1e-5
-    c2 = host(F.nvfp4_gemm(wq["codes_col"], wq["scales"], F.SCALE_2D_T, wq["global_scale"],
-                           aq["codes_row"], aq["scales_row"], 1, aq["global_scale"], 784, T, 784))
+    c2 = host(F.nvfp4_gemm(wcd, wsd, F.SCALE_2D_T, wgd, acd, asd, 1, agd, 784, T, 784))
     assert rel_fro(c2, w_hat_t @ a_hat.T) <= 1e-5
 
 
@@ -148,12 +169,14 @@ def test_wgrad_hadamard_operands_cancel(x_sr):
     mask = W.rht_sign_mask()
     dw = host(L.wgrad(dyd, xd, mask, SEED, x_sr=x_sr))
     dyq, xq = L.wgrad_operands(dyd, xd, mask, SEED, x_sr=x_sr)
+    hats = []
     for t, q, sr in ((dy, dyq, True), (x, xq, x_sr)):
         sg = oracle.global_scale(oracle.amax_rht(t, mask))
         c, s = oracle.quantize_1d_cols(t, sg, sr, SEED, True, mask)
         assert np.array_equal(host(q["codes_col"]), c) and np.array_equal(host(q["scales_col"]), s)
-    ref = recon(dyq["codes_col"], dyq["scales_col"], 1, dyq["global_scale"], N_OUT, T) @ \
-        recon(xq["codes_col"], xq["scales_col"], 1, xq["global_scale"], N_IN, T).T
+        assert f32_bits(host(q["global_scale"])[0]) == f32_bits(sg)
+        hats.append(recon(c, s, 1, sg, t.shape[1], T))
+    ref = hats[0] @ hats[1].T
     assert rel_fro(dw, ref) <= 1e-5
     # (H D dY)^T (H D X) / 16 = dY^T X: the transform cancels
     exact = W.bf16_bits_to_f32(dy).astype(np.float64).T @ W.bf16_bits_to_f32(x).astype(np.float64)
@@ -192,20 +215,19 @@ def test_gemm_2d_scales_beyond_the_lds_staged_k(mode):
     the per-row scale loads serve 2D and transposed 2D operands."""
     M, N, K = 48, 64, 16400
     a = W.activation(M, K, seed=36, n_outlier_cols=1)
-    ad = dev(a)
-    aq = F.nvfp4_quantize_1d(ad, F.nvfp4_amax(ad))
-    a_hat = recon(aq["codes_row"], aq["scales_row"], 1, aq["global_scale"], M, K)
+    sga = oracle.global_scale(oracle.amax(a))
+    ac, as_ = oracle.quantize_1d_rows(a, sga)
+    a_hat = recon(ac, as_, 1, sga, M, K)
     if mode == 2:
         w = W.weight(N, K, seed=37)                     # B = W [N][K], 2D scales [N/16][K/16]
-        wq = F.nvfp4_quantize_2d(dev(w), F.nvfp4_amax(dev(w)), colwise=False)
-        b_codes = wq["codes_row"]
-        b_hat = recon(wq["codes_row"], wq["scales"], 2, wq["global_scale"], N, K)
+        sgw = oracle.global_scale(oracle.amax(w))
+        b_codes, _, b_scales = oracle.quantize_2d(w, sgw)
+        b_hat = recon(b_codes, b_scales, 2, sgw, N, K)
     else:
         w = W.weight(K, N, seed=38)                     # B = W^T: W's column copy, scales [K/16][N/16]
-        wq = F.nvfp4_quantize_2d(dev(w), F.nvfp4_amax(dev(w)), rowwise=False)
-        b_codes = wq["codes_col"]
-        wq_rows = F.nvfp4_quantize_2d(dev(w), F.nvfp4_amax(dev(w)), colwise=False)
-        b_hat = recon(wq_rows["codes_row"], wq_rows["scales"], 2, wq_rows["global_scale"], K, N).T
-    c = host(F.nvfp4_gemm(aq["codes_row"], aq["scales_row"], 1, aq["global_scale"],
-                          b_codes, wq["scales"], mode, wq["global_scale"], M, N, K))
+        sgw = oracle.global_scale(oracle.amax(w))
+        w_rows, b_codes, b_scales = oracle.quantize_2d(w, sgw)
+        b_hat = recon(w_rows, b_scales, 2, sgw, K, N).T
+    c = host(F.nvfp4_gemm(to_gpu(ac), to_gpu(as_), 1, sg_gpu(sga),
+                          to_gpu(b_codes), to_gpu(b_scales), mode, sg_gpu(sgw), M, N, K))
     assert rel_fro(c, a_hat @ b_hat.T) <= 1e-5

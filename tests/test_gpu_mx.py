@@ -44,6 +44,11 @@ def dev(x_bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
 
 
+def to_gpu(a: np.ndarray) -> torch.Tensor:
+    """An oracle-made array (codes, scales) on the device."""
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     torch.cuda.synchronize()
     return t.cpu().numpy()
@@ -160,12 +165,12 @@ def test_quantize_full_gradient_hadamard_sampled():
 def test_dequantize_bit_exact(name):
     x = CASES[name]()
     R, C = x.shape
-    q = F.mxfp4_quantize(dev(x))
-    want = oracle.mx_dequantize(host(q["codes_row"]), host(q["scales_row"]), R, C)
-    got32 = host(F.mxfp4_dequantize(q["codes_row"], q["scales_row"], R, C))
+    codes, scales = oracle.mx_quantize_rows(x)     # the oracle's bytes, decoded on the GPU
+    cd, sd = to_gpu(codes), to_gpu(scales)
+    want = oracle.mx_dequantize(codes, scales, R, C)
+    got32 = host(F.mxfp4_dequantize(cd, sd, R, C))
     assert np.array_equal(got32.view(np.uint32), want.view(np.uint32))
-    got16 = host(F.mxfp4_dequantize(q["codes_row"], q["scales_row"], R, C, out_dtype=torch.bfloat16)
-                 .view(torch.int16)).view(np.uint16)
+    got16 = host(F.mxfp4_dequantize(cd, sd, R, C, out_dtype=torch.bfloat16).view(torch.int16)).view(np.uint16)
     nan = np.isnan(want)
     assert np.array_equal(got16[~nan], (want.view(np.uint32)[~nan] >> 16).astype(np.uint16))
     assert np.all((got16[nan] & 0x7F80) == 0x7F80) and np.all(got16[nan] & 0x7F)
@@ -186,22 +191,19 @@ def test_dequantize_every_code_and_scale_byte():
 
 # ------------------------------------------------------------------ GEMM
 
-def mx_operands(a, b):
-    qa = F.mxfp4_quantize(dev(a))
-    qb = F.mxfp4_quantize(dev(b))
-    return qa["codes_row"], qa["scales_row"], qb["codes_row"], qb["scales_row"]
-
-
 def gemm_check(a, b, rows, out_dtype=None):
+    """The oracle's MXFP4 operands multiplied on the GPU, against the
+    oracle's double product of the same operands."""
     M, K = a.shape
     N = b.shape[0]
-    ac, as_, bc, bs = mx_operands(a, b)
-    c = F.mxfp4_gemm(ac, as_, bc, bs, M, N, K, out_dtype=out_dtype)
+    ac, as_ = oracle.mx_quantize_rows(a)
+    bc, bs = oracle.mx_quantize_rows(b)
+    c = F.mxfp4_gemm(to_gpu(ac), to_gpu(as_), to_gpu(bc), to_gpu(bs), M, N, K, out_dtype=out_dtype)
     if out_dtype == torch.bfloat16:
         c = W.bf16_bits_to_f32(host(c.view(torch.int16)).view(np.uint16))
     else:
         c = host(c)
-    ref = oracle.mx_gemm_rows(host(ac), host(as_), host(bc), host(bs), M, N, K, np.asarray(rows))
+    ref = oracle.mx_gemm_rows(ac, as_, bc, bs, M, N, K, np.asarray(rows))
     got = c[np.asarray(rows)].astype(np.float64)
     err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     row_err = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)

@@ -54,6 +54,35 @@ def f32_bits(a) -> int:
     return int(np.float32(a).view(np.uint32))
 
 
+def to_gpu(a: np.ndarray) -> torch.Tensor:
+    """An oracle-made array (codes, scales) on the device, as the input of
+    the kernel under test."""
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def sg_gpu(sg) -> torch.Tensor:
+    return torch.tensor([float(np.float32(sg))], dtype=torch.float32, device="cuda")
+
+
+def oracle_operand(x: np.ndarray, mode: int):
+    """The oracle's NVFP4 encoding of x as a TN GEMM operand: (codes,
+    scales, S_g). mode 1: 1D rowwise; 2: 2D tiles, rowwise codes; 3: the
+    column copy of x^T (codes [R][C/2], the transposed tensor's tile
+    scales [C/16][R/16])."""
+    if mode == 1:
+        sg = oracle.global_scale(oracle.amax(x))
+        c, s = oracle.quantize_1d_rows(x, sg)
+        return c, s, sg
+    if mode == 2:
+        sg = oracle.global_scale(oracle.amax(x))
+        cr, _, s = oracle.quantize_2d(x, sg)
+        return cr, s, sg
+    xt = np.ascontiguousarray(x.T)
+    sg = oracle.global_scale(oracle.amax(xt))
+    _, cc, s = oracle.quantize_2d(xt, sg)
+    return cc, s, sg
+
+
 # ------------------------------------------------------------- workloads
 
 @functools.lru_cache(maxsize=None)
@@ -399,22 +428,17 @@ def test_rht16_standalone(name, axis):
 
 @pytest.mark.parametrize("mode", [1, 2])
 def test_dequantize(mode):
+    """The oracle's codes and scales, decoded on the GPU: bit-identical to
+    the oracle's decode of the same bytes."""
     x = wl("ragged_weight") if mode == 2 else wl("ragged_act")
-    xd = dev(x)
-    a = F.nvfp4_amax(xd)
     R, C = x.shape
-    if mode == 2:
-        q = F.nvfp4_quantize_2d(xd, a, colwise=False)
-        codes, scales = q["codes_row"], q["scales"]
-    else:
-        q = F.nvfp4_quantize_1d(xd, a)
-        codes, scales = q["codes_row"], q["scales_row"]
-    sg = q["global_scale"]
-    y32 = host(F.nvfp4_dequantize(codes, scales, mode, sg, R, C))
-    y16 = host(F.nvfp4_dequantize(codes, scales, mode, sg, R, C, out_dtype=torch.bfloat16).view(torch.int16))
-    ref = oracle.dequantize(host(codes), host(scales), mode, host(sg)[0], R, C)
+    codes, scales, sg = oracle_operand(x, mode)
+    cd, sd, gd = to_gpu(codes), to_gpu(scales), sg_gpu(sg)
+    y32 = host(F.nvfp4_dequantize(cd, sd, mode, gd, R, C))
+    y16 = host(F.nvfp4_dequantize(cd, sd, mode, gd, R, C, out_dtype=torch.bfloat16).view(torch.int16))
+    ref = oracle.dequantize(codes, scales, mode, sg, R, C)
     assert np.array_equal(y32.view(np.uint32), ref.view(np.uint32))
-    ref16 = oracle.dequantize_bf16(host(codes), host(scales), mode, host(sg)[0], R, C)
+    ref16 = oracle.dequantize_bf16(codes, scales, mode, sg, R, C)
     assert np.array_equal(y16.view(np.uint16), ref16)
 
 
@@ -450,23 +474,17 @@ def test_dequantize_every_code_and_scale_byte(mode):
 
 # ------------------------------------------------------------------- GEMM
 
-def quantized_operands(a_bits, b_bits):
-    ad, bd = dev(a_bits), dev(b_bits)
-    qa = F.nvfp4_quantize_1d(ad, F.nvfp4_amax(ad))
-    qb = F.nvfp4_quantize_2d(bd, F.nvfp4_amax(bd), colwise=False)
-    return qa, qb
-
-
 def gemm_check(a_bits, b_bits, rows, out_dtype=torch.float32):
+    """The oracle's operands (A 1D, B 2D) multiplied on the GPU, against the
+    oracle's double product of the same operands on the given rows."""
     M, K = a_bits.shape
     N = b_bits.shape[0]
-    qa, qb = quantized_operands(a_bits, b_bits)
-    c = F.nvfp4_gemm(qa["codes_row"], qa["scales_row"], 1, qa["global_scale"], qb["codes_row"],
-                     qb["scales"], 2, qb["global_scale"], M, N, K, out_dtype=out_dtype)
+    ac, as_, ag = oracle_operand(a_bits, 1)
+    bc, bs, bg = oracle_operand(b_bits, 2)
+    c = F.nvfp4_gemm(to_gpu(ac), to_gpu(as_), 1, sg_gpu(ag), to_gpu(bc), to_gpu(bs), 2, sg_gpu(bg),
+                     M, N, K, out_dtype=out_dtype)
     c = host(c.float() if out_dtype == torch.bfloat16 else c)
-    ref = oracle.gemm_rows(host(qa["codes_row"]), host(qa["scales_row"]), 1, host(qa["global_scale"])[0],
-                           host(qb["codes_row"]), host(qb["scales"]), 2, host(qb["global_scale"])[0],
-                           M, N, K, np.asarray(rows, np.int64))
+    ref = oracle.gemm_rows(ac, as_, 1, ag, bc, bs, 2, bg, M, N, K, np.asarray(rows, np.int64))
     got = c[np.asarray(rows)].astype(np.float64)
     return np.linalg.norm(got - ref) / np.linalg.norm(ref), c
 
@@ -496,20 +514,11 @@ def test_gemm_more_tiles_than_workgroups(a_mode, b_mode):
     a = W.normal_tensor(M, K, seed=44)
     b = W.normal_tensor(N, K, seed=45, std=0.02)
     log(f"[test_gemm_more_tiles_than_workgroups] modes=({a_mode},{b_mode})")
-    ad, bd = dev(a), dev(b)
-
-    def quant(xd, mode):
-        if mode == 1:
-            q = F.nvfp4_quantize_1d(xd, F.nvfp4_amax(xd))
-            return q["codes_row"], q["scales_row"], q["global_scale"]
-        q = F.nvfp4_quantize_2d(xd, F.nvfp4_amax(xd), colwise=False)
-        return q["codes_row"], q["scales"], q["global_scale"]
-
-    ac, as_, ag = quant(ad, a_mode)
-    bc, bs, bg = quant(bd, b_mode)
-    c = host(F.nvfp4_gemm(ac, as_, a_mode, ag, bc, bs, b_mode, bg, M, N, K))
-    ref = oracle.gemm_rows(host(ac), host(as_), a_mode, host(ag)[0], host(bc), host(bs), b_mode,
-                           host(bg)[0], M, N, K, np.arange(M, dtype=np.int64))
+    ac, as_, ag = oracle_operand(a, a_mode)
+    bc, bs, bg = oracle_operand(b, b_mode)
+    c = host(F.nvfp4_gemm(to_gpu(ac), to_gpu(as_), a_mode, sg_gpu(ag), to_gpu(bc), to_gpu(bs), b_mode,
+                          sg_gpu(bg), M, N, K))
+    ref = oracle.gemm_rows(ac, as_, a_mode, ag, bc, bs, b_mode, bg, M, N, K, np.arange(M, dtype=np.int64))
     err = np.linalg.norm(c.astype(np.float64) - ref) / np.linalg.norm(ref)
     assert err <= 1e-5
     # each row separately too, so a wrong tile cannot hide in the norm
@@ -517,28 +526,15 @@ def test_gemm_more_tiles_than_workgroups(a_mode, b_mode):
     assert row_err.max() <= 1e-5
 
 
-def quant_operand(xd, mode):
-    """NVFP4 operand of a TN GEMM: 1D rowwise, 2D tiles, or (mode 3) the
-    column copy of the transposed tensor with its tile scales."""
-    if mode == 1:
-        q = F.nvfp4_quantize_1d(xd, F.nvfp4_amax(xd))
-        return q["codes_row"], q["scales_row"], q["global_scale"]
-    if mode == 2:
-        q = F.nvfp4_quantize_2d(xd, F.nvfp4_amax(xd), colwise=False)
-        return q["codes_row"], q["scales"], q["global_scale"]
-    xt = xd.t().contiguous()                      # the operand is the column copy of x^T
-    q = F.nvfp4_quantize_2d(xt, F.nvfp4_amax(xt), rowwise=False)
-    return q["codes_col"], q["scales"], q["global_scale"]
-
-
 def reference_rows(codes, scales, mode, sg, R, C):
-    """Double reconstruction of an operand in any scale mode: mode 3 is
-    decoded as the 2D rowwise layout of the transposed tensor's tiles."""
+    """Double reconstruction by the oracle of an oracle-made operand in any
+    scale mode: mode 3 is decoded as the 2D rowwise layout of the
+    transposed tensor's tiles."""
     if mode != 3:
-        return oracle.dequantize_f64_rows(host(codes), host(scales), mode, host(sg)[0], R, C, np.arange(R))
+        return oracle.dequantize_f64_rows(codes, scales, mode, sg, R, C, np.arange(R))
     # codes_col [R][C/2] of x^T [C][R] with scales [C/16][R/16]: element (r, c) has scale [c/16][r/16]
-    st = np.ascontiguousarray(host(scales).T)      # [R/16][C/16]
-    return oracle.dequantize_f64_rows(host(codes), st, 2, host(sg)[0], R, C, np.arange(R))
+    st = np.ascontiguousarray(scales.T)      # [R/16][C/16]
+    return oracle.dequantize_f64_rows(codes, st, 2, sg, R, C, np.arange(R))
 
 
 @pytest.mark.parametrize("K", [1024, 4160])
@@ -550,9 +546,10 @@ def test_gemm_64_element_stages(K, a_mode, b_mode):
     log(f"[test_gemm_64] K={K} modes=({a_mode},{b_mode})")
     a = W.normal_tensor(M, K, seed=46)
     b = W.normal_tensor(N, K, seed=47, std=0.02)
-    ac, as_, ag = quant_operand(dev(a), a_mode)
-    bc, bs, bg = quant_operand(dev(b), b_mode)
-    c = host(F.nvfp4_gemm(ac, as_, a_mode, ag, bc, bs, b_mode, bg, M, N, K))
+    ac, as_, ag = oracle_operand(a, a_mode)
+    bc, bs, bg = oracle_operand(b, b_mode)
+    c = host(F.nvfp4_gemm(to_gpu(ac), to_gpu(as_), a_mode, sg_gpu(ag), to_gpu(bc), to_gpu(bs), b_mode,
+                          sg_gpu(bg), M, N, K))
     ref = reference_rows(ac, as_, a_mode, ag, M, K) @ reference_rows(bc, bs, b_mode, bg, N, K).T
     err = np.linalg.norm(c.astype(np.float64) - ref) / np.linalg.norm(ref)
     row_err = np.linalg.norm(c.astype(np.float64) - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
@@ -565,12 +562,13 @@ def test_gemm_unaligned_scales_take_the_32_element_stages():
     M, N, K = 272, 400, 1024
     a = W.normal_tensor(M, K, seed=48)
     b = W.normal_tensor(N, K, seed=49, std=0.02)
-    ac, as_, ag = quant_operand(dev(a), 1)
-    bc, bs, bg = quant_operand(dev(b), 2)
-    shifted = torch.empty(as_.numel() + 1, dtype=torch.uint8, device="cuda")[1:].view(as_.shape)
-    shifted.copy_(as_)
-    c_ref = host(F.nvfp4_gemm(ac, as_, 1, ag, bc, bs, 2, bg, M, N, K))
-    c = host(F.nvfp4_gemm(ac, shifted, 1, ag, bc, bs, 2, bg, M, N, K))
+    ac, as_, ag = oracle_operand(a, 1)
+    bc, bs, bg = oracle_operand(b, 2)
+    acd, asd, agd, bcd, bsd, bgd = to_gpu(ac), to_gpu(as_), sg_gpu(ag), to_gpu(bc), to_gpu(bs), sg_gpu(bg)
+    shifted = torch.empty(asd.numel() + 1, dtype=torch.uint8, device="cuda")[1:].view(asd.shape)
+    shifted.copy_(asd)
+    c_ref = host(F.nvfp4_gemm(acd, asd, 1, agd, bcd, bsd, 2, bgd, M, N, K))
+    c = host(F.nvfp4_gemm(acd, shifted, 1, agd, bcd, bsd, 2, bgd, M, N, K))
     ref = reference_rows(ac, as_, 1, ag, M, K) @ reference_rows(bc, bs, 2, bg, N, K).T
     for cc in (c, c_ref):
         assert np.linalg.norm(cc.astype(np.float64) - ref) / np.linalg.norm(ref) <= 1e-5
