@@ -19,7 +19,13 @@ and the dequantize-and-contract GEMM (8192x14336x4096, TFLOP/s).
 
 Prints one JSON line. Inputs are synthetic (seeded), resident in HBM before
 timing starts; the timed loop rotates over input copies whose total exceeds
-the 256 MB Infinity Cache, so each step reads its input from HBM.
+the 256 MB Infinity Cache, so each step reads its input from HBM (the warm
+figure, one copy served from that cache, is a separate row).
+
+CPU figures, from the CPU oracle on the host: `cpu_baseline` (the step's
+work on the activation, one thread), `cpu_baseline_all_cores` (the same
+functions over row and column ranges on every core, checked byte-identical)
+and `cpu_gemm_reference` (the fp64 product of 256 sampled GEMM rows).
 """
 from __future__ import annotations
 
@@ -72,6 +78,8 @@ def parse():
                    help="also run a plain 256 MiB device copy (counter calibration)")
     p.add_argument("--cpu-rows", type=int, default=8192,
                    help="rows of the activation in the CPU baseline sample")
+    p.add_argument("--no-cpu-gemm", action="store_true",
+                   help="skip the CPU oracle's sampled GEMM reference")
     return p.parse_args()
 
 
@@ -94,6 +102,95 @@ def recorded_traffic():
     if not m_sha or not m_b or m_sha.group(1) != sources_digest(DOMINANT_SOURCES):
         return None
     return float(m_b.group(1))
+
+
+def host_threads() -> int:
+    """Host threads for the all-cores oracle run: the CPUs this process may
+    use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def split(n: int, parts: int, align: int):
+    """[lo, hi) ranges covering 0..n, boundaries multiples of align."""
+    step = -(-n // parts)
+    step = -(-step // align) * align
+    return [(lo, min(n, lo + step)) for lo in range(0, n, step)]
+
+
+def cpu_all_cores(oracle, sample, ref, args):
+    """The same oracle functions on every host core: the amax over row
+    ranges, then the rowwise layout over row ranges and the columnwise
+    layout over column ranges, all with the one global scale; the result
+    must equal the single-threaded call's byte for byte. The C functions
+    release the interpreter lock, so threads run them in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    cores = host_threads()
+    R_s, C_s = sample.shape
+    rr, cr = split(R_s, cores, 16), split(C_s, cores, 1)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        a = max(ex.map(lambda r: oracle.amax(sample[r[0]:r[1]]), rr))
+        sg = oracle.global_scale(a)
+        rows = list(ex.map(lambda r: oracle.quantize_1d_rows(sample, sg, r0=r[0], r1=r[1]), rr))
+        cols = list(ex.map(lambda c: oracle.quantize_1d_cols(sample, sg, c0=c[0], c1=c[1]), cr))
+    t = time.perf_counter() - t0
+    same = (np.float32(a) == np.float32(ref["amax"]) and
+            np.array_equal(np.concatenate([r[0] for r in rows]), ref["codes_row"]) and
+            np.array_equal(np.concatenate([r[1] for r in rows]), ref["scales_row"]) and
+            np.array_equal(np.concatenate([c[0] for c in cols]), ref["codes_col"]) and
+            np.array_equal(np.concatenate([c[1] for c in cols]), ref["scales_col"]))
+    log(f"[bench] CPU oracle on {cores} threads: {t:.2f} s, identical={same}")
+    return {"value": round(sample.size * 3.125 / t / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"same {R_s}x{C_s} sample; amax over {len(rr)} row ranges, rowwise over {len(rr)} row "
+                      f"ranges, columnwise over {len(cr)} column ranges, one global scale",
+            "seconds": round(t, 2), "identical_to_single_thread": bool(same)}
+
+
+def cpu_gemm_reference(oracle, W):
+    """The oracle's GEMM reference as the parity tests use it: the NVFP4
+    operands of the 8192x14336x4096 product (quantized by the oracle), and
+    the double-precision product of 256 sampled rows of A with all of B
+    (B reconstructed once). The contraction runs in numpy's BLAS; its
+    thread count is recorded."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    a_bits, b_bits = W.gemm_operands()
+    M, K = a_bits.shape
+    N = b_bits.shape[0]
+    rows = W.gemm_sample_rows()
+    cores = host_threads()
+    t0 = time.perf_counter()
+    ag = oracle.global_scale(oracle.amax(a_bits))
+    with ThreadPoolExecutor(cores) as ex:
+        parts = list(ex.map(lambda r: oracle.quantize_1d_rows(a_bits, ag, r0=r[0], r1=r[1]),
+                            split(M, cores, 16)))
+    ac, as_ = np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+    bg = oracle.global_scale(oracle.amax(b_bits))
+    bc, _, bs = oracle.quantize_2d(b_bits, bg)
+    t_q = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.gemm_rows(ac, as_, 1, ag, bc, bs, 2, bg, M, N, K, rows)
+    t = time.perf_counter() - t0
+    flop = 2.0 * rows.size * N * K
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                   default=1)
+    except Exception:  # threadpoolctl missing or unreadable
+        blas = None
+    log(f"[bench] CPU oracle GEMM reference: {rows.size} rows in {t:.2f} s "
+        f"({flop / t / 1e9:.1f} GFLOP/s, BLAS threads {blas})")
+    return {"value": round(flop / t / 1e12, 5), "unit": "TFLOP/s", "cores": blas, "kind": "oracle",
+            "sample": f"{rows.size} sampled rows of the {M}x{N}x{K} product in fp64 (A rows and all of B "
+                      f"reconstructed exactly, then one BLAS product)",
+            "seconds": round(t, 2), "operand_quantization_seconds": round(t_q, 2),
+            "full_product_seconds_extrapolated": round(t * M / rows.size, 1)}
 
 
 def error_study(F, tensors, mask, dev):
@@ -306,6 +403,21 @@ def main():
         row_hbm("fill_256MiB_torch", timed(lambda: dst.fill_(2.0)), src.numel() * 4, [src.numel()],
                 note="device fill: practical ceiling for write-only streams")
         del src, dst
+        # The step on one input copy, back to back: the 64 MiB tensor stays in
+        # the 256 MB Infinity Cache between steps (warm), unlike the headline
+        # loop, which rotates copies so every step reads HBM.
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(5):
+            F.nvfp4_quantize_1d(xs[0], ws, rowwise=True, colwise=True, out=outs[0], fused_amax=True)
+        w0.record(stream)
+        for _ in range(50):
+            F.nvfp4_quantize_1d(xs[0], ws, rowwise=True, colwise=True, out=outs[0], fused_amax=True)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        row_hbm("step_warm_one_input_copy", w0.elapsed_time(w1) / 50 * 1e3, step_bytes, [R, C],
+                note="the headline step on one input copy, 50 back-to-back launches: the input is "
+                     "served from the Infinity Cache, so this is not an HBM figure")
         x = xs[0]
         n_x = R * C
         row_hbm("amax_activation", timed(lambda: F.nvfp4_amax(x, out=amax)), 2 * n_x, [R, C])
@@ -503,14 +615,14 @@ def main():
         del flush
 
     # -------------------------------------------------- CPU oracle baseline
-    cpu = None
+    cpu = cpu_all = cpu_gemm = None
     if not args.no_cpu:
         import oracle
 
         sample = np.ascontiguousarray(x_host[: args.cpu_rows])
         log(f"[bench] CPU oracle on the first {args.cpu_rows} rows")
         t0 = time.perf_counter()
-        oracle.quantize_1d(sample, rowwise=True, colwise=True)
+        ref = oracle.quantize_1d(sample, rowwise=True, colwise=True)
         t_cpu = time.perf_counter() - t0
         ns = sample.size
         cpu = {"value": round(ns * (2 + 2 + 2 * 0.5625) / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
@@ -518,6 +630,8 @@ def main():
                "sample": f"first {args.cpu_rows} rows of the activation ({args.cpu_rows}x{C}), amax + rowwise "
                          f"+ columnwise 1D RNE quantize as one tensor; {t_cpu:.1f} s single-threaded",
                "seconds": round(t_cpu, 2)}
+        cpu_all = cpu_all_cores(oracle, sample, ref, args)
+        cpu_gemm = None if args.no_cpu_gemm else cpu_gemm_reference(oracle, W)
 
     line = {
         "metric": METRIC,
@@ -542,6 +656,8 @@ def main():
         "gemm_tflops": gemm_tflops,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
+        "cpu_gemm_reference": cpu_gemm,
         "rows": rows,
     }
     print(json.dumps(line), flush=True)
