@@ -26,6 +26,7 @@ __all__ = [
     "gemm_sample_rows",
     "rht_sign_mask",
     "normal_tensor",
+    "large_tensor",
     "SR_SEED",
 ]
 
@@ -110,3 +111,24 @@ def rht_sign_mask(seed: int = 7) -> int:
     (bit j set = flip element j of each 16-point segment)."""
     rng = np.random.default_rng(seed)
     return int(rng.integers(0, 1 << 16))
+
+
+def large_tensor(rows: int = 65552, cols: int = 32768, seed: int = 9) -> np.ndarray:
+    """A tensor past 2^31 elements (65552 x 32768 = 2^31 + 2^19, 4.3 GB of
+    bf16), built in one pass: row r is row r % 16 of a seeded N(0,1) block
+    with its exponent field moved by a seeded per-row shift in [-3, 3]
+    (an exact power-of-two rescaling; elements with exponent fields outside
+    9..239 are left as drawn). Blocks therefore differ from row to row in
+    scale, and every element past offset 2^31 is a distinct function of
+    (row, column)."""
+    rng = np.random.default_rng(seed)
+    base = f32_to_bf16_bits(rng.standard_normal((16, cols), dtype=np.float32))
+    shift = rng.integers(-3, 4, size=rows)
+    exp_field = (base >> 7) & 0xFF
+    movable = (exp_field > 8) & (exp_field < 240)
+    table = np.empty((16 * 7, cols), np.uint16)
+    for k in range(7):
+        moved = (base.astype(np.int32) + ((k - 3) << 7)).astype(np.uint16)
+        table[k::7] = np.where(movable, moved, base)
+    index = (np.arange(rows) % 16) * 7 + (shift + 3)
+    return table[index]
