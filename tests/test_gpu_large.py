@@ -107,3 +107,40 @@ def test_past_2_31_elements():
     for i, col in enumerate(COLS):
         c, s = oracle.quantize_1d_cols(x, sg_t, True, SEED, True, mask, col, col + 1)
         assert np.array_equal(cc[i], c[0]) and np.array_equal(sc[i], s[0]), f"transformed column {col}"
+
+
+def rel_rows(got, ref):
+    return (np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)).max()
+
+
+def test_gemm_output_past_2_31_elements():
+    """C of 65552 x 32768 (2^31 + 2^19 elements) from K = 64: NVFP4 (fp32 and
+    bf16 C) and MXFP4 products of the oracle's operands, rows either side of
+    element 2^31 within 1e-5 of the oracle's double product."""
+    M, N, K = 65552, 32768, 64
+    a = W.normal_tensor(M, K, seed=91)
+    b = W.normal_tensor(N, K, seed=92, std=0.02)
+    rows = np.array([0, 1, 30001, 65535, 65536, 65537, 65551], np.int64)
+    to_gpu = lambda v: torch.from_numpy(np.ascontiguousarray(v)).cuda()
+    sg_gpu = lambda v: torch.tensor([float(np.float32(v))], dtype=torch.float32, device="cuda")
+    ag = oracle.global_scale(oracle.amax(a))
+    ac, as_ = oracle.quantize_1d_rows(a, ag)
+    bg = oracle.global_scale(oracle.amax(b))
+    bc, _, bs = oracle.quantize_2d(b, bg)
+    ref = oracle.gemm_rows(ac, as_, 1, ag, bc, bs, 2, bg, M, N, K, rows)
+    sel = torch.tensor(rows, device="cuda")
+    for dt in (torch.float32, torch.bfloat16):
+        log(f"[test_gemm_output_past_2_31_elements] NVFP4 {dt}")
+        c = F.nvfp4_gemm(to_gpu(ac), to_gpu(as_), 1, sg_gpu(ag), to_gpu(bc), to_gpu(bs), 2, sg_gpu(bg),
+                         M, N, K, out_dtype=dt)
+        got = host(c[sel].float()).astype(np.float64)
+        del c
+        torch.cuda.empty_cache()
+        assert rel_rows(got, ref) <= (1e-5 if dt == torch.float32 else 2.0 ** -8)
+    log("[test_gemm_output_past_2_31_elements] MXFP4 float32")
+    mac, mas = oracle.mx_quantize_rows(a)
+    mbc, mbs = oracle.mx_quantize_rows(b)
+    mref = oracle.mx_gemm_rows(mac, mas, mbc, mbs, M, N, K, rows)
+    c = F.mxfp4_gemm(to_gpu(mac), to_gpu(mas), to_gpu(mbc), to_gpu(mbs), M, N, K)
+    got = host(c[sel]).astype(np.float64)
+    assert rel_rows(got, mref) <= 1e-5
