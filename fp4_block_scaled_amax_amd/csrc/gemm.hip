@@ -27,7 +27,9 @@
 //     NVFP4_SCALE_2D_T, transposed on the way in), so its rows fetch only
 //     codes per stage; K above kLdsScaleK falls back to per-row scale loads.
 //   - The grid is persistent (one workgroup per CU); a tile's output stores
-//     drain while the next tile starts.
+//     drain while the next tile starts. A last round that would occupy at
+//     most half the grid runs as a second launch of 256 x 128 half tiles
+//     (waves of 64 x 64) on twice as many workgroups.
 //   - Optionally the epilogue also reduces max |C| of the stored values (the
 //     tensor amax a following NVFP4 quantization of C needs), so that
 //     quantization reads C once instead of twice.
@@ -180,24 +182,24 @@ __device__ __forceinline__ f16x8 lds_fragment(const uint8_t* lds, int row, int k
     return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(lds + row * Geo<KS>::kRowBytes + kbyte));
 }
 
-// The MFMAs of one stage for this wave's 64 x 128 sub-tile.
-template <int KS>
+// The MFMAs of one stage for this wave's 64 x (32 FN) sub-tile.
+template <int KS, int FN>
 __device__ __forceinline__ void stage_mfma(const uint8_t* buf, int wm, int wn, int frow, int fk,
                                            floatx16 (&acc)[2][4])
 {
 #pragma unroll
     for (int ks = 0; ks < KS / 16; ++ks) {
-        f16x8 fa[2], fb[4];
+        f16x8 fa[2], fb[FN];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
             fa[a] = lds_fragment<KS>(buf, wm + a * 32 + frow, ks * 32 + fk);
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < FN; ++b)
             fb[b] = lds_fragment<KS>(buf + kBM * Geo<KS>::kRowBytes, wn + b * 32 + frow, ks * 32 + fk);
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < FN; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[a], fb[b], acc[a][b], 0, 0, 0);
     }
 }
@@ -264,8 +266,15 @@ __device__ __forceinline__ void stage_tile_scales(uint8_t* dst, const uint8_t* s
 // patterns, an integer maximum like nvfp4_amax's) into *g.c_amax, which the
 // launch has reset: a running maximum per lane over its tiles, one atomic
 // per wave at the end.
-template <bool BF16_OUT, bool WIDE, bool AMAX, int KS>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n)
+//
+// FN = 4: whole 256 x 256 tiles, positions 0 .. count-1 of the tile order.
+// FN = 2: half tiles of 256 x 128 (each wave 64 x 64), units 0 .. count-1,
+// unit u being half u & 1 of tile first + u / 2: a partial last round of
+// whole tiles, split so that it fills twice as many CUs. Every output
+// element is summed in the same order either way.
+template <bool BF16_OUT, bool WIDE, bool AMAX, int KS, int FN>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int first,
+                                                        int count)
 {
     constexpr int kRowBytes = Geo<KS>::kRowBytes;
     constexpr int kStageBytes = Geo<KS>::kStageBytes;
@@ -277,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     const int64_t K = g.K;
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * (32 * FN);
     const int nstages = (int)((K + KS - 1) / KS);
     const int last = nstages - 1;
     const int frow = lane & 31;
@@ -295,14 +304,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     const bool a_stage = g.a_two_d && K <= kLdsScaleK && ((reinterpret_cast<uintptr_t>(g.a_scales) & 15) == 0);
     const bool b_stage = g.b_two_d && K <= kLdsScaleK && ((reinterpret_cast<uintptr_t>(g.b_scales) & 15) == 0);
     const bool my_stage = is_b ? b_stage : a_stage;
+    // Half tiles need 128 B rows: the last two waves fetch nothing.
+    const bool loads = FN == 4 || !is_b || t - kBM < 64 * FN;
 
     // Persistent: each workgroup walks tiles; a tile's output stores drain
     // while the next tile's first stages load and decode.
-    const int nt = tiles_m * tiles_n;
     for (int round = 0;; ++round) {
-        const int tile = gemm_tile_index(round);
-        if (tile >= nt)
+        const int unit = gemm_tile_index(round);
+        if (unit >= count)
             break;
+        const int tile = FN == 4 ? unit : first + (unit >> 1);
+        const int half = FN == 4 ? 0 : (unit & 1);
         // Tiles are ordered in groups of kGroupM tile rows, column by column
         // inside a group. At one workgroup per CU an XCD's share of a round
         // is 32 consecutive positions, inside a group a 4 x 8 block of tiles:
@@ -311,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         const int gm = min(kGroupM, tiles_m - group * kGroupM);
         const int in_group = tile - group * kGroupM * tiles_n;
         const int tm = group * kGroupM + in_group % gm, tn = in_group / gm;
-        const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+        const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN + half * (32 * FN * 2);
 
         // This thread's row: A rows 0..255, then B rows 0..255.
         const int64_t row = is_b ? n0 + (t - kBM) : m0 + t;
@@ -340,40 +352,49 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
             for (int b = 0; b < 4; ++b)
                 acc[a][b] = floatx16{};
 
-        decode_stage_to_lds<KS>(fetch_stage<KS, WIDE>(code_row, scale_row, 0, sstride, bstride, K, my_lds_scales), my_row0);
-        // Two register sets alternate (stage s+1 in one, s+2 in the other)
-        // so a fetch lands in registers the decode has just consumed: no
-        // copies of in-flight loads, hence no wait on the newest fetch.
-        RowStage<KS> sa = fetch_stage<KS, WIDE>(code_row, scale_row, min(1, last), sstride, bstride, K, my_lds_scales);
-        __builtin_amdgcn_sched_barrier(0);  // issue order sa, sb as in the loop
-        RowStage<KS> sb = fetch_stage<KS, WIDE>(code_row, scale_row, min(2, last), sstride, bstride, K, my_lds_scales);
+        RowStage<KS> sa, sb;
+        if (loads) {
+            decode_stage_to_lds<KS>(fetch_stage<KS, WIDE>(code_row, scale_row, 0, sstride, bstride, K, my_lds_scales),
+                                    my_row0);
+            // Two register sets alternate (stage s+1 in one, s+2 in the
+            // other) so a fetch lands in registers the decode has just
+            // consumed: no copies of in-flight loads, hence no wait on the
+            // newest fetch.
+            sa = fetch_stage<KS, WIDE>(code_row, scale_row, min(1, last), sstride, bstride, K, my_lds_scales);
+            __builtin_amdgcn_sched_barrier(0);  // issue order sa, sb as in the loop
+            sb = fetch_stage<KS, WIDE>(code_row, scale_row, min(2, last), sstride, bstride, K, my_lds_scales);
+        }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
 
         int s = 0;
         for (; s + 1 < nstages; s += 2) {
-            stage_mfma<KS>(lds, wm, wn, frow, fk, acc);
-            decode_stage_to_lds<KS>(sa, my_row0 + kStageBytes);
-            sa = fetch_stage<KS, WIDE>(code_row, scale_row, min(s + 3, last), sstride, bstride, K, my_lds_scales);
+            stage_mfma<KS, FN>(lds, wm, wn, frow, fk, acc);
+            if (loads) {
+                decode_stage_to_lds<KS>(sa, my_row0 + kStageBytes);
+                sa = fetch_stage<KS, WIDE>(code_row, scale_row, min(s + 3, last), sstride, bstride, K, my_lds_scales);
+            }
             __syncthreads();
             // keep each half's work in its half: the scheduler would
             // otherwise hoist the next decode and wait on the newest fetch
             __builtin_amdgcn_sched_barrier(0);
-            stage_mfma<KS>(lds + kStageBytes, wm, wn, frow, fk, acc);
-            decode_stage_to_lds<KS>(sb, my_row0);
-            sb = fetch_stage<KS, WIDE>(code_row, scale_row, min(s + 4, last), sstride, bstride, K, my_lds_scales);
+            stage_mfma<KS, FN>(lds + kStageBytes, wm, wn, frow, fk, acc);
+            if (loads) {
+                decode_stage_to_lds<KS>(sb, my_row0);
+                sb = fetch_stage<KS, WIDE>(code_row, scale_row, min(s + 4, last), sstride, bstride, K, my_lds_scales);
+            }
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
         }
         if (s < nstages) {
-            stage_mfma<KS>(lds, wm, wn, frow, fk, acc);
+            stage_mfma<KS, FN>(lds, wm, wn, frow, fk, acc);
             __syncthreads();  // buffer 0 is rewritten by the next tile
         }
 
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
+            for (int b = 0; b < FN; ++b) {
                 const int64_t col = n0 + wn + b * 32 + (lane & 31);
                 if (col >= g.N)
                     continue;
@@ -420,7 +441,7 @@ int gemm_capacity()
         return c;
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(gemm_kernel<BF16_OUT, WIDE, AMAX, KS>), kThreads, 0) !=
+            &per_cu, reinterpret_cast<const void*>(gemm_kernel<BF16_OUT, WIDE, AMAX, KS, 4>), kThreads, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
@@ -430,6 +451,9 @@ int gemm_capacity()
     return c;
 }
 
+// Whole tiles round by round on a persistent grid; a last round that would
+// fill at most half the grid runs instead as half tiles on twice as many
+// workgroups (a second launch), so it takes about half a round.
 template <bool BF16_OUT, bool WIDE, bool AMAX, int KS>
 hipError_t launch_variant(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t stream)
 {
@@ -437,10 +461,17 @@ hipError_t launch_variant(const GemmArgs& a, int tiles_m, int tiles_n, hipStream
     if (cap <= 0)
         return hipErrorInvalidDevice;
     const int nt = tiles_m * tiles_n;
-    const dim3 grid((unsigned)(nt < cap ? nt : cap));
+    const int rounds = nt / cap, rem = nt % cap;
+    const bool split_tail = rem > 0 && 2 * rem <= cap;
+    const int whole = split_tail ? rounds * cap : nt;
     if (AMAX)
         hipLaunchKernelGGL(gemm_amax_reset_kernel, dim3(1), dim3(1), 0, stream, a.c_amax);
-    hipLaunchKernelGGL((gemm_kernel<BF16_OUT, WIDE, AMAX, KS>), grid, dim3(kThreads), 0, stream, a, tiles_m, tiles_n);
+    if (whole > 0)
+        hipLaunchKernelGGL((gemm_kernel<BF16_OUT, WIDE, AMAX, KS, 4>), dim3((unsigned)(whole < cap ? whole : cap)),
+                           dim3(kThreads), 0, stream, a, tiles_m, tiles_n, 0, whole);
+    if (split_tail)
+        hipLaunchKernelGGL((gemm_kernel<BF16_OUT, WIDE, AMAX, KS, 2>), dim3((unsigned)(2 * rem)), dim3(kThreads), 0,
+                           stream, a, tiles_m, tiles_n, whole, 2 * rem);
     return hipGetLastError();
 }
 

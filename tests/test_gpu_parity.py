@@ -574,6 +574,27 @@ def test_gemm_unaligned_scales_take_the_32_element_stages():
         assert np.linalg.norm(cc.astype(np.float64) - ref) / np.linalg.norm(ref) <= 1e-5
 
 
+def test_gemm_half_tiles_equal_whole_tiles():
+    """A last round of at most half the grid runs as 256 x 128 half tiles:
+    the 1024 x 2048 product (32 tiles, all halved) equals the same block of
+    the 4096 x 4096 product (256 whole tiles, one full round on 256 CUs)
+    bit for bit, from the same operand bytes; both within 1e-5 of the
+    oracle."""
+    K = 512
+    a = W.normal_tensor(4096, K, seed=93)
+    b = W.normal_tensor(4096, K, seed=94, std=0.02)
+    ac, as_, ag = oracle_operand(a, 1)
+    bc, bs, bg = oracle_operand(b, 2)
+    big = host(F.nvfp4_gemm(to_gpu(ac), to_gpu(as_), 1, sg_gpu(ag), to_gpu(bc), to_gpu(bs), 2, sg_gpu(bg),
+                            4096, 4096, K))
+    small = host(F.nvfp4_gemm(to_gpu(ac[:1024]), to_gpu(as_[:1024]), 1, sg_gpu(ag), to_gpu(bc[:2048]),
+                              to_gpu(bs[:128]), 2, sg_gpu(bg), 1024, 2048, K))
+    assert np.array_equal(small.view(np.uint32), big[:1024, :2048].view(np.uint32))
+    rows = np.arange(0, 1024, 37, dtype=np.int64)
+    ref = oracle.gemm_rows(ac, as_, 1, ag, bc[:2048], bs[:128], 2, bg, 4096, 2048, K, rows)
+    assert np.linalg.norm(small[rows] - ref) / np.linalg.norm(ref) <= 1e-5
+
+
 def test_gemm_bf16_output_is_rounded_fp32():
     a = W.normal_tensor(272, 528, seed=42)
     b = W.normal_tensor(400, 528, seed=43, std=0.02)
