@@ -215,7 +215,10 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int scale_mode
  * and lies in [2^-10, 2688], so it is an fp16 value), products are summed
  * in fp32 on the matrix cores, and the sum is multiplied by
  * fl(S_gA * S_gB). The summation order differs from a sequential sum, so
- * results match an exact product to fp32 rounding, not bit for bit.
+ * results match an exact product to fp32 rounding, not bit for bit. Each
+ * element is accumulated in one fixed order (K ascending, 16 products at a
+ * time) whatever M, N and the work split, so a given element of C is
+ * reproducible bit for bit across calls and shapes.
  *   a_codes [M][K/2], a_scales per a_scale_mode over [M][K]
  *   b_codes [N][K/2], b_scales per b_scale_mode over [N][K]
  *   Scale modes: NVFP4_SCALE_1D [rows][K/16]; NVFP4_SCALE_2D [rows/16][K/16];
