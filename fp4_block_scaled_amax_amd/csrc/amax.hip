@@ -12,6 +12,11 @@ constexpr int kThreads = 256;
 // so a few hundred atomics on one address instead of thousands).
 constexpr int kAmaxThreads = 1024;
 constexpr int kAmaxMaxBlocks = 256;
+// The transform's amax: the pipelined loop (two register sets, one
+// workgroup per CU) where the butterflies would otherwise wait for the
+// loads, the plain loop (more waves per SIMD) for large tensors.
+constexpr int64_t kRhtPipeItems = (int64_t)1 << 18;
+constexpr int kRhtPipeBlocks = 256;
 
 __global__ void amax_reset_kernel(uint32_t* out, int n)
 {
@@ -83,7 +88,54 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_bf16_kernel(const uint4* __
 // the sign diagonal is applied to the packed words, the 1/4 to the maximum.
 // BOTH: the same read also gives the plain amax (into out[0]; the
 // transform's into out[1]), half an integer max per element more.
+//
+// Each thread walks items of 16 rows x 8 columns. PIPE: it loads the next
+// item into the other of two register sets before transforming the current
+// one, so the butterflies overlap the loads in flight (one wave per SIMD
+// at this register count); else one item at a time, with more waves per
+// SIMD to overlap them instead.
+
+// Load one item: 16 rows of 8 bf16, sign-flipped by the mask; with BOTH
+// also fold the raw magnitudes into pm.
 template <bool BOTH>
+__device__ __forceinline__ void rht_load_item(const uint16_t* __restrict__ x, int64_t cols, int64_t groups,
+                                              int64_t it, uint4 (&v)[16])
+{
+    const int64_t rb = it / groups, cg = it - rb * groups;
+    const uint16_t* base = x + (rb * 16) * cols + cg * 8;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        v[i] = load16(base + i * cols);
+}
+
+template <bool BOTH>
+__device__ __forceinline__ void rht_item_max(uint4 (&v)[16], uint32_t mask, uint32_t& pm, uint32_t& m)
+{
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (BOTH) {
+            pm = pk_max_u16(pm, v[i].x & 0x7FFF7FFFu);
+            pm = pk_max_u16(pm, v[i].y & 0x7FFF7FFFu);
+            pm = pk_max_u16(pm, v[i].z & 0x7FFF7FFFu);
+            pm = pk_max_u16(pm, v[i].w & 0x7FFF7FFFu);
+        }
+        const uint32_t sg = rht_row_sign(mask, i);
+        v[i] = make_uint4(v[i].x ^ sg, v[i].y ^ sg, v[i].z ^ sg, v[i].w ^ sg);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float z[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            z[i] = bf16_at(v[i], j);
+        hadamard16(z);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            m = max(m, __float_as_uint(z[i]) & 0x7FFFFFFFu);
+    }
+}
+
+template <bool BOTH, bool PIPE>
 __global__ __launch_bounds__(kThreads) void amax_rht_kernel(const uint16_t* __restrict__ x,
                                                              int64_t rows, int64_t cols,
                                                              uint32_t mask,
@@ -94,33 +146,28 @@ __global__ __launch_bounds__(kThreads) void amax_rht_kernel(const uint16_t* __re
     const int64_t items = (rows >> 4) * groups;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     uint32_t m = 0u;
-    for (int64_t it = (int64_t)blockIdx.x * kThreads + threadIdx.x; it < items; it += stride) {
-        const int64_t rb = it / groups, cg = it - rb * groups;
-        const uint16_t* base = x + (rb * 16) * cols + cg * 8;
-        uint4 v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            v[i] = load16(base + i * cols);
-            if (BOTH) {
-                pm = pk_max_u16(pm, v[i].x & 0x7FFF7FFFu);
-                pm = pk_max_u16(pm, v[i].y & 0x7FFF7FFFu);
-                pm = pk_max_u16(pm, v[i].z & 0x7FFF7FFFu);
-                pm = pk_max_u16(pm, v[i].w & 0x7FFF7FFFu);
-            }
-            const uint32_t sg = rht_row_sign(mask, i);
-            v[i] = make_uint4(v[i].x ^ sg, v[i].y ^ sg, v[i].z ^ sg, v[i].w ^ sg);
+    int64_t it = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (!PIPE) {
+        for (; it < items; it += stride) {
+            uint4 v[16];
+            rht_load_item<BOTH>(x, cols, groups, it, v);
+            rht_item_max<BOTH>(v, mask, pm, m);
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float z[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                z[i] = bf16_at(v[i], j);
-            hadamard16(z);
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                m = max(m, __float_as_uint(z[i]) & 0x7FFFFFFFu);
-        }
+    }
+    uint4 va[16], vb[16];
+    if (PIPE && it < items)
+        rht_load_item<BOTH>(x, cols, groups, it, va);
+    while (PIPE && it < items) {
+        if (it + stride < items)
+            rht_load_item<BOTH>(x, cols, groups, it + stride, vb);
+        rht_item_max<BOTH>(va, mask, pm, m);
+        it += stride;
+        if (it >= items)
+            break;
+        if (it + stride < items)
+            rht_load_item<BOTH>(x, cols, groups, it + stride, va);
+        rht_item_max<BOTH>(vb, mask, pm, m);
+        it += stride;
     }
     // The 1/4 once, on the maximum: scaling by a power of two is monotone
     // (also where it rounds, in the subnormal range), so
@@ -165,13 +212,17 @@ hipError_t launch_amax_rht(const uint16_t* x, int64_t rows, int64_t cols, uint32
     uint32_t* out = reinterpret_cast<uint32_t*>(amax);
     hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(64), 0, stream, out, both ? 2 : 1);
     const int64_t items = (rows >> 4) * (cols >> 3);
-    const int grid = grid_for(items, kThreads, 1024);
+    const bool pipe = both || items <= kRhtPipeItems;
+    const int grid = pipe ? grid_for(items, kThreads, kRhtPipeBlocks) : grid_for(items, kThreads, 1024);
     if (both)
-        hipLaunchKernelGGL(amax_rht_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, mask,
-                           out);
+        hipLaunchKernelGGL((amax_rht_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols,
+                           mask, out);
+    else if (pipe)
+        hipLaunchKernelGGL((amax_rht_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols,
+                           mask, out);
     else
-        hipLaunchKernelGGL(amax_rht_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, x, rows, cols, mask,
-                           out);
+        hipLaunchKernelGGL((amax_rht_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols,
+                           mask, out);
     return hipGetLastError();
 }
 
