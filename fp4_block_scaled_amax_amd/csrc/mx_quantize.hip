@@ -278,55 +278,61 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_rows_kernel(const uint16
     }
 }
 
-// Dequantize: one thread per 32-element block (16 code bytes, one scale).
+// Dequantize: each lane reconstructs E consecutive elements (8 for bf16
+// output, 4 for binary32: one 16-byte store), so a wave's stores are one
+// contiguous run; the lanes of a 32-element block share its scale byte.
 // Every reconstruction e2m1 * 2^(byte - 127) is exact in binary32 and in
 // bf16 (two significant bits; 2^-128 and up), so the bf16 output is the
-// binary32 result's top half.
+// binary32 result's top half. U chunks per thread have their loads in
+// flight together.
 template <bool BF16_OUT>
 __global__ __launch_bounds__(kThreads) void mx_dequantize_kernel(const uint8_t* __restrict__ codes,
                                                                 const uint8_t* __restrict__ scales,
-                                                                int64_t nblocks, void* __restrict__ out)
+                                                                int64_t nchunks, void* __restrict__ out)
 {
+    constexpr int E = BF16_OUT ? 8 : 4;
+    constexpr int U = 4;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
-        const uint4 c = load16(codes + 16 * b);
-        const uint32_t sb = scales[b];
-        const float X = sb == 0xFFu ? __uint_as_float(0x7FC00000u)
-                        : sb == 0u  ? __uint_as_float(0x00400000u)
-                                    : __uint_as_float(sb << 23);
-        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-        float v[32];
+    for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < nchunks; c0 += U * stride) {
+        uint32_t w[U], sb[U];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const auto g0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 0);
-            const auto g1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 1);
-            const auto g2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 2);
-            const auto g3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 3);
-            v[8 * q + 0] = g0[0] * X;
-            v[8 * q + 1] = g0[1] * X;
-            v[8 * q + 2] = g1[0] * X;
-            v[8 * q + 3] = g1[1] * X;
-            v[8 * q + 4] = g2[0] * X;
-            v[8 * q + 5] = g2[1] * X;
-            v[8 * q + 6] = g3[0] * X;
-            v[8 * q + 7] = g3[1] * X;
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + u * stride;
+            w[u] = 0u;
+            sb[u] = 0u;
+            if (c < nchunks) {
+                w[u] = BF16_OUT ? *reinterpret_cast<const uint32_t*>(codes + c * 4)
+                                : (uint32_t)*reinterpret_cast<const uint16_t*>(codes + c * 2);
+                sb[u] = scales[(c * E) >> 5];
+            }
         }
-        if (BF16_OUT) {
-            uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + 32 * b);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + u * stride;
+            if (c >= nchunks)
+                break;
+            const float X = sb[u] == 0xFFu ? __uint_as_float(0x7FC00000u)
+                            : sb[u] == 0u  ? __uint_as_float(0x00400000u)
+                                           : __uint_as_float(sb[u] << 23);
+            float v[E];
+#pragma unroll
+            for (int j = 0; j < E / 2; ++j) {
+                const auto g = j == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 0)
+                             : j == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 1)
+                             : j == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 2)
+                                      : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 3);
+                v[2 * j] = g[0] * X;
+                v[2 * j + 1] = g[1] * X;
+            }
+            if (BF16_OUT) {
                 uint32_t h[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    h[k] = (__float_as_uint(v[8 * q + 2 * k]) >> 16) |
-                           (__float_as_uint(v[8 * q + 2 * k + 1]) & 0xFFFF0000u);
-                o[q] = make_uint4(h[0], h[1], h[2], h[3]);
+                    h[k] = (__float_as_uint(v[2 * k]) >> 16) | (__float_as_uint(v[2 * k + 1]) & 0xFFFF0000u);
+                reinterpret_cast<uint4*>(out)[c] = make_uint4(h[0], h[1], h[2], h[3]);
+            } else {
+                reinterpret_cast<float4*>(out)[c] = make_float4(v[0], v[1], v[2], v[3]);
             }
-        } else {
-            float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + 32 * b);
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
         }
     }
 }
@@ -366,16 +372,17 @@ hipError_t launch_mx_quantize(const MxQuantizeArgs& a, hipStream_t stream)
 hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                                 void* out, bool bf16_out, hipStream_t stream)
 {
-    const int64_t nblocks = rows * (cols >> 5);
-    int64_t g = (nblocks + kThreads - 1) / kThreads;
+    // chunks of 8 (bf16) or 4 (binary32) elements; cols is a multiple of 32
+    const int64_t nchunks = rows * cols / (bf16_out ? 8 : 4);
+    int64_t g = (nchunks + 4 * kThreads - 1) / (4 * kThreads);
     if (g > 8192)
         g = 8192;
     if (bf16_out)
         hipLaunchKernelGGL(mx_dequantize_kernel<true>, dim3((unsigned)g), dim3(kThreads), 0, stream, codes,
-                           scales, nblocks, out);
+                           scales, nchunks, out);
     else
         hipLaunchKernelGGL(mx_dequantize_kernel<false>, dim3((unsigned)g), dim3(kThreads), 0, stream, codes,
-                           scales, nblocks, out);
+                           scales, nchunks, out);
     return hipGetLastError();
 }
 
