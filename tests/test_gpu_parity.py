@@ -574,6 +574,33 @@ def test_gemm_unaligned_scales_take_the_32_element_stages():
         assert np.linalg.norm(cc.astype(np.float64) - ref) / np.linalg.norm(ref) <= 1e-5
 
 
+def test_minimum_shape_16x16():
+    """The smallest tensor the 1D and 2D layouts take (one block per row and
+    column, one tile, one workgroup holding a fraction of a tile): every
+    path bit-identical to the oracle, and the 16 x 16 x 16 product within
+    1e-5 of the oracle's."""
+    x = W.normal_tensor(16, 16, seed=98)
+    for rowwise, colwise, sr, rht in ((True, True, False, False), (True, True, True, False),
+                                      (False, True, True, True)):
+        got, a = run_q1(x, rowwise, colwise, sr, rht)
+        check_q1(x, got, a, rowwise, colwise, sr, rht)
+    ws = F.nvfp4_workspace()
+    out = F.nvfp4_quantize_1d(dev(x), ws, rowwise=True, colwise=True, fused_amax=True)
+    got = {k: host(v) for k, v in out.items()}
+    check_q1(x, got, host(ws)[:1].view(np.float32)[0], True, True, False, False)
+    sg = oracle.global_scale(oracle.amax(x))
+    cr, cc, s2 = oracle.quantize_2d(x, sg)
+    q2 = F.nvfp4_quantize_2d(dev(x), F.nvfp4_amax(dev(x)))
+    assert np.array_equal(host(q2["codes_row"]), cr) and np.array_equal(host(q2["codes_col"]), cc)
+    assert np.array_equal(host(q2["scales"]), s2)
+    codes, scales = oracle.quantize_1d_rows(x, sg)
+    y = host(F.nvfp4_dequantize(to_gpu(codes), to_gpu(scales), 1, sg_gpu(sg), 16, 16))
+    assert np.array_equal(y.view(np.uint32), oracle.dequantize(codes, scales, 1, sg, 16, 16).view(np.uint32))
+    b = W.normal_tensor(16, 16, seed=99, std=0.02)
+    err, _ = gemm_check(x, b, np.arange(16))
+    assert err <= 1e-5
+
+
 def test_gemm_half_tiles_equal_whole_tiles():
     """A last round of at most half the grid runs as 256 x 128 half tiles:
     the 1024 x 2048 product (32 tiles, all halved) equals the same block of
