@@ -25,7 +25,9 @@
 //   - A 2D-scaled operand's tile scales (16 row groups x K/16 bytes) are
 //     staged in LDS once per tile with coalesced loads (transposed storage,
 //     NVFP4_SCALE_2D_T, transposed on the way in), so its rows fetch only
-//     codes per stage; K above kLdsScaleK falls back to per-row scale loads.
+//     codes per stage. The region holds kLdsScaleK bytes per operand, or
+//     twice that for a lone 2D operand; larger K falls back to per-row
+//     scale loads.
 //   - The grid is persistent (one workgroup per CU); a tile's output stores
 //     drain while the next tile starts. A last round that would occupy at
 //     most half the grid runs as a second launch of 256 x 128 half tiles
@@ -60,7 +62,7 @@ template <int KS>
 struct Geo {
     static constexpr int kRowBytes = KS * 2 + 16;
     static constexpr int kStageBytes = (kBM + kBN) * kRowBytes;
-    static constexpr int kLdsScaleK = KS == 32 ? 16384 : 4096;
+    static constexpr int kLdsScaleK = KS == 32 ? 16384 : 8192;
     static_assert(2 * kStageBytes + 2 * kLdsScaleK <= 160 * 1024, "LDS");
 };
 
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     constexpr int kLdsScaleK = Geo<KS>::kLdsScaleK;
     uint32_t cmax = 0u;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2][kLdsScaleK];  // A, B tile scales
+    __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2 * kLdsScaleK];  // A, B tile scales
 
     const int64_t K = g.K;
     const int t = threadIdx.x;
@@ -301,9 +303,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
     const float scale = (*g.a_sg) * (*g.b_sg);
     // 2D operands read their tile scales from LDS (K small enough, 16-byte
     // aligned scale arrays); the flags are uniform over the workgroup.
-    const bool a_stage = g.a_two_d && K <= kLdsScaleK && ((reinterpret_cast<uintptr_t>(g.a_scales) & 15) == 0);
-    const bool b_stage = g.b_two_d && K <= kLdsScaleK && ((reinterpret_cast<uintptr_t>(g.b_scales) & 15) == 0);
+    // Each takes half of the region, or all of it when it is the only one.
+    const bool a_al = g.a_two_d && ((reinterpret_cast<uintptr_t>(g.a_scales) & 15) == 0);
+    const bool b_al = g.b_two_d && ((reinterpret_cast<uintptr_t>(g.b_scales) & 15) == 0);
+    const bool a_stage = a_al && (K <= kLdsScaleK || (!b_al && K <= 2 * kLdsScaleK));
+    const bool b_stage = b_al && (K <= kLdsScaleK || (!a_al && K <= 2 * kLdsScaleK));
     const bool my_stage = is_b ? b_stage : a_stage;
+    uint8_t* const my_sc = lds_sc + (is_b && a_stage ? kLdsScaleK : 0);
     // Half tiles need 128 B rows: the last two waves fetch nothing.
     const bool loads = FN == 4 || !is_b || t - kBM < 64 * FN;
 
@@ -339,9 +345,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
         const int64_t bstride = !valid ? 0 : scales_t ? tile_rows : 1;
         const int64_t sstride = (KS / 16) * bstride;
         const int lt = is_b ? t - kBM : t;  // this thread's index among its operand's 256
-        const uint8_t* my_lds_scales = my_stage ? lds_sc[is_b ? 1 : 0] + (lt >> 4) * (K >> 4) : nullptr;
+        const uint8_t* my_lds_scales = my_stage ? my_sc + (lt >> 4) * (K >> 4) : nullptr;
         if (my_stage)
-            stage_tile_scales(lds_sc[is_b ? 1 : 0], scales, scales_t, (is_b ? n0 : m0) >> 4, tile_rows, K, lt);
+            stage_tile_scales(my_sc, scales, scales_t, (is_b ? n0 : m0) >> 4, tile_rows, K, lt);
         if (a_stage || b_stage)
             __syncthreads();
 
