@@ -538,3 +538,158 @@ def test_gemm_identity_operand():
     c = oracle.gemm_rows(a_codes, a_scales, 1, 1.0, cb, sb, 2, sgb, K, N, K, np.arange(K))
     bhat = oracle.dequantize_f64_rows(cb, sb, 2, sgb, N, K, np.arange(N))
     assert np.array_equal(c, bhat.T)
+
+
+# ------------------------------------- block scales and the reconstruction
+#
+# The block scale is the E4M3 value nearest to b / (6 S_g), b the block's
+# largest magnitude (page "Melatih model dalam 4 bit: pengaman numerik di
+# balik NVFP4", section "Anatomi NVFP4": S_g = amax / (448 * 6) and one E4M3
+# scale per 16 values; page "NVFP4 Is a Scaling System, Not Just a 4-Bit
+# Number", section "The smallest example": local scales come from block
+# maxima once the global scale is fixed). The tests below compute the block
+# maxima and the binary32 quotient with numpy and round it with torch's
+# float8_e4m3fn conversion (nearest even), never through the oracle.
+
+_E4M3_VALUES = (torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+                .to(torch.float32).numpy().astype(np.float64))
+
+
+def _torch_e4m3_bytes(q):
+    """E4M3 nearest-even bytes of non-negative binary32 values, saturating at
+    448 (torch's conversion returns NaN from 464 up)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    out = torch.from_numpy(np.minimum(q, np.float32(448.0))).to(torch.float8_e4m3fn)
+    return out.view(torch.uint8).numpy()
+
+
+def _expected_scale_bytes(block_max, sg):
+    t = np.float32(6.0) * np.float32(sg)  # one binary32 product
+    q = block_max.astype(np.float32) / t  # one binary32 division per block
+    return _torch_e4m3_bytes(q)
+
+
+def _block_max_rows(xf):
+    R, C = xf.shape
+    return np.abs(xf).reshape(R, C // 16, 16).max(axis=-1)
+
+
+@pytest.mark.parametrize("name,maker", [
+    ("round_trip", lambda: W.activation_small()),
+    ("activation", lambda: W.activation(256, 1024, seed=17)),
+    ("weight", lambda: W.weight(128, 512, seed=18)),
+    ("gradient", lambda: W.gradient(128, 1024, seed=19)),
+])
+def test_every_1d_block_scale_is_e4m3_rne_of_quotient(name, maker):
+    """Every rowwise and columnwise block, not only the amax block."""
+    x = maker()
+    xf = W.bf16_bits_to_f32(x)
+    a = np.float32(np.max(np.abs(xf)))
+    sg = np.float32(a / np.float32(2688.0))
+    assert oracle.amax(x) == a and oracle.global_scale(a) == sg
+    _, sr = oracle.quantize_1d_rows(x, sg)
+    assert np.array_equal(sr, _expected_scale_bytes(_block_max_rows(xf), sg))
+    _, sc = oracle.quantize_1d_cols(x, sg)
+    assert np.array_equal(sc, _expected_scale_bytes(_block_max_rows(np.ascontiguousarray(xf.T)), sg))
+    # the test is not vacuous: the blocks span many scale bytes
+    assert len(np.unique(sr)) > 15
+
+
+def test_every_2d_tile_scale_is_e4m3_rne_of_quotient():
+    x = W.weight(96, 160, seed=20)
+    xf = W.bf16_bits_to_f32(x)
+    sg = oracle.global_scale(oracle.amax(x))
+    _, _, s2 = oracle.quantize_2d(x, sg)
+    R, C = xf.shape
+    tmax = np.abs(xf).reshape(R // 16, 16, C // 16, 16).max(axis=(1, 3))
+    assert np.array_equal(s2, _expected_scale_bytes(tmax, sg))
+
+
+def test_transformed_block_scales_are_e4m3_rne_of_quotient():
+    """With the Hadamard transform the block maximum is taken over the
+    transformed values (the transform itself is pinned above)."""
+    x = W.gradient(64, 96, seed=22)
+    mask = W.rht_sign_mask()
+    y = oracle.rht16_tensor(x, 0, mask)
+    a = np.float32(np.max(np.abs(y)))
+    assert oracle.amax_rht(x, mask) == a
+    sg = np.float32(a / np.float32(2688.0))
+    _, sc = oracle.quantize_1d_cols(x, sg, rht=True, mask=mask)
+    assert np.array_equal(sc, _expected_scale_bytes(_block_max_rows(np.ascontiguousarray(y.T)), sg))
+
+
+def test_rne_block_scales_saturate_about_half_the_block_maxima():
+    """Consequence of nearest-even block scales: about half the blocks get a
+    scale below b / (6 S_g), and their largest element lies above 6 units and
+    saturates to 6. On N(0,1) data that is about 3.4 % of the elements. A
+    scale rounded up instead would leave no element above 6 units."""
+    x = W.normal_tensor(256, 2048, seed=21)
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    sg = oracle.global_scale(oracle.amax(x))
+    codes, scales = oracle.quantize_1d_rows(x, sg)
+    unit = _E4M3_VALUES[scales] * float(sg)  # exact in double
+    b = _block_max_rows(xf)
+    down = unit * 6 < b
+    assert 0.45 < down.mean() < 0.55
+    above = np.abs(xf) > 6 * np.repeat(unit, 16, axis=1)
+    assert 0.025 < above.mean() < 0.045
+    # saturation happens exactly in the blocks whose scale rounded down
+    assert np.array_equal(above.reshape(*b.shape, 16).any(axis=-1), down)
+    # and those elements carry magnitude code 7
+    q = _unpack(codes)
+    assert np.all(q[above] & 7 == 7)
+
+
+def test_element_codes_are_nearest_to_exact_ratio():
+    """Each element's magnitude code is a nearest grid value of the exact
+    ratio |x| / (s S_g) (ties to the even code), except where that ratio lies
+    within 2^-20 of a midpoint, where the binary32 reciprocal can decide the
+    side; such elements are rare."""
+    x = W.activation(512, 1024, seed=23)
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    sg = oracle.global_scale(oracle.amax(x))
+    codes, scales = oracle.quantize_1d_rows(x, sg)
+    unit = np.repeat(_E4M3_VALUES[scales], 16, axis=1) * float(sg)
+    ratio = np.abs(xf) / unit  # within 2^-52 relative of the exact ratio
+    grid = np.array([float(g) for g in GRID])
+    mids = (grid[1:] + grid[:-1]) / 2
+    near = np.min(np.abs(ratio[..., None] - mids), axis=-1) <= 2.0 ** -20 * np.maximum(ratio, 1)
+    # nearest grid index, ties (exact midpoints) to the even code
+    idx = np.searchsorted(mids, ratio, side="left")
+    at_mid = np.isin(ratio, mids)
+    idx = np.where(at_mid & (idx % 2 == 1), idx + 1, idx)
+    idx = np.minimum(idx, 7)
+    q = _unpack(codes) & 7
+    assert near.mean() < 1e-3
+    assert np.array_equal(q[~near], idx[~near])
+
+
+@pytest.mark.parametrize("sg", [np.float32(0.25), np.float32(1.0 / 3.0), np.float32(7.1e-5),
+                                np.float32(3.3e-41), np.float32(1.17e35)])
+def test_dequantize_every_code_and_scale_byte(sg):
+    """x^ = e2m1 * e4m3 * S_g ("NVFP4 Is a Scaling System", section "The
+    smallest example"). The product of a code (at most 2 significant bits)
+    and a scale (at most 4) with S_g (24) is exact in double, so one binary32
+    rounding of the double product is the correctly rounded result; the bf16
+    output is torch's nearest-even conversion of that binary32 value.
+    Codebook from the page fixture, scales from torch's E4M3 decode."""
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    C = 16
+    R = 16 * 256
+    codes = np.zeros((R, C // 2), np.uint8)
+    for k in range(16):  # every code in every 16-element row
+        codes[:, k // 2] |= np.uint8(k << (4 * (k % 2)))
+    scales = np.repeat(np.arange(256, dtype=np.uint8), 16).reshape(R, 1)
+    got = oracle.dequantize(codes, scales, 1, sg, R, C)
+    g = np.tile(np.concatenate([mags, -mags]), (R, 1))
+    want = (g * _E4M3_VALUES[scales] * np.float64(sg)).astype(np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+    gotb = oracle.dequantize_bf16(codes, scales, 1, sg, R, C)
+    wantb = torch.from_numpy(np.ascontiguousarray(want)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(gotb[~nan], wantb[~nan])
+    assert np.all((gotb[nan] & 0x7F80) == 0x7F80) and np.all((gotb[nan] & 0x7F) != 0)
+    # the bf16 rounding is exercised: many values are not bf16 already
+    finite = want[~nan]
+    assert np.count_nonzero(finite.view(np.uint32) & 0xFFFF) > 0 or sg == np.float32(0.25)
