@@ -318,7 +318,7 @@ def main():
     def step(k):
         x = xs[k % args.copies]
         o = outs[k % args.copies]
-        F.nvfp4_quantize_1d(x, ws, rowwise=True, colwise=True, out=o, fused_amax=True)
+        F.nvfp4_quantize_1d_fused(x, ws, rowwise=True, colwise=True, out=o)
 
     if args.calib_copy:
         # A plain copy of known size: reads and writes 256 MiB each. Hardware
@@ -409,10 +409,10 @@ def main():
         w0 = torch.cuda.Event(enable_timing=True)
         w1 = torch.cuda.Event(enable_timing=True)
         for _ in range(5):
-            F.nvfp4_quantize_1d(xs[0], ws, rowwise=True, colwise=True, out=outs[0], fused_amax=True)
+            F.nvfp4_quantize_1d_fused(xs[0], ws, rowwise=True, colwise=True, out=outs[0])
         w0.record(stream)
         for _ in range(50):
-            F.nvfp4_quantize_1d(xs[0], ws, rowwise=True, colwise=True, out=outs[0], fused_amax=True)
+            F.nvfp4_quantize_1d_fused(xs[0], ws, rowwise=True, colwise=True, out=outs[0])
         w1.record(stream)
         torch.cuda.synchronize()
         row_hbm("step_warm_one_input_copy", w0.elapsed_time(w1) / 50 * 1e3, step_bytes, [R, C],

@@ -5,8 +5,8 @@ ABI declared in include/nvfp4.h. PyTorch provides device memory (output
 tensors are allocated here with torch.empty) and the current stream. There
 is no fallback: if the library is missing, every call raises.
 
-Names follow the C ABI: nvfp4_amax, nvfp4_quantize_1d, nvfp4_quantize_2d,
-nvfp4_rht16, nvfp4_dequantize, nvfp4_gemm, nvfp4_status_string, and the
+Names follow the C ABI: nvfp4_amax, nvfp4_quantize_1d, nvfp4_quantize_1d_fused,
+nvfp4_quantize_2d, nvfp4_rht16, nvfp4_dequantize, nvfp4_gemm, nvfp4_status_string, and the
 MXFP4 comparator format's mxfp4_quantize, mxfp4_dequantize, mxfp4_gemm
 (include/mxfp4.h).
 """
@@ -21,7 +21,6 @@ ROWWISE = 0x1
 COLWISE = 0x2
 SR = 0x4
 RHT = 0x8
-FUSED_AMAX = 0x10
 AMAX_BOTH = 0x20
 WORKSPACE_BYTES = 32832
 SCALE_1D = 1
@@ -44,6 +43,7 @@ EXPORTS = (
     "nvfp4_status_string",
     "nvfp4_amax",
     "nvfp4_quantize_1d",
+    "nvfp4_quantize_1d_fused",
     "nvfp4_quantize_2d",
     "nvfp4_quantize_2d_tscales",
     "nvfp4_rht16",
@@ -84,6 +84,8 @@ def lib():
     L.nvfp4_amax.argtypes = [P, I64, I64, U32, U16, P, P]
     L.nvfp4_quantize_1d.restype = I
     L.nvfp4_quantize_1d.argtypes = [P, I64, I64, P, U32, U16, U64, P, P, P, P, P, P]
+    L.nvfp4_quantize_1d_fused.restype = I
+    L.nvfp4_quantize_1d_fused.argtypes = [P, I64, I64, U32, U64, P, P, P, P, P, P, P]
     L.nvfp4_quantize_2d.restype = I
     L.nvfp4_quantize_2d.argtypes = [P, I64, I64, P, P, P, P, P, P]
     L.nvfp4_quantize_2d_tscales.restype = I
@@ -179,29 +181,13 @@ def nvfp4_amax(x, rht: bool = False, rht_mask: int = 0, out=None, stream=None, b
 
 
 def nvfp4_workspace(device=None):
-    """A zero-filled workspace for nvfp4_quantize_1d(..., fused_amax=True)."""
+    """A zero-filled workspace for nvfp4_quantize_1d_fused."""
     torch = _torch()
     return torch.zeros(WORKSPACE_BYTES // 4, dtype=torch.int32, device=device or "cuda")
 
 
-def nvfp4_quantize_1d(x, amax, rowwise: bool = True, colwise: bool = False, sr: bool = False,
-                      rht: bool = False, rht_mask: int = 0, seed: int = 0, out: dict | None = None,
-                      stream=None, fused_amax: bool = False):
-    """1D NVFP4 quantization. Returns a dict with codes_row [R][C/2],
-    scales_row [R][C/16], codes_col [C][R/2], scales_col [C][R/16] (the
-    requested layouts) and global_scale (float32 [1]).
-
-    amax: float32 [1] from nvfp4_amax, or with fused_amax=True a workspace
-    from nvfp4_workspace() (the call computes the amax itself and leaves it
-    in the workspace's first float, readable as ws.view(torch.float32)[0])."""
+def _q1_outputs(x, rowwise, colwise, out):
     torch = _torch()
-    _bits16(x)
-    if fused_amax:
-        _dev_tensor(amax, "workspace")
-        if amax.numel() * amax.element_size() < WORKSPACE_BYTES:
-            raise ValueError(f"workspace must hold {WORKSPACE_BYTES} bytes")
-    else:
-        _dev_tensor(amax, "amax", torch.float32)
     R, C = x.shape
     out = dict(out or {})
     dev = x.device
@@ -212,10 +198,46 @@ def nvfp4_quantize_1d(x, amax, rowwise: bool = True, colwise: bool = False, sr: 
         out["codes_col"] = _empty((C, R // 2), torch.uint8, dev, out.get("codes_col"))
         out["scales_col"] = _empty((C, R // 16), torch.uint8, dev, out.get("scales_col"))
     out["global_scale"] = _empty((1,), torch.float32, dev, out.get("global_scale"))
+    return out
+
+
+def nvfp4_quantize_1d(x, amax, rowwise: bool = True, colwise: bool = False, sr: bool = False,
+                      rht: bool = False, rht_mask: int = 0, seed: int = 0, out: dict | None = None,
+                      stream=None):
+    """1D NVFP4 quantization with the amax given (float32 [1] from
+    nvfp4_amax). Returns a dict with codes_row [R][C/2], scales_row
+    [R][C/16], codes_col [C][R/2], scales_col [C][R/16] (the requested
+    layouts) and global_scale (float32 [1])."""
+    torch = _torch()
+    _bits16(x)
+    _dev_tensor(amax, "amax", torch.float32)
+    R, C = x.shape
+    out = _q1_outputs(x, rowwise, colwise, out)
     flags = ((ROWWISE if rowwise else 0) | (COLWISE if colwise else 0) | (SR if sr else 0)
-             | (RHT if rht else 0) | (FUSED_AMAX if fused_amax else 0))
+             | (RHT if rht else 0))
     _check(lib().nvfp4_quantize_1d(
         _ptr(x), R, C, _ptr(amax), flags, rht_mask & 0xFFFF, seed & ((1 << 64) - 1),
+        _ptr(out.get("codes_row")), _ptr(out.get("scales_row")),
+        _ptr(out.get("codes_col")), _ptr(out.get("scales_col")),
+        _ptr(out["global_scale"]), _stream(stream)))
+    return out
+
+
+def nvfp4_quantize_1d_fused(x, workspace, rowwise: bool = True, colwise: bool = False,
+                            sr: bool = False, seed: int = 0, out: dict | None = None, stream=None):
+    """1D NVFP4 quantization that finds the amax in the same call (one pass
+    over x when it fits on chip). workspace: from nvfp4_workspace(); the amax
+    lands in its first float (ws.view(torch.float32)[0]). Outputs as
+    nvfp4_quantize_1d."""
+    _bits16(x)
+    _dev_tensor(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < WORKSPACE_BYTES:
+        raise ValueError(f"workspace must hold {WORKSPACE_BYTES} bytes")
+    R, C = x.shape
+    out = _q1_outputs(x, rowwise, colwise, out)
+    flags = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0) | (SR if sr else 0)
+    _check(lib().nvfp4_quantize_1d_fused(
+        _ptr(x), R, C, flags, seed & ((1 << 64) - 1), _ptr(workspace),
         _ptr(out.get("codes_row")), _ptr(out.get("scales_row")),
         _ptr(out.get("codes_col")), _ptr(out.get("scales_col")),
         _ptr(out["global_scale"]), _stream(stream)))

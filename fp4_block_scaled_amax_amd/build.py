@@ -46,15 +46,36 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES]
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompiles; writes the library atomically."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-o", tmp, *sources()]
+OBJ_DIR = os.path.join(HERE, "_build")
+
+
+def _run(cmd, verbose):
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + proc.stdout + proc.stderr)
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + proc.stdout + proc.stderr)
     if verbose:
         print(" ".join(cmd))
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles (one hipcc per source, in parallel, then one link);
+    writes the library atomically."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f not in ("-shared",) and not f.startswith("-Wl,")]
+    objs, cmds = [], []
+    for src in sources():
+        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmds.append([hipcc(), *compile_flags, "-c", "-o", obj, src])
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-rpath,/opt/rocm/lib", "-o", tmp,
+          *objs], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -74,10 +74,8 @@ int nvfp4_quantize_1d(const uint16_t* x, int64_t rows, int64_t cols, const float
                       uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                       float* global_scale, hipStream_t stream)
 {
-    const uint32_t known = NVFP4_ROWWISE | NVFP4_COLWISE | NVFP4_SR | NVFP4_RHT | NVFP4_FUSED_AMAX;
+    const uint32_t known = NVFP4_ROWWISE | NVFP4_COLWISE | NVFP4_SR | NVFP4_RHT;
     if ((flags & ~known) != 0 || (flags & (NVFP4_ROWWISE | NVFP4_COLWISE)) == 0)
-        return NVFP4_ERR_FLAGS;
-    if ((flags & NVFP4_FUSED_AMAX) && (flags & NVFP4_RHT))
         return NVFP4_ERR_FLAGS;
     if ((flags & NVFP4_RHT) && ((flags & NVFP4_ROWWISE) || !(flags & NVFP4_COLWISE)))
         return NVFP4_ERR_FLAGS;
@@ -93,12 +91,9 @@ int nvfp4_quantize_1d(const uint16_t* x, int64_t rows, int64_t cols, const float
     if (!dims_ok(rows, cols) || rows / 256 >= (1 << 20) || cols / 256 >= (1 << 20))
         return NVFP4_ERR_SIZE;
     if (!aligned16(x) || (row && (!aligned16(codes_row) || !aligned16(scales_row))) ||
-        (col && (!aligned16(codes_col) || !aligned16(scales_col))) ||
-        ((flags & NVFP4_FUSED_AMAX) && !aligned16(amax)))
+        (col && (!aligned16(codes_col) || !aligned16(scales_col))))
         return NVFP4_ERR_ALIGN;
     nvfp4::QuantizeArgs a{};
-    a.fused_amax = (flags & NVFP4_FUSED_AMAX) != 0;
-    a.workspace = a.fused_amax ? reinterpret_cast<uint32_t*>(const_cast<float*>(amax)) : nullptr;
     a.x = x;
     a.rows = rows;
     a.cols = cols;
@@ -119,6 +114,42 @@ int nvfp4_quantize_1d(const uint16_t* x, int64_t rows, int64_t cols, const float
 }
 
 namespace {
+
+// Validation shared by the fused entry points; `a` receives the arguments.
+int fused_args(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
+               uint8_t* codes_row, uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+               float* global_scale, nvfp4::QuantizeArgs& a)
+{
+    const uint32_t known = NVFP4_ROWWISE | NVFP4_COLWISE | NVFP4_SR;
+    if ((flags & ~known) != 0 || (flags & (NVFP4_ROWWISE | NVFP4_COLWISE)) == 0)
+        return NVFP4_ERR_FLAGS;
+    const bool row = (flags & NVFP4_ROWWISE) != 0, col = (flags & NVFP4_COLWISE) != 0;
+    if (x == nullptr || (row && (codes_row == nullptr || scales_row == nullptr)) ||
+        (col && (codes_col == nullptr || scales_col == nullptr)))
+        return NVFP4_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || rows % 16 != 0 || cols % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!dims_ok(rows, cols) || rows / 256 >= (1 << 20) || cols / 256 >= (1 << 20))
+        return NVFP4_ERR_SIZE;
+    if (!aligned16(x) || (row && (!aligned16(codes_row) || !aligned16(scales_row))) ||
+        (col && (!aligned16(codes_col) || !aligned16(scales_col))))
+        return NVFP4_ERR_ALIGN;
+    a = nvfp4::QuantizeArgs{};
+    a.fused_amax = true;
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.seed = seed;
+    a.rowwise = row;
+    a.colwise = col;
+    a.sr = (flags & NVFP4_SR) != 0;
+    a.codes_row = codes_row;
+    a.scales_row = scales_row;
+    a.codes_col = codes_col;
+    a.scales_col = scales_col;
+    a.global_scale = global_scale;
+    return NVFP4_OK;
+}
 
 int quantize_2d_common(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
                        uint8_t* codes_row, uint8_t* codes_col, uint8_t* scales, uint8_t* scales_t,
@@ -151,6 +182,24 @@ int quantize_2d_common(const uint16_t* x, int64_t rows, int64_t cols, const floa
 }
 
 }  // namespace
+
+int nvfp4_quantize_1d_fused(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
+                            uint64_t seed, void* workspace, uint8_t* codes_row,
+                            uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                            float* global_scale, hipStream_t stream)
+{
+    nvfp4::QuantizeArgs a;
+    const int st = fused_args(x, rows, cols, flags, seed, codes_row, scales_row, codes_col, scales_col,
+                              global_scale, a);
+    if (st != NVFP4_OK)
+        return st;
+    if (workspace == nullptr)
+        return NVFP4_ERR_NULL;
+    if (!aligned16(workspace))
+        return NVFP4_ERR_ALIGN;
+    a.workspace = static_cast<uint32_t*>(workspace);
+    return status_of(nvfp4::launch_quantize(a, stream));
+}
 
 int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
                       uint8_t* codes_row, uint8_t* codes_col, uint8_t* scales,

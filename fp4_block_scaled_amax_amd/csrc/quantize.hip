@@ -677,10 +677,20 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
 // Workspace (32-bit words): [0] amax bits, [1] generation of the last
 // completed call, [2] slow-path counter, [3] wait limit in ticks of the
 // 100 MHz counter (0: the default; a tiny value makes every wait expire, so
-// tests can drive the fallback), then 2 words per workgroup of arrival
-// slots and 2 words per workgroup of release slots.
+// tests can drive the fallback), [4] count of this call's workgroups that
+// have read the generation, then 2 words per workgroup of arrival slots and
+// 2 words per workgroup of release slots.
+//
+// The generation advances only once every workgroup of the call has read
+// it: each workgroup counts itself in word 4 after its arrival post (whose
+// value depends on the generation it read), and the workgroup that brings
+// the count to the grid size resets the count and stores the new
+// generation. Advancing it any earlier (say when workgroup 0 gives up
+// waiting) would let a workgroup of the same call that starts later read
+// the next call's generation and post a stale maximum under it, which the
+// next call's workgroup 0 could take for a fresh one.
 
-constexpr int kWsAmax = 0, kWsGen = 1, kWsSlow = 2, kWsWait = 3, kWsArrive = 16;
+constexpr int kWsAmax = 0, kWsGen = 1, kWsSlow = 2, kWsWait = 3, kWsExit = 4, kWsArrive = 16;
 constexpr int kMaxFusedBlocks = 2048;                       // slots in the workspace
 constexpr int kWsRelease = kWsArrive + 2 * kMaxFusedBlocks;
 constexpr int kMaxFusedGrid = 1024;                         // largest grid launched
@@ -743,7 +753,7 @@ __device__ uint32_t direct_amax(const Params& p, uint32_t* red)
 
 // This call's generation: one more than the last completed call's. Read at
 // the start of the kernel, off the exchange's critical path (the word only
-// changes once every workgroup of this call has posted its arrival).
+// changes once every workgroup of this call has read it).
 __device__ __forceinline__ uint32_t call_generation(const uint32_t* ws)
 {
     return ws_load(&ws[kWsGen]) + 1u;
@@ -752,8 +762,11 @@ __device__ __forceinline__ uint32_t call_generation(const uint32_t* ws)
 // Grid-wide maximum of one value per workgroup (binary32 bits); every
 // workgroup returns the same result. gen0 and wait0 (workspace word 3: the
 // bound on each wait in 100 MHz ticks, 0 for the default) are read by
-// thread 0 at the start of the kernel.
-__device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t* ws, const Params& p)
+// thread 0 at the start of the kernel. Thread 0 also receives in
+// `read_rank` how many workgroups of the call had counted themselves in
+// word 4 before this one (see release_generation).
+__device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t* ws, const Params& p,
+                             uint32_t& read_rank)
 {
     __shared__ uint32_t red[kThreads / 64];
     __shared__ uint32_t gen_s, wait_s, result_s, ok_s;
@@ -762,6 +775,10 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
         gen_s = gen0;
         wait_s = wait0;
         slot_store(&ws[kWsArrive + 2 * blockIdx.x], gen0, m);
+        // The store above carries gen0, so the generation word has been read
+        // by the time this count is made. The result is used only at the end
+        // of the kernel.
+        read_rank = __hip_atomic_fetch_add(&ws[kWsExit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     const uint32_t gen = gen_s;
@@ -819,9 +836,6 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
         }
         for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads)
             slot_store(&ws[kWsRelease + 2 * i], gen, amax);
-        __syncthreads();
-        if (threadIdx.x == 0)
-            ws_store(&ws[kWsGen], gen);
         return amax;
     }
     if (threadIdx.x == 0) {
@@ -845,6 +859,18 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
         return amax;
     }
     return result_s;
+}
+
+// Called by thread 0 of every workgroup at the end of the kernel: the
+// workgroup that was the last to count itself (every other one has read the
+// generation by then) resets the count and publishes this call's generation
+// as the last completed one.
+__device__ __forceinline__ void release_generation(uint32_t* ws, uint32_t gen, uint32_t read_rank)
+{
+    if (read_rank == gridDim.x - 1u) {
+        ws_store(&ws[kWsExit], 0u);
+        ws_store(&ws[kWsGen], gen);
+    }
 }
 
 // Write the staged columnwise output of two vertically adjacent tiles (A at
@@ -945,7 +971,9 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
             row_maxima(vb, qb.odd, bb);
         m = max(m, item_max(bb));
     }
-    const uint32_t amax_bits = p.amax_given ? __float_as_uint(*p.amax) : grid_max(m, gen, wait, ws, p);
+    uint32_t read_rank = 0u;
+    const uint32_t amax_bits =
+        p.amax_given ? __float_as_uint(*p.amax) : grid_max(m, gen, wait, ws, p, read_rank);
 
     const ScaleCtx sc = scale_ctx(__uint_as_float(amax_bits));
     if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
@@ -967,6 +995,8 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
         __syncthreads();
         write_col_pair(p, qa.tile_r0, qa.tile_c0, lds_codes[0], lds_codes[1], lds_scales[0], lds_scales[1]);
     }
+    if (!p.amax_given && threadIdx.x == 0)
+        release_generation(ws, gen, read_rank);
 }
 
 // Workgroups of one fused kernel that fit on the device at once (cached).

@@ -32,7 +32,7 @@ bf16 bit patterns (int16/uint16 tensors), every dimension a multiple of 16.
 from __future__ import annotations
 
 from . import (SCALE_1D, SCALE_2D, SCALE_2D_T, _torch, nvfp4_amax, nvfp4_gemm,
-               nvfp4_quantize_1d, nvfp4_quantize_2d, nvfp4_workspace)
+               nvfp4_quantize_1d, nvfp4_quantize_1d_fused, nvfp4_quantize_2d, nvfp4_workspace)
 
 
 def quantize_weight(w, stream=None) -> dict:
@@ -49,7 +49,7 @@ def fprop(x, wq: dict, ws=None, out_dtype=None, stream=None):
     tokens, k = x.shape
     n = wq["codes_row"].shape[0]
     ws = nvfp4_workspace(x.device) if ws is None else ws
-    xq = nvfp4_quantize_1d(x, ws, rowwise=True, fused_amax=True, stream=stream)
+    xq = nvfp4_quantize_1d_fused(x, ws, rowwise=True, stream=stream)
     return nvfp4_gemm(xq["codes_row"], xq["scales_row"], SCALE_1D, xq["global_scale"],
                       wq["codes_row"], wq["scales"], SCALE_2D, wq["global_scale"],
                       tokens, n, k, out_dtype=out_dtype, stream=stream)
@@ -64,7 +64,7 @@ def forward_quantized(x, wq: dict, ws=None, stream=None):
     tokens, k = x.shape
     n = wq["codes_row"].shape[0]
     ws = nvfp4_workspace(x.device) if ws is None else ws
-    xq = nvfp4_quantize_1d(x, ws, rowwise=True, fused_amax=True, stream=stream)
+    xq = nvfp4_quantize_1d_fused(x, ws, rowwise=True, stream=stream)
     y_amax = torch.empty(1, dtype=torch.float32, device=x.device)
     y = nvfp4_gemm(xq["codes_row"], xq["scales_row"], SCALE_1D, xq["global_scale"],
                    wq["codes_row"], wq["scales"], SCALE_2D, wq["global_scale"],
@@ -91,8 +91,7 @@ def dgrad(dy, wq: dict, seed: int, ws=None, out_dtype=None, stream=None, dy_amax
         dyq = nvfp4_quantize_1d(dy, dy_amax, rowwise=True, sr=True, seed=seed, stream=stream)
     else:
         ws = nvfp4_workspace(dy.device) if ws is None else ws
-        dyq = nvfp4_quantize_1d(dy, ws, rowwise=True, sr=True, seed=seed, fused_amax=True,
-                                stream=stream)
+        dyq = nvfp4_quantize_1d_fused(dy, ws, rowwise=True, sr=True, seed=seed, stream=stream)
     if "scales_t" in wq:
         b_scales, b_mode = wq["scales_t"], SCALE_2D
     else:

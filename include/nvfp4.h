@@ -13,8 +13,10 @@
  *  - Tensors are row-major [rows][cols] with cols contiguous. bf16 inputs
  *    are passed as their 16-bit patterns.
  *  - All pointers are DEVICE pointers (hipMalloc / torch CUDA tensors)
- *    owned by the caller. The library allocates nothing, keeps no state
- *    between calls and is safe to call from several host threads.
+ *    owned by the caller. The library allocates nothing and is safe to
+ *    call from several host threads. Between calls it keeps only facts
+ *    about the device (how many workgroups of a kernel fit at once, looked
+ *    up on first use per device); results never depend on earlier calls.
  *  - Every call is asynchronous on `stream` (0 = the null stream) and never
  *    synchronises the host. Outputs are valid once the stream reaches them.
  *  - Arguments are validated before any HIP call; a failed check returns a
@@ -54,10 +56,9 @@ extern "C" {
 #define NVFP4_COLWISE 0x2u /* blocks of 16 consecutive rows of one column   */
 #define NVFP4_SR 0x4u      /* stochastic rounding (gradients) instead of RNE */
 #define NVFP4_RHT 0x8u     /* random-sign 16-point Hadamard along rows first */
-#define NVFP4_FUSED_AMAX 0x10u /* compute the amax inside nvfp4_quantize_1d  */
 #define NVFP4_AMAX_BOTH 0x20u  /* nvfp4_amax with NVFP4_RHT: plain amax too    */
 
-/* Size of the workspace nvfp4_quantize_1d takes with NVFP4_FUSED_AMAX. */
+/* Size of the workspace nvfp4_quantize_1d_fused takes. */
 #define NVFP4_WORKSPACE_BYTES 32832
 
 /* scale_mode values */
@@ -122,25 +123,38 @@ int nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags, ui
  * Per block: s = e4m3_rne(b / (6*S_g)) with b the block's max |x| (after
  * the transform with NVFP4_RHT); each element is |x| * (1 / (s*S_g))
  * rounded to E2M1 (ties to even, saturating at 6) or stochastically.
- *
- * NVFP4_FUSED_AMAX (not with NVFP4_RHT): the call computes the tensor amax
- * itself, in the same pass over x when the tensor fits on chip (the data
- * stays in registers between the amax and the encoding, so x is read from
- * memory once). `amax` then points to a caller-owned device workspace of
- * NVFP4_WORKSPACE_BYTES bytes, zero-filled before its first use and reused
- * as is afterwards; its first float receives the amax (exactly what
- * nvfp4_amax would give). The single pass needs all of its workgroups on
- * the device at once; if they are not (another kernel holds the device),
- * a bounded wait expires, the amax is computed from x directly (same
- * result, slower) and 32-bit word 2 of the workspace is incremented. Word 3
- * sets that wait in ticks of the 100 MHz real-time counter (0, as after
- * zero-filling: 2 ms; a tiny value forces the direct computation, for
- * tests). Calls that overlap in time must use different workspaces.
  */
 int nvfp4_quantize_1d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
                       uint32_t flags, uint16_t rht_mask, uint64_t seed, uint8_t* codes_row,
                       uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                       float* global_scale, hipStream_t stream);
+
+/*
+ * nvfp4_quantize_1d_fused -- nvfp4_quantize_1d that finds the tensor amax
+ * itself (page "Melatih model dalam 4 bit", section "Anatomi NVFP4": the
+ * global scale comes from the tensor amax), in the same pass over x when
+ * the tensor fits on chip: the data stays in registers between the amax and
+ * the encoding, so x is read from memory once. Larger tensors take two
+ * passes (amax, then quantize) inside the same call.
+ *   flags      NVFP4_ROWWISE and/or NVFP4_COLWISE, optionally NVFP4_SR (no
+ *              NVFP4_RHT: the transformed operand's amax is nvfp4_amax's).
+ *   workspace  caller-owned device memory of NVFP4_WORKSPACE_BYTES bytes,
+ *              16-byte aligned, zero-filled before its first use and then
+ *              reused as is (each call leaves it ready for the next). Its
+ *              first float receives the amax (what nvfp4_amax would give).
+ *   Other arguments and the outputs as nvfp4_quantize_1d.
+ * The single pass needs all of its workgroups on the device at once; if
+ * they are not (another kernel holds the device), a bounded wait expires,
+ * the amax is computed from x directly (same result, slower) and 32-bit
+ * word 2 of the workspace is incremented. Word 3 sets that wait in ticks of
+ * the 100 MHz real-time counter (0, as after zero-filling: 2 ms; a tiny
+ * value forces the direct computation, for tests). Calls that overlap in
+ * time must use different workspaces.
+ */
+int nvfp4_quantize_1d_fused(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
+                            uint64_t seed, void* workspace, uint8_t* codes_row,
+                            uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                            float* global_scale, hipStream_t stream);
 
 /*
  * nvfp4_quantize_2d -- weight quantization with one E4M3 scale per 16x16

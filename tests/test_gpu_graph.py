@@ -49,7 +49,7 @@ def test_replays_equal_eager():
     c_amax = torch.empty(1, dtype=torch.float32, device="cuda")
 
     def work():
-        q = F.nvfp4_quantize_1d(x, ws, rowwise=True, colwise=True, fused_amax=True)
+        q = F.nvfp4_quantize_1d_fused(x, ws, rowwise=True, colwise=True)
         F.nvfp4_amax(g, rht=True, rht_mask=mask, out=ga)
         qg = F.nvfp4_quantize_1d(g, ga, rowwise=False, colwise=True, sr=True, rht=True, rht_mask=mask,
                                  seed=SEED)
@@ -78,5 +78,5 @@ def test_replays_equal_eager():
         for i, (a, e) in enumerate(zip(got, eager)):
             assert torch.equal(a.view(torch.uint8), e.view(torch.uint8)), f"replay {rep}, output {i}"
         # eager work of the program between replays
-        F.nvfp4_quantize_1d(x, ws, rowwise=True, colwise=False, fused_amax=True)
+        F.nvfp4_quantize_1d_fused(x, ws, rowwise=True, colwise=False)
         torch.cuda.synchronize()

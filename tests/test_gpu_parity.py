@@ -294,8 +294,7 @@ def test_scale_bytes_near_rounding_midpoints(layouts, fused):
     x = straddle_tensor(128, 512, 31)
     log(f"[test_scale_bytes_near_rounding_midpoints] {layouts} fused={fused}")
     if fused:
-        out = F.nvfp4_quantize_1d(dev(x), F.nvfp4_workspace(), rowwise=rowwise, colwise=colwise,
-                                  fused_amax=True)
+        out = F.nvfp4_quantize_1d_fused(dev(x), F.nvfp4_workspace(), rowwise=rowwise, colwise=colwise)
         torch.cuda.synchronize()
         got = {k: host(v) for k, v in out.items()}
         a = np.float32(oracle.amax(x))
@@ -585,7 +584,7 @@ def test_minimum_shape_16x16():
         got, a = run_q1(x, rowwise, colwise, sr, rht)
         check_q1(x, got, a, rowwise, colwise, sr, rht)
     ws = F.nvfp4_workspace()
-    out = F.nvfp4_quantize_1d(dev(x), ws, rowwise=True, colwise=True, fused_amax=True)
+    out = F.nvfp4_quantize_1d_fused(dev(x), ws, rowwise=True, colwise=True)
     got = {k: host(v) for k, v in out.items()}
     check_q1(x, got, host(ws)[:1].view(np.float32)[0], True, True, False, False)
     sg = oracle.global_scale(oracle.amax(x))
@@ -647,11 +646,13 @@ def test_fused_amax_quantize(name, sr, layouts):
     ws = F.nvfp4_workspace()
     got = None
     for rep in range(2):  # the workspace is reused as is
-        out = F.nvfp4_quantize_1d(xd, ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED, fused_amax=True)
+        out = F.nvfp4_quantize_1d_fused(xd, ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED)
         torch.cuda.synchronize()
         got = {k: host(v) for k, v in out.items()}
         wsh = host(ws)
         assert wsh[2] == 0, "in-kernel exchange fell back to the slow path"
+        if x.size <= (1 << 25):  # single pass: one generation per call, read count back at 0
+            assert wsh[1] == rep + 1 and wsh[4] == 0, (wsh[1], wsh[4])
         amax_gpu = wsh[:1].view(np.float32)[0]
         check_q1(x, got, amax_gpu, rowwise, colwise, sr, False,
                  rows=None if x.shape[0] <= 512 else sample_idx(x.shape[0], 16, 7 + rep),
@@ -674,7 +675,7 @@ def test_fused_exchange_fallback_forced(sr, layouts):
     xd = dev(x)
     ws = F.nvfp4_workspace()
     ws[3] = 1
-    out = F.nvfp4_quantize_1d(xd, ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED, fused_amax=True)
+    out = F.nvfp4_quantize_1d_fused(xd, ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED)
     torch.cuda.synchronize()
     wsh = host(ws)
     assert wsh[2] > 0, "no workgroup took the direct amax"
@@ -682,7 +683,7 @@ def test_fused_exchange_fallback_forced(sr, layouts):
     check_q1(x, got, wsh[:1].view(np.float32)[0], rowwise, colwise, sr, False)
     slow = int(wsh[2])
     ws[3] = 0
-    out = F.nvfp4_quantize_1d(xd, ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED, fused_amax=True)
+    out = F.nvfp4_quantize_1d_fused(xd, ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED)
     torch.cuda.synchronize()
     wsh = host(ws)
     assert int(wsh[2]) == slow, "the exchange fell back again with the default wait"
@@ -691,12 +692,44 @@ def test_fused_exchange_fallback_forced(sr, layouts):
         assert np.array_equal(got[k], got2[k]), k
 
 
+@pytest.mark.parametrize("sr,layouts", [(False, (True, True)), (True, (True, True)), (False, (True, False)),
+                                       (True, (False, True))])
+def test_fused_fallback_then_smaller_tensor(sr, layouts):
+    """A call whose exchange waits all expire (word 3 = one tick) on a tensor
+    with a large amax, then a normal call on another tensor with a much
+    smaller amax through the same workspace. The generation advances only
+    after every workgroup of a call has read it, so no workgroup of the
+    first call can post its maximum under the second call's generation: the
+    second call's amax and every code and scale byte are the oracle's for
+    its own tensor. The generation word moves by one per call and the count
+    of workgroups that have read it is back at 0 after each."""
+    rowwise, colwise = layouts
+    log(f"[test_fused_fallback_then_smaller_tensor] sr={sr} layouts={layouts}")
+    big = W.f32_to_bf16_bits(W.bf16_bits_to_f32(W.activation(1024, 1280, seed=31)) * np.float32(1e4))
+    small = W.activation(1024, 1280, seed=32)
+    ws = F.nvfp4_workspace()
+    ws[3] = 1
+    out = F.nvfp4_quantize_1d_fused(dev(big), ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED)
+    wsh = host(ws)
+    assert wsh[2] > 0, "no workgroup took the direct amax"
+    assert wsh[1] == 1 and wsh[4] == 0, (wsh[1], wsh[4])
+    check_q1(big, {k: host(v) for k, v in out.items()}, wsh[:1].view(np.float32)[0], rowwise, colwise, sr,
+             False)
+    ws[3] = 0
+    out = F.nvfp4_quantize_1d_fused(dev(small), ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED)
+    wsh = host(ws)
+    assert wsh[1] == 2 and wsh[4] == 0, (wsh[1], wsh[4])
+    a = wsh[:1].view(np.float32)[0]
+    assert f32_bits(a) == f32_bits(oracle.amax(small))
+    check_q1(small, {k: host(v) for k, v in out.items()}, a, rowwise, colwise, sr, False)
+
+
 def test_fused_workspace_across_tensors():
     """Consecutive fused calls on different tensors through one workspace."""
     ws = F.nvfp4_workspace()
     for seed, scale in ((21, 1.0), (22, 1e-3), (23, 300.0)):
         x = W.f32_to_bf16_bits(W.bf16_bits_to_f32(W.activation(640, 768, seed=seed)) * np.float32(scale))
-        out = F.nvfp4_quantize_1d(dev(x), ws, rowwise=True, colwise=True, fused_amax=True)
+        out = F.nvfp4_quantize_1d_fused(dev(x), ws, rowwise=True, colwise=True)
         torch.cuda.synchronize()
         got = {k: host(v) for k, v in out.items()}
         check_q1(x, got, host(ws)[:1].view(np.float32)[0], True, True, False, False)

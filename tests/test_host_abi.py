@@ -84,6 +84,27 @@ def test_quantize_1d_validation(L):
     assert q1(L, rows=1 << 40, cols=1 << 40) == -6
 
 
+def q1f(L, x=A, rows=64, cols=64, flags=F.ROWWISE, ws=A, cr=A, sr_=A, cc=A, sc=A):
+    return L.nvfp4_quantize_1d_fused(x, rows, cols, flags, 0, ws, cr, sr_, cc, sc, NULL, NULL)
+
+
+def test_quantize_1d_fused_validation(L):
+    assert q1f(L, flags=0) == -4
+    assert q1f(L, flags=F.ROWWISE | F.RHT) == -4  # the transform's amax is nvfp4_amax's
+    assert q1f(L, flags=F.COLWISE | F.RHT) == -4
+    assert q1f(L, flags=F.ROWWISE | 0x10) == -4  # unknown flag
+    assert q1f(L, x=NULL) == -1
+    assert q1f(L, ws=NULL) == -1
+    assert q1f(L, cr=NULL) == -1
+    assert q1f(L, flags=F.COLWISE, sc=NULL) == -1
+    assert q1f(L, rows=24) == -2
+    assert q1f(L, x=MIS) == -3
+    assert q1f(L, ws=MIS) == -3
+    assert q1f(L, rows=1 << 40, cols=1 << 40) == -6
+    # nvfp4_quantize_1d itself no longer takes a workspace flag
+    assert q1(L, flags=F.ROWWISE | 0x10) == -4
+
+
 def test_quantize_2d_validation(L):
     assert L.nvfp4_quantize_2d(A, 32, 32, A, NULL, NULL, A, NULL, NULL) == -1
     assert L.nvfp4_quantize_2d(A, 32, 32, A, A, A, NULL, NULL, NULL) == -1
