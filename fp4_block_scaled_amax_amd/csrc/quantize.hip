@@ -677,20 +677,30 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
 // Workspace (32-bit words): [0] amax bits, [1] generation of the last
 // completed call, [2] slow-path counter, [3] wait limit in ticks of the
 // 100 MHz counter (0: the default; a tiny value makes every wait expire, so
-// tests can drive the fallback), [4] count of this call's workgroups that
-// have read the generation, then 2 words per workgroup of arrival slots and
-// 2 words per workgroup of release slots.
+// tests can drive the fallback), [4..5] (generation tag, count) of the
+// workgroups that went through an expired exchange, then 2 words per
+// workgroup of arrival slots and 2 words per workgroup of release slots.
 //
-// The generation advances only once every workgroup of the call has read
-// it: each workgroup counts itself in word 4 after its arrival post (whose
-// value depends on the generation it read), and the workgroup that brings
-// the count to the grid size resets the count and stores the new
-// generation. Advancing it any earlier (say when workgroup 0 gives up
-// waiting) would let a workgroup of the same call that starts later read
-// the next call's generation and post a stale maximum under it, which the
-// next call's workgroup 0 could take for a fresh one.
+// The generation may advance only once every workgroup of the call has read
+// it; advancing it earlier would let a workgroup of the same call that
+// starts later read the next call's generation and post a stale maximum
+// under it, which the next call's workgroup 0 could take for a fresh one.
+//  - When workgroup 0 collects every arrival, each arrival carries the
+//    generation its workgroup read, so all have read it: workgroup 0 stores
+//    the generation right after posting the releases (no atomic operation).
+//  - When workgroup 0's wait expires, some workgroups may not have started.
+//    Workgroup 0 then flags its releases (bit 31 of the posted amax, which an
+//    amax never has), and every workgroup of the call counts itself in words
+//    4..5 under the call's generation as a tag: workgroup 0, every workgroup
+//    that receives a flagged release, and every workgroup whose own wait
+//    expires. Each counts after reading the generation, and the one whose
+//    count reaches the grid size stores the generation. (A workgroup whose
+//    own wait expired in a call where workgroup 0 collected everything
+//    counts too, under that call's tag; no later call shares the tag, and
+//    workgroup 0 has already stored the generation.)
 
-constexpr int kWsAmax = 0, kWsGen = 1, kWsSlow = 2, kWsWait = 3, kWsExit = 4, kWsArrive = 16;
+constexpr int kWsAmax = 0, kWsGen = 1, kWsSlow = 2, kWsWait = 3, kWsExpired = 4, kWsArrive = 16;
+constexpr uint32_t kExpiredFlag = 0x80000000u;
 constexpr int kMaxFusedBlocks = 2048;                       // slots in the workspace
 constexpr int kWsRelease = kWsArrive + 2 * kMaxFusedBlocks;
 constexpr int kMaxFusedGrid = 1024;                         // largest grid launched
@@ -754,6 +764,26 @@ __device__ uint32_t direct_amax(const Params& p, uint32_t* red)
 // This call's generation: one more than the last completed call's. Read at
 // the start of the kernel, off the exchange's critical path (the word only
 // changes once every workgroup of this call has read it).
+
+// A workgroup of a call whose exchange expired counts itself under the
+// call's generation; the count that reaches the grid size publishes it.
+// Only reached when a wait has expired, so the compare-and-swap loop is off
+// every common path; each retry means another workgroup's count went in.
+__device__ void count_expired(uint32_t* ws, uint32_t gen)
+{
+    uint64_t* word = reinterpret_cast<uint64_t*>(&ws[kWsExpired]);
+    uint64_t seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const uint32_t n = ((uint32_t)seen == gen) ? (uint32_t)(seen >> 32) + 1u : 1u;
+        const uint64_t want = ((uint64_t)n << 32) | gen;
+        if (__hip_atomic_compare_exchange_weak(word, &seen, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)) {
+            if (n == gridDim.x)
+                ws_store(&ws[kWsGen], gen);
+            return;
+        }
+    }
+}
 __device__ __forceinline__ uint32_t call_generation(const uint32_t* ws)
 {
     return ws_load(&ws[kWsGen]) + 1u;
@@ -762,11 +792,8 @@ __device__ __forceinline__ uint32_t call_generation(const uint32_t* ws)
 // Grid-wide maximum of one value per workgroup (binary32 bits); every
 // workgroup returns the same result. gen0 and wait0 (workspace word 3: the
 // bound on each wait in 100 MHz ticks, 0 for the default) are read by
-// thread 0 at the start of the kernel. Thread 0 also receives in
-// `read_rank` how many workgroups of the call had counted themselves in
-// word 4 before this one (see release_generation).
-__device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t* ws, const Params& p,
-                             uint32_t& read_rank)
+// thread 0 at the start of the kernel.
+__device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t* ws, const Params& p)
 {
     __shared__ uint32_t red[kThreads / 64];
     __shared__ uint32_t gen_s, wait_s, result_s, ok_s;
@@ -775,10 +802,6 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
         gen_s = gen0;
         wait_s = wait0;
         slot_store(&ws[kWsArrive + 2 * blockIdx.x], gen0, m);
-        // The store above carries gen0, so the generation word has been read
-        // by the time this count is made. The result is used only at the end
-        // of the kernel.
-        read_rank = __hip_atomic_fetch_add(&ws[kWsExit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     const uint32_t gen = gen_s;
@@ -834,8 +857,15 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
             if (ok_s == 0u)
                 __hip_atomic_fetch_add(&ws[kWsSlow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        const uint32_t flag = ok_s != 0u ? 0u : kExpiredFlag;
         for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads)
-            slot_store(&ws[kWsRelease + 2 * i], gen, amax);
+            slot_store(&ws[kWsRelease + 2 * i], gen, amax | flag);
+        if (threadIdx.x == 0) {
+            if (ok_s != 0u)
+                ws_store(&ws[kWsGen], gen);  // every workgroup has read it
+            else
+                count_expired(ws, gen);
+        }
         return amax;
     }
     if (threadIdx.x == 0) {
@@ -854,23 +884,16 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
     __syncthreads();
     if (ok_s == 0u) {
         const uint32_t amax = direct_amax(p, red);
-        if (threadIdx.x == 0)
+        if (threadIdx.x == 0) {
             __hip_atomic_fetch_add(&ws[kWsSlow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            count_expired(ws, gen);
+        }
         return amax;
     }
-    return result_s;
-}
-
-// Called by thread 0 of every workgroup at the end of the kernel: the
-// workgroup that was the last to count itself (every other one has read the
-// generation by then) resets the count and publishes this call's generation
-// as the last completed one.
-__device__ __forceinline__ void release_generation(uint32_t* ws, uint32_t gen, uint32_t read_rank)
-{
-    if (read_rank == gridDim.x - 1u) {
-        ws_store(&ws[kWsExit], 0u);
-        ws_store(&ws[kWsGen], gen);
-    }
+    const uint32_t v = result_s;
+    if ((v & kExpiredFlag) != 0u && threadIdx.x == 0)
+        count_expired(ws, gen);  // workgroup 0's wait expired
+    return v & ~kExpiredFlag;
 }
 
 // Write the staged columnwise output of two vertically adjacent tiles (A at
@@ -971,9 +994,7 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
             row_maxima(vb, qb.odd, bb);
         m = max(m, item_max(bb));
     }
-    uint32_t read_rank = 0u;
-    const uint32_t amax_bits =
-        p.amax_given ? __float_as_uint(*p.amax) : grid_max(m, gen, wait, ws, p, read_rank);
+    const uint32_t amax_bits = p.amax_given ? __float_as_uint(*p.amax) : grid_max(m, gen, wait, ws, p);
 
     const ScaleCtx sc = scale_ctx(__uint_as_float(amax_bits));
     if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
@@ -995,8 +1016,6 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
         __syncthreads();
         write_col_pair(p, qa.tile_r0, qa.tile_c0, lds_codes[0], lds_codes[1], lds_scales[0], lds_scales[1]);
     }
-    if (!p.amax_given && threadIdx.x == 0)
-        release_generation(ws, gen, read_rank);
 }
 
 // Workgroups of one fused kernel that fit on the device at once (cached).

@@ -651,8 +651,10 @@ def test_fused_amax_quantize(name, sr, layouts):
         got = {k: host(v) for k, v in out.items()}
         wsh = host(ws)
         assert wsh[2] == 0, "in-kernel exchange fell back to the slow path"
-        if x.size <= (1 << 25):  # single pass: one generation per call, read count back at 0
-            assert wsh[1] == rep + 1 and wsh[4] == 0, (wsh[1], wsh[4])
+        # a single pass moves the generation by one per call (the two-pass
+        # path, for tensors that do not fit on chip, leaves it); with no
+        # expired wait nothing is counted in words 4..5
+        assert wsh[1] in (0, rep + 1) and wsh[4] == 0 and wsh[5] == 0, (wsh[1], wsh[4], wsh[5])
         amax_gpu = wsh[:1].view(np.float32)[0]
         check_q1(x, got, amax_gpu, rowwise, colwise, sr, False,
                  rows=None if x.shape[0] <= 512 else sample_idx(x.shape[0], 16, 7 + rep),
@@ -701,8 +703,11 @@ def test_fused_fallback_then_smaller_tensor(sr, layouts):
     after every workgroup of a call has read it, so no workgroup of the
     first call can post its maximum under the second call's generation: the
     second call's amax and every code and scale byte are the oracle's for
-    its own tensor. The generation word moves by one per call and the count
-    of workgroups that have read it is back at 0 after each."""
+    its own tensor. The generation word moves by one per call; after the
+    expired call, words 4..5 hold its generation as the tag and the number
+    of its workgroups that went through an expired wait (all 20 when
+    workgroup 0's own wait expired; fewer when workgroup 0 still saw every
+    arrival on its first look), and the normal call leaves them."""
     rowwise, colwise = layouts
     log(f"[test_fused_fallback_then_smaller_tensor] sr={sr} layouts={layouts}")
     big = W.f32_to_bf16_bits(W.bf16_bits_to_f32(W.activation(1024, 1280, seed=31)) * np.float32(1e4))
@@ -712,13 +717,15 @@ def test_fused_fallback_then_smaller_tensor(sr, layouts):
     out = F.nvfp4_quantize_1d_fused(dev(big), ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED)
     wsh = host(ws)
     assert wsh[2] > 0, "no workgroup took the direct amax"
-    assert wsh[1] == 1 and wsh[4] == 0, (wsh[1], wsh[4])
+    grid = 4 * 5  # pairs of 128-row tiles x 256-column tiles
+    assert wsh[1] == 1 and wsh[4] == 1 and 1 <= wsh[5] <= grid, (wsh[1], wsh[4], wsh[5])
+    expired = int(wsh[5])
     check_q1(big, {k: host(v) for k, v in out.items()}, wsh[:1].view(np.float32)[0], rowwise, colwise, sr,
              False)
     ws[3] = 0
     out = F.nvfp4_quantize_1d_fused(dev(small), ws, rowwise=rowwise, colwise=colwise, sr=sr, seed=SEED)
     wsh = host(ws)
-    assert wsh[1] == 2 and wsh[4] == 0, (wsh[1], wsh[4])
+    assert wsh[1] == 2 and wsh[4] == 1 and wsh[5] == expired, (wsh[1], wsh[4], wsh[5])
     a = wsh[:1].view(np.float32)[0]
     assert f32_bits(a) == f32_bits(oracle.amax(small))
     check_q1(small, {k: host(v) for k, v in out.items()}, a, rowwise, colwise, sr, False)
