@@ -44,6 +44,7 @@ EXPORTS = (
     "nvfp4_amax",
     "nvfp4_quantize_1d",
     "nvfp4_quantize_1d_fused",
+    "nvfp4_quantize_1d_fused_noalloc",
     "nvfp4_quantize_2d",
     "nvfp4_quantize_2d_tscales",
     "nvfp4_rht16",
@@ -86,6 +87,8 @@ def lib():
     L.nvfp4_quantize_1d.argtypes = [P, I64, I64, P, U32, U16, U64, P, P, P, P, P, P]
     L.nvfp4_quantize_1d_fused.restype = I
     L.nvfp4_quantize_1d_fused.argtypes = [P, I64, I64, U32, U64, P, P, P, P, P, P, P]
+    L.nvfp4_quantize_1d_fused_noalloc.restype = I
+    L.nvfp4_quantize_1d_fused_noalloc.argtypes = [P, I64, I64, U32, U64, P, P, P, P, P, P, P]
     L.nvfp4_quantize_2d.restype = I
     L.nvfp4_quantize_2d.argtypes = [P, I64, I64, P, P, P, P, P, P]
     L.nvfp4_quantize_2d_tscales.restype = I
@@ -241,6 +244,27 @@ def nvfp4_quantize_1d_fused(x, workspace, rowwise: bool = True, colwise: bool = 
         _ptr(out.get("codes_row")), _ptr(out.get("scales_row")),
         _ptr(out.get("codes_col")), _ptr(out.get("scales_col")),
         _ptr(out["global_scale"]), _stream(stream)))
+    return out
+
+
+def nvfp4_quantize_1d_fused_noalloc(x, rowwise: bool = True, colwise: bool = False, sr: bool = False,
+                                    seed: int = 0, out: dict | None = None, amax=None, stream=None):
+    """nvfp4_quantize_1d_fused on the library's own static workspace (no
+    device allocation by the library; pass preallocated outputs in `out` to
+    allocate nothing here either). amax: optional float32 [1] that receives
+    the amax. Calls that overlap in time on one device race."""
+    torch = _torch()
+    _bits16(x)
+    if amax is not None:
+        _dev_tensor(amax, "amax", torch.float32)
+    R, C = x.shape
+    out = _q1_outputs(x, rowwise, colwise, out)
+    flags = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0) | (SR if sr else 0)
+    _check(lib().nvfp4_quantize_1d_fused_noalloc(
+        _ptr(x), R, C, flags, seed & ((1 << 64) - 1),
+        _ptr(out.get("codes_row")), _ptr(out.get("scales_row")),
+        _ptr(out.get("codes_col")), _ptr(out.get("scales_col")),
+        _ptr(out["global_scale"]), _ptr(amax), _stream(stream)))
     return out
 
 

@@ -201,6 +201,26 @@ int nvfp4_quantize_1d_fused(const uint16_t* x, int64_t rows, int64_t cols, uint3
     return status_of(nvfp4::launch_quantize(a, stream));
 }
 
+int nvfp4_quantize_1d_fused_noalloc(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
+                                    uint64_t seed, uint8_t* codes_row, uint8_t* scales_row,
+                                    uint8_t* codes_col, uint8_t* scales_col, float* global_scale,
+                                    float* amax, hipStream_t stream)
+{
+    nvfp4::QuantizeArgs a;
+    const int st = fused_args(x, rows, cols, flags, seed, codes_row, scales_row, codes_col, scales_col,
+                              global_scale, a);
+    if (st != NVFP4_OK)
+        return st;
+    if (amax != nullptr && (reinterpret_cast<uintptr_t>(amax) & 3u) != 0)
+        return NVFP4_ERR_ALIGN;
+    uint32_t* ws = nullptr;
+    if (nvfp4::noalloc_workspace(&ws) != hipSuccess)
+        return NVFP4_ERR_HIP;
+    a.workspace = ws;
+    a.amax_out = amax;
+    return status_of(nvfp4::launch_quantize(a, stream));
+}
+
 int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
                       uint8_t* codes_row, uint8_t* codes_col, uint8_t* scales,
                       float* global_scale, hipStream_t stream)

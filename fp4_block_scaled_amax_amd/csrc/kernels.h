@@ -26,8 +26,13 @@ struct QuantizeArgs {
     float* global_scale;  // optional
     bool fused_amax;      // compute the amax in the same call (workspace)
     uint32_t* workspace;  // fused_amax: amax bits in word 0, scratch after
+    float* amax_out;      // fused_amax: optional copy of the amax
 };
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
+
+// Device address of the library's own exchange workspace on the current
+// device (NVFP4_WORKSPACE_BYTES, never allocated: a static device array).
+hipError_t noalloc_workspace(uint32_t** ws);
 
 hipError_t launch_rht16(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint32_t mask,
                         float* y, hipStream_t stream);

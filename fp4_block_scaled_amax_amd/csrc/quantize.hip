@@ -28,6 +28,7 @@
 // rule exactly (see sr_operand); blocks with a non-finite multiplier use the
 // software encoder e2m1_sr_nibble.
 #include <atomic>
+#include <mutex>
 
 #include "device.h"
 #include "kernels.h"
@@ -55,6 +56,7 @@ struct Params {
     float* sg_out;
     int tiles_r, tiles_c;
     int amax_given;  // quantize_fused_kernel: *amax holds the amax, no exchange
+    float* amax_out;  // quantize_fused_kernel: optional copy of the amax it finds
 };
 
 // Map the workgroup index to a tile so that each XCD (workgroups are dealt
@@ -854,6 +856,8 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
         const uint32_t amax = result_s;
         if (threadIdx.x == 0) {
             ws_store(&ws[kWsAmax], amax);
+            if (p.amax_out != nullptr)
+                *p.amax_out = __uint_as_float(amax);
             if (ok_s == 0u)
                 __hip_atomic_fetch_add(&ws[kWsSlow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -1074,7 +1078,44 @@ hipError_t launch_variant(const Params& p, hipStream_t stream)
     return hipGetLastError();
 }
 
+// The exchange workspace of nvfp4_quantize_1d_fused_noalloc: one copy per
+// device (zero when the code object loads), shared by every such call on
+// that device and held until the process ends. The exchange leaves it ready
+// for the next call, so it is never cleared; calls on one device that
+// overlap in time race on it.
+constexpr int kScratchWords = kWsRelease + 2 * kMaxFusedBlocks;
+static_assert(kScratchWords * 4 == 32832, "the workspace size the C header states");
+static_assert(kMaxFusedGrid <= kMaxFusedBlocks, "every workgroup of a single pass has its slots");
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
 }  // namespace
+
+hipError_t noalloc_workspace(uint32_t** ws)
+{
+    // Device addresses of `scratch`, looked up once per device with that
+    // device current. The host-side name `scratch` is not a device address.
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static uint32_t* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (ptr == nullptr)
+            return hipErrorInvalidSymbol;
+        addr[dev] = static_cast<uint32_t*>(ptr);
+    }
+    *ws = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
 {
@@ -1095,6 +1136,7 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
         p.tiles_r = (int)((a.rows + kTileR - 1) / kTileR);
         p.tiles_c = (int)((a.cols + kTileC - 1) / kTileC);
         p.amax_given = 0;
+        p.amax_out = a.amax_out;
         bool launched = false;
         hipError_t e;
         if (a.rowwise && a.colwise)
@@ -1108,8 +1150,9 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
                      : launch_fused_variant<false, true, false>(p, a.workspace, stream, launched);
         if (e != hipSuccess || launched)
             return e;
-        // Too large to keep on chip: the two-pass path, amax into the workspace.
-        float* amax = reinterpret_cast<float*>(a.workspace);
+        // Too large to keep on chip: the two-pass path, amax into the
+        // workspace (or straight into the caller's copy of it).
+        float* amax = a.amax_out != nullptr ? a.amax_out : reinterpret_cast<float*>(a.workspace);
         e = launch_amax(a.x, a.rows * a.cols, amax, stream);
         if (e != hipSuccess)
             return e;
@@ -1134,6 +1177,7 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
     p.tiles_r = (int)((a.rows + kTileR - 1) / kTileR);
     p.tiles_c = (int)((a.cols + kTileC - 1) / kTileC);
     p.amax_given = 0;
+    p.amax_out = nullptr;
 
     if (a.two_d) {
         if (a.rowwise && a.colwise)

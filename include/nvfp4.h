@@ -157,6 +157,33 @@ int nvfp4_quantize_1d_fused(const uint16_t* x, int64_t rows, int64_t cols, uint3
                             float* global_scale, hipStream_t stream);
 
 /*
+ * nvfp4_quantize_1d_fused_noalloc -- for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): nvfp4_quantize_1d_fused without the
+ * workspace argument. Its exchange runs in the library's own workspace, a
+ * static device array of NVFP4_WORKSPACE_BYTES (32,832 bytes) per GPU,
+ * held until the process ends. The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); its first call on a device looks
+ * up that device's copy of the array.
+ *   amax   optional device float (4-byte aligned, may be NULL) that
+ *          receives the amax; the global scale goes to global_scale as in
+ *          nvfp4_quantize_1d.
+ *   Other arguments, validation and outputs as nvfp4_quantize_1d_fused;
+ *   results are bit-identical to it.
+ * Size limit: none beyond nvfp4_quantize_1d_fused's. The workspace holds
+ * the exchange slots of the largest single pass (1024 workgroups); larger
+ * tensors take the two-pass path, which needs no slots.
+ * Every such call on one GPU shares the array: calls that overlap in time
+ * on one device (different streams, or host threads without ordering)
+ * race and give wrong results; order them on one stream. Each call leaves
+ * the array ready for the next, so nothing needs clearing.
+ */
+int nvfp4_quantize_1d_fused_noalloc(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
+                                    uint64_t seed, uint8_t* codes_row, uint8_t* scales_row,
+                                    uint8_t* codes_col, uint8_t* scales_col, float* global_scale,
+                                    float* amax, hipStream_t stream);
+
+/*
  * nvfp4_quantize_2d -- weight quantization with one E4M3 scale per 16x16
  * tile, emitted in both layouts with identical codes (page "Melatih model
  * dalam 4 bit", section "Empat pengaman", second safeguard: rowwise and

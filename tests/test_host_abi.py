@@ -105,6 +105,20 @@ def test_quantize_1d_fused_validation(L):
     assert q1(L, flags=F.ROWWISE | 0x10) == -4
 
 
+def test_quantize_1d_fused_noalloc_validation(L):
+    f = lambda **k: L.nvfp4_quantize_1d_fused_noalloc(
+        k.get("x", A), k.get("rows", 64), k.get("cols", 64), k.get("flags", F.ROWWISE), 0, k.get("cr", A),
+        k.get("sr", A), k.get("cc", A), k.get("sc", A), NULL, k.get("amax", NULL), NULL)
+    assert f(flags=0) == -4
+    assert f(flags=F.COLWISE | F.RHT) == -4
+    assert f(x=NULL) == -1
+    assert f(cr=NULL) == -1
+    assert f(rows=40) == -2
+    assert f(x=MIS) == -3
+    assert f(amax=P(4098)) == -3
+    assert f(rows=1 << 40, cols=1 << 40) == -6
+
+
 def test_quantize_2d_validation(L):
     assert L.nvfp4_quantize_2d(A, 32, 32, A, NULL, NULL, A, NULL, NULL) == -1
     assert L.nvfp4_quantize_2d(A, 32, 32, A, A, A, NULL, NULL, NULL) == -1
