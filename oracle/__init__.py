@@ -358,3 +358,124 @@ def mx_gemm_rows(a_codes, a_scales, b_codes, b_scales, M, N, K, rows):
     a = mx_dequantize_f64_rows(a_codes, a_scales, M, K, rows)
     b = mx_dequantize_f64_rows(b_codes, b_scales, N, K, np.arange(N, dtype=np.int64))
     return a @ b.T
+
+
+# ------------------------------------------- the same functions on all cores
+#
+# The C functions take row, column or tile-row ranges and release the
+# interpreter lock, so threads run them side by side on disjoint ranges of
+# one output array. The arithmetic is the single-threaded functions'; only
+# the work is split (whole 16-row blocks for the transform, whole tiles for
+# 2D), so the bytes are the same.
+
+def host_threads(limit: int = 16) -> int:
+    """Threads for the multi-threaded drivers: the CPUs this process may
+    use, at most `limit`."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(limit, n))
+
+
+def _ranges(n: int, parts: int, align: int = 1):
+    step = -(-n // max(1, parts))
+    step = max(align, -(-step // align) * align)
+    return [(lo, min(n, lo + step)) for lo in range(0, n, step)]
+
+
+def _run(fn, ranges, threads):
+    from concurrent.futures import ThreadPoolExecutor
+
+    if len(ranges) == 1:
+        return [fn(ranges[0])]
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(fn, ranges))
+
+
+def _at(a: np.ndarray, offset: int):
+    return ctypes.c_void_p(a.ctypes.data + offset)
+
+
+def amax_mt(x: np.ndarray, threads: int | None = None) -> np.float32:
+    x = _c(x, np.uint16)
+    t = threads or host_threads()
+    parts = _run(lambda r: amax(x[r[0]:r[1]]), _ranges(x.shape[0], t), t)
+    return np.float32(np.nan) if any(np.isnan(p) for p in parts) else np.float32(max(parts))
+
+
+def amax_rht_mt(x: np.ndarray, mask: int, threads: int | None = None) -> np.float32:
+    x = _c(x, np.uint16)
+    t = threads or host_threads()
+    parts = _run(lambda r: amax_rht(x[r[0]:r[1]], mask), _ranges(x.shape[0], t, 16), t)
+    return np.float32(np.nan) if any(np.isnan(p) for p in parts) else np.float32(max(parts))
+
+
+def quantize_1d_rows_mt(x: np.ndarray, sg, sr: bool = False, seed: int = 0, threads: int | None = None):
+    """quantize_1d_rows over the whole tensor, row ranges on threads."""
+    x = _c(x, np.uint16)
+    R, C = x.shape
+    codes = np.empty((R, C // 2), np.uint8)
+    scales = np.empty((R, C // 16), np.uint8)
+    lib = _load()
+    t = threads or host_threads()
+
+    def work(r):
+        lib.nvfp4_oracle_quantize_1d_rows(_ptr(x), R, C, float(sg), int(bool(sr)), seed, r[0], r[1],
+                                          _at(codes, r[0] * (C // 2)), _at(scales, r[0] * (C // 16)))
+
+    _run(work, _ranges(R, t), t)
+    return codes, scales
+
+
+def quantize_1d_cols_mt(x: np.ndarray, sg, sr: bool = False, seed: int = 0, rht: bool = False,
+                        mask: int = 0, threads: int | None = None):
+    """quantize_1d_cols over the whole tensor, column ranges on threads."""
+    x = _c(x, np.uint16)
+    R, C = x.shape
+    codes = np.empty((C, R // 2), np.uint8)
+    scales = np.empty((C, R // 16), np.uint8)
+    lib = _load()
+    t = threads or host_threads()
+
+    def work(c):
+        lib.nvfp4_oracle_quantize_1d_cols(_ptr(x), R, C, float(sg), int(bool(sr)), seed, int(bool(rht)), mask,
+                                          c[0], c[1], _at(codes, c[0] * (R // 2)), _at(scales, c[0] * (R // 16)))
+
+    _run(work, _ranges(C, t), t)
+    return codes, scales
+
+
+def quantize_2d_mt(x: np.ndarray, sg, threads: int | None = None):
+    """quantize_2d over the whole tensor, tile-row ranges on threads."""
+    x = _c(x, np.uint16)
+    R, C = x.shape
+    codes_row = np.zeros((R, C // 2), np.uint8)
+    codes_col = np.zeros((C, R // 2), np.uint8)
+    scales = np.zeros((R // 16, C // 16), np.uint8)
+    lib = _load()
+    t = threads or host_threads()
+
+    def work(tr):
+        lib.nvfp4_oracle_quantize_2d(_ptr(x), R, C, float(sg), tr[0], tr[1], _ptr(codes_row), _ptr(codes_col),
+                                     _ptr(scales))
+
+    _run(work, _ranges(R // 16, t), t)
+    return codes_row, codes_col, scales
+
+
+def dequantize_mt(codes: np.ndarray, scales: np.ndarray, scale_mode: int, sg, R: int, C: int,
+                  bf16: bool = False, threads: int | None = None) -> np.ndarray:
+    """dequantize (binary32) or dequantize_bf16 over the whole tensor."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    out = np.empty((R, C), np.uint16 if bf16 else np.float32)
+    lib = _load()
+    fn = lib.nvfp4_oracle_dequantize_bf16 if bf16 else lib.nvfp4_oracle_dequantize
+    t = threads or host_threads()
+
+    def work(r):
+        fn(_ptr(codes), _ptr(scales), scale_mode, float(sg), R, C, r[0], r[1], _at(out, r[0] * C * out.itemsize))
+
+    _run(work, _ranges(R, t, 16), t)
+    return out

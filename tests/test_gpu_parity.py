@@ -6,10 +6,12 @@ Hadamard transform must match the oracle's binary32 butterfly bit for bit
 must satisfy ||C - C_ref||_F / ||C_ref||_F <= 1e-5 against the double
 reference on the dequantized operands.
 
-Small cases are compared in full; the full-size workloads (8192x4096
-activation, 14336x4096 weight, 8192x14336 gradient, the 8192x14336x4096
-product) are compared on sampled rows / columns / tiles that the oracle
-computes one by one, with the same launch configuration bench.py times.
+Every quantizer output is compared whole, the full-size workloads (8192x4096
+activation, 14336x4096 weight, 8192x14336 gradient) included, against the
+oracle run on all host cores (the same C functions over disjoint row,
+column or tile-row ranges), in the launch configurations bench.py times.
+The 8192x14336x4096 product is checked on 256 sampled rows in full, as its
+workload states.
 """
 import functools
 import sys
@@ -109,11 +111,12 @@ MASK = W.rht_sign_mask()
 SEED = W.SR_SEED
 
 
-def sample_idx(n, count, seed):
-    rng = np.random.default_rng(seed)
-    idx = set(rng.choice(n, size=min(count, n), replace=False).tolist())
-    idx.update([0, n - 1])
-    return sorted(idx)
+def same_rows(got, want, what):
+    """Whole-array byte equality, naming the first rows that differ."""
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if not np.array_equal(got, want):
+        bad = np.nonzero(np.any(got != want, axis=tuple(range(1, got.ndim))))[0]
+        raise AssertionError(f"{what} differ in {bad.size} rows, first {bad[:8].tolist()}")
 
 
 # ------------------------------------------------------------------ amax
@@ -152,28 +155,21 @@ def run_q1(x, rowwise, colwise, sr=False, rht=False):
     return {k: host(v) for k, v in out.items()}, host(a)[0]
 
 
-def check_q1(x, got, amax_gpu, rowwise, colwise, sr, rht, rows=None, cols=None):
-    amax = oracle.amax_rht(x, MASK) if rht else oracle.amax(x)
+def check_q1(x, got, amax_gpu, rowwise, colwise, sr, rht):
+    """Every byte of the requested layouts, the amax and S_g, against the
+    oracle on the whole tensor."""
+    amax = oracle.amax_rht_mt(x, MASK) if rht else oracle.amax_mt(x)
     assert f32_bits(amax_gpu) == f32_bits(amax)
     sg = oracle.global_scale(amax)
     assert f32_bits(got["global_scale"][0]) == f32_bits(sg)
-    R, C = x.shape
     if rowwise:
-        for r in (range(R) if rows is None else rows):
-            c, s = oracle.quantize_1d_rows(x, sg, sr, SEED, r, r + 1)
-            assert np.array_equal(got["codes_row"][r], c[0]), f"row codes differ at row {r}"
-            assert np.array_equal(got["scales_row"][r], s[0]), f"row scales differ at row {r}"
+        c, s = oracle.quantize_1d_rows_mt(x, sg, sr, SEED)
+        same_rows(got["codes_row"], c, "rowwise codes")
+        same_rows(got["scales_row"], s, "rowwise scales")
     if colwise:
-        if cols is None:
-            c, s = oracle.quantize_1d_cols(x, sg, sr, SEED, rht, MASK)
-            bad = np.nonzero(np.any(got["codes_col"] != c, axis=1))[0]
-            assert bad.size == 0, f"column codes differ at columns {bad[:10]}"
-            assert np.array_equal(got["scales_col"], s)
-        else:
-            for col in cols:
-                c, s = oracle.quantize_1d_cols(x, sg, sr, SEED, rht, MASK, col, col + 1)
-                assert np.array_equal(got["codes_col"][col], c[0]), f"column codes differ at {col}"
-                assert np.array_equal(got["scales_col"][col], s[0]), f"column scales differ at {col}"
+        c, s = oracle.quantize_1d_cols_mt(x, sg, sr, SEED, rht, MASK)
+        same_rows(got["codes_col"], c, "columnwise codes (rows = input columns)")
+        same_rows(got["scales_col"], s, "columnwise scales")
 
 
 CASES_SMALL = [
@@ -200,24 +196,35 @@ def test_quantize_1d_small(case):
     check_q1(x, got, a, rowwise, colwise, sr, rht)
 
 
-def test_quantize_1d_full_activation_row_and_col():
-    """The 8192x4096 activation, rowwise + columnwise RNE in one call (the
-    benchmarked step), sampled rows and columns."""
-    x = wl("act")
-    log("[test_quantize_1d_full_activation_row_and_col]")
-    got, a = run_q1(x, True, True)
-    R, C = x.shape
-    check_q1(x, got, a, True, True, False, False, rows=sample_idx(R, 48, 1), cols=sample_idx(C, 48, 2))
+FULL_CASES = [
+    # (workload, rowwise, colwise, sr, rht): the activation's layouts as the
+    # bench rows time them (both layouts with round-to-nearest take the
+    # paired-tile kernel, single layouts and stochastic rounding the
+    # one-tile kernel), the gradient path of the wgrad operands (transform +
+    # stochastic rounding, columnwise, seed 42, gradient and activation),
+    # the transform with round-to-nearest, stochastic rounding without the
+    # transform, and the gradient's rowwise dgrad operand.
+    ("act", True, True, False, False),
+    ("act", True, False, False, False),
+    ("act", False, True, False, False),
+    ("act", True, True, True, False),
+    ("act", False, True, True, True),
+    ("act", False, True, False, True),
+    ("grad", False, True, True, True),
+    ("grad", False, True, True, False),
+    ("grad", True, False, True, False),
+    ("grad", True, True, False, False),
+]
 
 
-@pytest.mark.parametrize("name", ["grad", "act"])
-def test_quantize_1d_full_gradient_path(name):
-    """Hadamard + stochastic rounding, columnwise, seed 42 (wgrad operands)."""
+@pytest.mark.parametrize("case", FULL_CASES, ids=lambda c: "-".join(str(v) for v in c))
+def test_quantize_1d_full_size(case):
+    """The full-size workloads, every byte of every requested output."""
+    name, rowwise, colwise, sr, rht = case
     x = wl(name)
-    log(f"[test_quantize_1d_full_gradient_path] {name}")
-    got, a = run_q1(x, False, True, sr=True, rht=True)
-    R, C = x.shape
-    check_q1(x, got, a, False, True, True, True, cols=sample_idx(C, 32, 3))
+    log(f"[test_quantize_1d_full_size] {case} {x.shape}")
+    got, a = run_q1(x, rowwise, colwise, sr, rht)
+    check_q1(x, got, a, rowwise, colwise, sr, rht)
 
 
 def wide_range_blocks(rows, cols, seed):
@@ -375,20 +382,23 @@ def test_quantize_2d_ragged_full_compare():
     assert np.array_equal(got["codes_col"], cc)
 
 
-def test_quantize_2d_full_weight_sampled_tiles():
+def test_quantize_2d_full_weight():
+    """The 14336x4096 weight: every tile scale and every code of both
+    layouts; the transposed tile grid equals the grid transposed."""
     x = wl("weight")
-    log("[test_quantize_2d_full_weight_sampled_tiles]")
-    got, a = run_q2(x)
-    amax = oracle.amax(x)
-    assert f32_bits(a) == f32_bits(amax)
+    log("[test_quantize_2d_full_weight]")
+    xd = dev(x)
+    a = F.nvfp4_amax(xd)
+    got = {k: host(v) for k, v in F.nvfp4_quantize_2d(xd, a, transposed_scales=True).items()}
+    amax = oracle.amax_mt(x)
+    assert f32_bits(host(a)[0]) == f32_bits(amax)
     sg = oracle.global_scale(amax)
-    R, C = x.shape
-    for tr in sample_idx(R // 16, 24, 4):
-        cr, cc, s = oracle.quantize_2d(x, sg, tr, tr + 1)
-        assert np.array_equal(got["scales"][tr], s[tr])
-        rs = slice(tr * 16, tr * 16 + 16)
-        assert np.array_equal(got["codes_row"][rs], cr[rs])
-        assert np.array_equal(got["codes_col"][:, tr * 8:tr * 8 + 8], cc[:, tr * 8:tr * 8 + 8])
+    assert f32_bits(got["global_scale"][0]) == f32_bits(sg)
+    cr, cc, s = oracle.quantize_2d_mt(x, sg)
+    same_rows(got["scales"], s, "tile scales")
+    same_rows(got["scales_t"], np.ascontiguousarray(s.T), "transposed tile scales")
+    same_rows(got["codes_row"], cr, "rowwise codes")
+    same_rows(got["codes_col"], cc, "columnwise codes")
 
 
 def test_quantize_2d_single_layout_outputs():
@@ -398,9 +408,12 @@ def test_quantize_2d_single_layout_outputs():
     both = F.nvfp4_quantize_2d(xd, a)
     rows_only = F.nvfp4_quantize_2d(xd, a, rowwise=True, colwise=False)
     cols_only = F.nvfp4_quantize_2d(xd, a, rowwise=False, colwise=True)
+    sg = oracle.global_scale(oracle.amax(x))
+    cr, cc, s = oracle.quantize_2d(x, sg)
+    assert np.array_equal(host(rows_only["codes_row"]), cr) and np.array_equal(host(rows_only["scales"]), s)
+    assert np.array_equal(host(cols_only["codes_col"]), cc) and np.array_equal(host(cols_only["scales"]), s)
     assert torch.equal(both["codes_row"], rows_only["codes_row"])
     assert torch.equal(both["codes_col"], cols_only["codes_col"])
-    assert torch.equal(both["scales"], cols_only["scales"])
 
 
 # ------------------------------------------------------------------- RHT
@@ -656,9 +669,7 @@ def test_fused_amax_quantize(name, sr, layouts):
         # expired wait nothing is counted in words 4..5
         assert wsh[1] in (0, rep + 1) and wsh[4] == 0 and wsh[5] == 0, (wsh[1], wsh[4], wsh[5])
         amax_gpu = wsh[:1].view(np.float32)[0]
-        check_q1(x, got, amax_gpu, rowwise, colwise, sr, False,
-                 rows=None if x.shape[0] <= 512 else sample_idx(x.shape[0], 16, 7 + rep),
-                 cols=None if x.shape[1] <= 1024 else sample_idx(x.shape[1], 16, 9 + rep))
+        check_q1(x, got, amax_gpu, rowwise, colwise, sr, False)
     two, _ = run_q1(x, rowwise, colwise, sr=sr)
     for k in two:
         assert np.array_equal(got[k], two[k]), k
