@@ -185,6 +185,19 @@ def test_e2m1_rne_matches_exact_midpoints():
     assert np.array_equal(got, _e2m1_rne_thresholds(v))
 
 
+def test_e2m1_rne_nondecreasing_over_all_binades():
+    """The rule is a step function of the value: over positive binary32
+    patterns (which increase with the value) the code never decreases;
+    sampled every 2^10 patterns from 0 to +inf, plus every pattern within
+    2^14 of the grid points and midpoints."""
+    pats = np.arange(0, 0x7F800001, 1 << 10, dtype=np.uint64).astype(np.uint32)
+    near = _fp32_neighbourhood([0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6], 1 << 14)
+    v = np.sort(np.concatenate([bits_to_f32(pats), near]))
+    codes = oracle.e2m1_rne_array(v)
+    assert np.all(np.diff(codes.astype(int)) >= 0)
+    assert codes[0] == 0 and codes[-1] == 7
+
+
 def test_e2m1_rne_exact_rationals():
     """A few hundred values checked against exact rational nearest-even."""
     rng = np.random.default_rng(1)
@@ -315,6 +328,8 @@ def test_sr_counts_over_all_draws():
         ups = int(np.count_nonzero(codes == lo + 1))
         assert np.all((codes == lo) | (codes == lo + 1))
         assert ups == math.ceil(p * (1 << 16)), (v, ups)
+        # the draws that round up are exactly the lowest ones (u < p)
+        assert np.all(codes[:ups] == lo + 1) and np.all(codes[ups:] == lo)
         # so the mean over all draws is within one 2^-16 step of v
         mean = (GRID[lo] * ((1 << 16) - ups) + GRID[lo + 1] * ups) / (1 << 16)
         assert abs(mean - fv) <= (GRID[lo + 1] - GRID[lo]) / (1 << 16)
