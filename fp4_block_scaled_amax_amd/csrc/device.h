@@ -162,11 +162,13 @@ __device__ __forceinline__ uint32_t block_scale_byte_approx(uint32_t b_bits, flo
 }
 
 // The 128 possible multipliers of a tensor (one per scale byte 0..127),
-// built once per workgroup in LDS by the first 128 threads.
-__device__ __forceinline__ void build_reciprocal_table(float* table, float sg)
+// built once per workgroup in LDS by the first 128 threads, each times a
+// power of two `factor` (exact where the caller uses it; see
+// fold_sr_scale_ok and fold_quarter_ok).
+__device__ __forceinline__ void build_reciprocal_table(float* table, float sg, float factor = 1.0f)
 {
     if (threadIdx.x < 128)
-        table[threadIdx.x] = unit_reciprocal(threadIdx.x, sg);
+        table[threadIdx.x] = unit_reciprocal(threadIdx.x, sg) * factor;
 }
 
 // Sufficient for every multiplier of a byte 0..126 to be finite: then
@@ -175,6 +177,30 @@ __device__ __forceinline__ void build_reciprocal_table(float* table, float sg)
 __device__ __forceinline__ bool reciprocals_finite(float sg)
 {
     return sg >= 0x1p-100f && sg <= 0x1p100f;
+}
+
+// Folding powers of two into the multipliers. Every bf16 value is an
+// integer multiple of 2^-133, and so is every binary32 sum and difference
+// of such values (a rounded result of magnitude >= 2^-110 lands on a grid
+// of at least 2^-133; a smaller exact one has at most 23 significant bits
+// and needs no rounding): the Hadamard outputs z included. Hence:
+//  - fold_quarter_ok: y = z / 4 is exact for every z, so fl(y * r) equals
+//    fl(z * (r / 4)) whenever r / 4 is exact, which holds for every
+//    multiplier when S_g is in [2^-100, 2^100] (r in [2^-109, 2^109]).
+//  - fold_sr_scale_ok(sg, shift): the stochastic operand ceil(2^23 fl(v))
+//    with v = fl(w * r) (w = x, or y = z/4 with shift 2) equals
+//    ceil(fl(w' * r')) with r' = 2^(23 - shift) r: both are exact scalings
+//    of one product while fl(v) is normal, and while it is not, both round
+//    up to 1 as long as no nonzero product underflows to 0, i.e.
+//    |w| r > 2^-150. |w| >= 2^-133 (2^-135 for y) and r = 1/(s S_g) >=
+//    fl(1/(448 S_g)), so S_g <= 256 keeps it for x (r > 2^-16.9) and
+//    S_g <= 32 for y (r > 2^-13.9); S_g >= 2^-95 keeps r' <= 2^127.
+__device__ __forceinline__ bool fold_quarter_ok(float sg) { return reciprocals_finite(sg); }
+
+template <int SHIFT>
+__device__ __forceinline__ bool fold_sr_scale_ok(float sg)
+{
+    return sg >= 0x1p-95f && sg <= (SHIFT == 2 ? 32.0f : 256.0f);
 }
 
 // ----------------------------------------------------------- E2M1 codes

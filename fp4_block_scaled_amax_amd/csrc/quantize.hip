@@ -63,11 +63,10 @@ struct Params {
 // Map the workgroup index to a tile so that each XCD (workgroups are dealt
 // round-robin over 8) walks a contiguous run of tiles; `vertical` makes the
 // run go down the rows first.
-__device__ __forceinline__ void tile_of_block(int tiles_r, int tiles_c, bool vertical, int& tr,
+__device__ __forceinline__ void tile_of_index(int t, int tiles_r, int tiles_c, bool vertical, int& tr,
                                               int& tc)
 {
     const int nt = tiles_r * tiles_c;
-    int t = blockIdx.x;
     if ((nt & 7) == 0) {
         const int per = nt >> 3;
         t = (t & 7) * per + (t >> 3);
@@ -81,30 +80,14 @@ __device__ __forceinline__ void tile_of_block(int tiles_r, int tiles_c, bool ver
     }
 }
 
+__device__ __forceinline__ void tile_of_block(int tiles_r, int tiles_c, bool vertical, int& tr, int& tc)
+{
+    tile_of_index(blockIdx.x, tiles_r, tiles_c, vertical, tr, tc);
+}
+
 __device__ __forceinline__ bool finite_bits(float r)
 {
     return (__float_as_uint(r) & 0x7F800000u) != 0x7F800000u;
-}
-
-// 16 values of one column (rows in order) -> 8 bytes of codes.
-template <int MODE>
-__device__ __forceinline__ uint2 encode_column16(const float (&y)[16], float r,
-                                                 const uint4 (&draws)[16], int j)
-{
-    uint32_t w[2] = {MODE == kEncSr ? 0u : fresh_word(), MODE == kEncSr ? 0u : fresh_word()};
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#define NVFP4_PAIR(B)                                                                      \
-    {                                                                                      \
-        const int i = 8 * half + 2 * (B);                                                  \
-        const uint32_t ha = is_sr(MODE) ? sr_input<MODE>(draws[i], j) : 0u;               \
-        const uint32_t hb = is_sr(MODE) ? sr_input<MODE>(draws[i + 1], j) : 0u;           \
-        w[half] = put_pair<MODE, B>(w[half], y[i], y[i + 1], r, ha, hb);                   \
-    }
-        NVFP4_PAIR(0) NVFP4_PAIR(1) NVFP4_PAIR(2) NVFP4_PAIR(3)
-#undef NVFP4_PAIR
-    }
-    return make_uint2(w[0], w[1]);
 }
 
 // Row-and/or-column encoding of a whole item in 2x2 groups: elements
@@ -303,27 +286,46 @@ __device__ __forceinline__ uint32_t scale_byte(uint32_t b_bits, const ScaleCtx& 
 // bm: the item's block maxima (column maxima are ignored with RHT, which
 // recomputes them from the transformed values; row maxima are needed for
 // rowwise 1D only).
+// fold (uniform): the multipliers in lds_rcp carry a power of two
+// (kFoldFactor): 1/4 of the transform (its outputs then stay unscaled) and,
+// with stochastic rounding, the converter's 2^23 operand scaling; the
+// caller has checked that this is exact (fold_quarter_ok, fold_sr_scale_ok).
+template <bool SR, bool RHT>
+constexpr float kFoldFactor = SR ? (RHT ? 0x1p21f : 0x1p23f) : (RHT ? 0.25f : 1.0f);
+
+// Stochastic-rounding draws of an item: one Philox call per row covers the
+// item's 8 consecutive flat indices. They do not depend on the data, so the
+// kernels compute them right after issuing the item's loads; `pin` makes
+// them complete at that point (an empty statement that uses them, then a
+// scheduling barrier that keeps the data's first uses below), so they run
+// while the loads are in flight.
+__device__ __forceinline__ void item_draws(const Params& p, const ItemPos& q, uint4 (&draws)[16], bool pin)
+{
+    const uint64_t flat0 = (uint64_t)(q.r0 * p.cols + q.c0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint64_t qq = (flat0 + (uint64_t)i * (uint64_t)p.cols) >> 3;
+        draws[i] = philox4x32_10((uint32_t)qq, (uint32_t)(qq >> 32), p.seed_lo, p.seed_hi);
+    }
+    if (pin) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            asm volatile("" ::"v"(draws[i].x), "v"(draws[i].y), "v"(draws[i].z), "v"(draws[i].w));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <bool ROW, bool COL, bool TWO_D, bool SR, bool RHT>
 __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
                                              const uint4 (&v)[16], const BlockMax& bm,
-                                             const ScaleCtx& sc, const float* lds_rcp,
-                                             uint2* lds_codes, uint8_t* lds_scales)
+                                             const uint4 (&draws)[16], const ScaleCtx& sc,
+                                             const float* lds_rcp, uint2* lds_codes,
+                                             uint8_t* lds_scales, bool fold)
 {
     const int64_t cols = p.cols;
     const int64_t r0 = q.r0, c0 = q.c0;
     const int rb = q.rb, cg = q.cg;
     const bool odd = q.odd;
-    // Stochastic-rounding draws: one Philox call per row covers the
-    // item's 8 consecutive flat indices.
-    uint4 draws[16];
-    if (SR) {
-        const uint64_t flat0 = (uint64_t)(r0 * cols + c0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint64_t qq = (flat0 + (uint64_t)i * (uint64_t)cols) >> 3;
-            draws[i] = philox4x32_10((uint32_t)qq, (uint32_t)(qq >> 32), p.seed_lo, p.seed_hi);
-        }
-    }
 
     if (COL && !ROW && !TWO_D) {
         // -------------------------------------------- columnwise only
@@ -337,20 +339,38 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
                            : bf16_at(v[i], j);
             uint32_t m;
             if (RHT) {
-                rht16_signed(y);
-                m = 0u;
+                // z = H D x. Every z is a multiple of 2^-133 (see
+                // fold_quarter_ok), so y = z / 4 is exact and max |y| =
+                // max |z| / 4. Largest magnitude from the raw bits: the
+                // signed maximum finds the largest positive value, the
+                // unsigned one the negative value of largest magnitude.
+                hadamard16(y);
+                int32_t mi = 0;
+                uint32_t mu = 0u;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    m = max(m, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+                for (int i = 0; i < 16; ++i) {
+                    mi = max(mi, (int32_t)__float_as_uint(y[i]));
+                    mu = max(mu, __float_as_uint(y[i]));
+                }
+                m = __float_as_uint(0.25f * __uint_as_float(max((uint32_t)mi, mu & 0x7FFFFFFFu)));
+                if (!fold) {  // the 1/4 is not in the multipliers
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        y[i] = 0.25f * y[i];
+                }
             } else {
                 m = (j & 1) ? half_bits<1>(bm.col[j >> 1]) : half_bits<0>(bm.col[j >> 1]);
             }
             const uint32_t byte = scale_byte(m, sc);
             const float r = lds_rcp[byte];
             uint2 words;
+            // Stochastic rounding takes the hardware converter when the
+            // multipliers carry its 2^23 (the common case); otherwise, or for
+            // a block whose multiplier is not finite, the software encoder.
             if (SR)
-                words = __all(finite_bits(r)) ? encode_column16<kEncSrHw>(y, r, draws, j)
-                                              : encode_column16<kEncSr>(y, r, draws, j);
+                words = (fold && __all(finite_bits(r)))
+                            ? encode_column16<kEncSrHwScaled>(y, r, draws, j)
+                            : encode_column16<kEncSr>(y, fold ? r * 0x1p-23f : r, draws, j);
             else if (__all(finite_bits(r)))
                 words = encode_column16<kEncHw>(y, r, draws, j);
             else
@@ -526,11 +546,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
     const ItemPos q = item_pos(tr, tc, p.rows, p.cols);
     uint4 v[16];
     load_item(p, q, v);
+    uint4 draws[16];
+    if (SR && q.valid)
+        item_draws(p, q, draws, true);
 
     const ScaleCtx sc = scale_ctx(*p.amax);
     if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
         *p.sg_out = sc.sg;
-    build_reciprocal_table(lds_rcp, sc.sg);
+    // Powers of two folded into the multipliers where that is exact
+    // (uniform); the columnwise-only kernels take it.
+    constexpr bool kCanFold = COL && !ROW && !TWO_D && (SR || RHT);
+    const bool fold = kCanFold && (SR ? (RHT ? fold_sr_scale_ok<2>(sc.sg) : fold_sr_scale_ok<0>(sc.sg))
+                                      : fold_quarter_ok(sc.sg));
+    build_reciprocal_table(lds_rcp, sc.sg, fold ? kFoldFactor<SR, RHT> : 1.0f);
     __syncthreads();
 
     if (q.valid) {
@@ -539,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
             column_maxima(v, bm);
         if (ROW && !TWO_D)
             row_maxima(v, q.odd, bm);
-        compute_item<ROW, COL, TWO_D, SR, RHT>(p, q, v, bm, sc, lds_rcp, lds_codes, lds_scales);
+        compute_item<ROW, COL, TWO_D, SR, RHT>(p, q, v, bm, draws, sc, lds_rcp, lds_codes, lds_scales, fold);
     }
     if (COL) {
         __syncthreads();
@@ -890,18 +918,30 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
     const ScaleCtx sc = scale_ctx(__uint_as_float(amax_bits));
     if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
         *p.sg_out = sc.sg;
-    build_reciprocal_table(lds_rcp, sc.sg);
+    // Columnwise-only stochastic rounding: the converter's 2^23 goes into
+    // the multipliers where that is exact (uniform).
+    constexpr bool kCanFold = COL && !ROW && SR;
+    const bool fold = kCanFold && fold_sr_scale_ok<0>(sc.sg);
+    build_reciprocal_table(lds_rcp, sc.sg, fold ? kFoldFactor<SR, false> : 1.0f);
     __syncthreads();
 
     if (qa.valid) {
         if (ROW && !kEarlyRows)
             row_maxima(va, qa.odd, ba);
-        compute_item<ROW, COL, false, SR, false>(p, qa, va, ba, sc, lds_rcp, lds_codes[0], lds_scales[0]);
+        uint4 draws[16];
+        if (SR)
+            item_draws(p, qa, draws, false);
+        compute_item<ROW, COL, false, SR, false>(p, qa, va, ba, draws, sc, lds_rcp, lds_codes[0], lds_scales[0],
+                                                 fold);
     }
     if (has_b && qb.valid) {
         if (ROW && !kEarlyRows)
             row_maxima(vb, qb.odd, bb);
-        compute_item<ROW, COL, false, SR, false>(p, qb, vb, bb, sc, lds_rcp, lds_codes[1], lds_scales[1]);
+        uint4 draws[16];
+        if (SR)
+            item_draws(p, qb, draws, false);
+        compute_item<ROW, COL, false, SR, false>(p, qb, vb, bb, draws, sc, lds_rcp, lds_codes[1], lds_scales[1],
+                                                 fold);
     }
     if (COL) {
         __syncthreads();

@@ -8,8 +8,10 @@
 //   both nibbles of all four byte positions; records each pattern whose
 //   code differs from the previous pattern's (run starts).
 // probe_sr_thresholds: for each value, every 16-bit draw h through the
-//   stochastic encoder (hardware converter with its input mapping, both
-//   halves of a Philox word) and through the software encoder; records the
+//   stochastic column encoder in every row and column position (hardware
+//   converter with its input mapping, the 2^23 operand scaling applied by
+//   the encoder or carried by the multiplier), through the software encoder
+//   and through the rowwise pair encoder; records the
 //   code for h = 0 and h = 65535 and the number of draws giving the h = 0
 //   code, and flags any value whose codes are not a prefix of one code
 //   followed by the other, or on which the encoders disagree.
@@ -62,19 +64,35 @@ __global__ void rne_runs_kernel(uint32_t lo, uint32_t hi, uint32_t chunk, uint32
         atomicAdd(mismatch, 1u);
 }
 
-// Code of the stochastic encoder for v with draw h: the hardware path in
-// the low-half (even element) and high-half (odd element) positions of a
-// Philox word, and the software path; `agree` is cleared on any difference.
-template <int B>
-__device__ __forceinline__ uint32_t sr_code(float v, uint32_t h, bool& agree)
+// Codes of the stochastic encoders for v with the 16 draws h0 .. h0 + 15:
+// the column encoder the columnwise kernels use (encode_column16: the
+// hardware converter with the 2^23 carried by the multiplier, and with it
+// applied by the encoder; the software encoder), placing draw h0 + i in row
+// i of column j; `agree` is cleared where the three differ or a row's code
+// is not what the pair encoder (put_pair, rowwise kernels) gives.
+__device__ __forceinline__ void sr_codes16(float v, uint32_t h0, int j, uint32_t (&c)[16], bool& agree)
 {
-    const uint4 w = make_uint4(h | (h << 16), 0u, 0u, 0u);  // draw h for elements 0 and 1
-    const uint32_t hw = put_pair<kEncSrHw, B>(0u, v, v, 1.0f, sr_input<kEncSrHw>(w, 0), sr_input<kEncSrHw>(w, 1));
-    const uint32_t sw = put_pair<kEncSr, B>(0u, v, v, 1.0f, sr_input<kEncSr>(w, 0), sr_input<kEncSr>(w, 1));
-    const uint32_t b = (hw >> (8 * B)) & 0xFFu;
-    const uint32_t c = b & 0xFu;
-    agree = agree && b == (c | (c << 4)) && ((sw >> (8 * B)) & 0xFFu) == b;
-    return c;
+    float y[16];
+    uint4 draws[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        y[i] = v;
+        const uint32_t h = h0 + i;
+        const uint32_t word = (j & 1) ? (h << 16) : h;
+        draws[i] = make_uint4((j >> 1) == 0 ? word : 0u, (j >> 1) == 1 ? word : 0u, (j >> 1) == 2 ? word : 0u,
+                              (j >> 1) == 3 ? word : 0u);
+    }
+    const uint2 hs = encode_column16<kEncSrHwScaled>(y, 0x1p23f, draws, j);
+    const uint2 hw = encode_column16<kEncSrHw>(y, 1.0f, draws, j);
+    const uint2 sw = encode_column16<kEncSr>(y, 1.0f, draws, j);
+    agree = agree && hs.x == hw.x && hs.y == hw.y && hs.x == sw.x && hs.y == sw.y;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        c[i] = (((i < 8) ? hs.x : hs.y) >> (4 * (i & 7))) & 0xFu;
+    // the pair encoder of the rowwise kernels, rows 0 and 1 in byte 2
+    const uint32_t pr = put_pair<kEncSrHw, 2>(0u, v, v, 1.0f, sr_input<kEncSrHw>(draws[0], j),
+                                              sr_input<kEncSrHw>(draws[1], j));
+    agree = agree && ((pr >> 16) & 0xFFu) == (c[0] | (c[1] << 4));
 }
 
 __global__ void sr_thresholds_kernel(const float* values, uint32_t n, uint32_t* out)
@@ -84,16 +102,22 @@ __global__ void sr_thresholds_kernel(const float* values, uint32_t n, uint32_t* 
         return;
     const float v = values[i];
     bool agree = true;
-    const uint32_t c0 = sr_code<0>(v, 0u, agree);
-    const uint32_t c1 = sr_code<3>(v, 65535u, agree);
+    uint32_t c[16];
+    sr_codes16(v, 0u, 0, c, agree);
+    const uint32_t c0 = c[0];
+    sr_codes16(v, 65520u, 7, c, agree);
+    const uint32_t c1 = c[15];
     uint32_t count = 0u;
     bool prefix = true, two_valued = true;
-    for (uint32_t h = 0; h < 65536u; ++h) {
-        const uint32_t c = (h & 1u) ? sr_code<1>(v, h, agree) : sr_code<2>(v, h, agree);
-        const bool is0 = c == c0;
-        two_valued = two_valued && (is0 || c == c1);
-        prefix = prefix && (is0 ? count == h : true);  // every h = 0 code comes before any other
-        count += is0 ? 1u : 0u;
+    for (uint32_t h0 = 0; h0 < 65536u; h0 += 16u) {
+        sr_codes16(v, h0, (h0 >> 4) & 7, c, agree);  // every column position in turn
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const bool is0 = c[k] == c0;
+            two_valued = two_valued && (is0 || c[k] == c1);
+            prefix = prefix && (is0 ? count == h0 + k : true);  // every h = 0 code comes first
+            count += is0 ? 1u : 0u;
+        }
     }
     out[4 * i + 0] = c0;
     out[4 * i + 1] = c1;

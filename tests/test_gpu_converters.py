@@ -13,7 +13,9 @@ The oracle is evaluated at every run's first and last pattern.
 Stochastic rounding (same section: gradients round up with probability
 (v - lo)/(hi - lo)): for each of about 77,000 values, every one of the 65,536
 16-bit draws goes through the hardware converter with the library's input
-mapping (both halves of a Philox word) and through the software encoder.
+mapping (both halves of a Philox word; the 2^23 operand scaling applied by
+the encoder, or carried by the multiplier as the columnwise kernels fold it)
+and through the software encoder.
 The probe reports the code at h = 0 and h = 65535 and the number of draws
 giving the h = 0 code, and checks that those draws come first and that the
 encoders agree. The oracle's rule rounds up exactly for the lowest draws
