@@ -58,6 +58,7 @@ PROFILE_PMC = os.path.join(ROOT, "profiles", "quantize_rowcol_activation_8192x40
 DOMINANT_SOURCES = [
     os.path.join(ROOT, "fp4_block_scaled_amax_amd", "csrc", "quantize.hip"),
     os.path.join(ROOT, "fp4_block_scaled_amax_amd", "csrc", "device.h"),
+    os.path.join(ROOT, "fp4_block_scaled_amax_amd", "csrc", "encode.h"),
 ]
 
 
@@ -76,6 +77,10 @@ def parse():
     p.add_argument("--row-iters", type=int, default=10)
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (counter calibration)")
+    p.add_argument("--summarize-trace", metavar="DIR",
+                   help="no GPU work: summarise a rocprofv3 --kernel-trace --marker-trace output directory of "
+                        "a bench.py run per bench row (needs --bench-json)")
+    p.add_argument("--bench-json", metavar="FILE", help="the JSON line that traced bench.py run printed")
     p.add_argument("--cpu-rows", type=int, default=8192,
                    help="rows of the activation in the CPU baseline sample")
     p.add_argument("--no-cpu-gemm", action="store_true",
@@ -270,8 +275,73 @@ def wgrad_product_error(F, dy, x, mask):
     return res
 
 
+def summarize_trace(trace_dir, bench_json):
+    """Per bench row: the kernels rocprofv3 traced inside the row's ROCTx
+    range (its timed calls only), with launches and average duration, the
+    kernel time per call (launch latency and the gaps between kernels left
+    out) and the fraction of peak it gives, next to the row's own
+    event-timed figure from the same run. Prints markdown."""
+    import csv
+    import glob
+
+    def one(pattern):
+        files = sorted(glob.glob(os.path.join(trace_dir, "**", pattern), recursive=True))
+        if not files:
+            raise SystemExit(f"no {pattern} under {trace_dir}")
+        return list(csv.DictReader(open(files[0])))
+
+    kernels = one("*kernel_trace.csv")
+    markers = one("*marker_api_trace.csv")
+    line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    rows = dict(line.get("rows", {}))
+    rows["step"] = {"us": line["roofline"]["avg_launch_us"], "calls": line["steps"],
+                    "alg_bytes": line["roofline"]["alg_bytes_per_launch"], "peak": HBM_PEAK_GBS}
+    ranges = {}
+    for m in markers:
+        label = next((v for v in m.values() if isinstance(v, str) and v.startswith("row:")), None)
+        if label:
+            ranges[label[4:]] = (int(m["Start_Timestamp"]), int(m["End_Timestamp"]))
+    grid_key = next(k for k in kernels[0] if k.startswith("Grid_Size"))
+    out = ["| row | kernel | grid | launches | avg µs | kernel µs per call | alg. work per call | "
+           "kernel-only rate | frac | event-timed µs per call (same run) |", "|---|---|---|---:|---:|---:|---:|---:|"
+           "---:|---:|"]
+    for name, (t0, t1) in ranges.items():
+        inside = [k for k in kernels if t0 <= int(k["Start_Timestamp"]) <= t1]
+        groups = {}
+        for k in inside:
+            kname = k["Kernel_Name"].replace("(anonymous namespace)::", "")
+            kname = re.sub(r"\([^()]*\)$", "", kname.strip())  # the parameter list
+            key = (kname.replace("void ", "")[-80:], k[grid_key])
+            groups.setdefault(key, []).append((int(k["End_Timestamp"]) - int(k["Start_Timestamp"])) / 1e3)
+        row = rows.get(name, {})
+        calls = row.get("calls") or 1
+        per_call = sum(sum(v) for v in groups.values()) / calls
+        work = row.get("alg_bytes") or row.get("flop")
+        rate = frac = ""
+        work_s = f"{work:.4g}" if work else ""
+        if work and per_call > 0:
+            if "flop" in row and "alg_bytes" not in row:
+                r = work / (per_call * 1e-6) / 1e12
+                rate = f"{r:.1f} TFLOP/s"
+                frac = f"{r / row['peak']:.3f}" if row.get("peak") else ""
+            else:
+                r = work / (per_call * 1e-6) / 1e9
+                rate = f"{r:.0f} GB/s"
+                frac = f"{r / HBM_PEAK_GBS:.3f}"
+        first = True
+        for (kname, grid), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"| {name if first else ''} | `{kname}` | {grid} | {len(ds)} | {statistics.mean(ds):.2f} | "
+                       + (f"{per_call:.2f} | {work_s} | {rate} | {frac} | {row.get('us', '')} |" if first
+                          else "| | | | |"))
+            first = False
+    print("\n".join(out))
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.bench_json)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(there is no multi-GPU path: every block is independent, and only the tensor amax "
@@ -335,19 +405,29 @@ def main():
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
+    # The K timed steps are captured once in a HIP graph (the launch-bound
+    # loop then runs without the host's per-call overhead) and replayed once
+    # as the timed region.
+    step_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(step_graph):
+        for k in range(args.steps):
+            step(k)
+    torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
+    torch.cuda.nvtx.range_push("row:step")
     t0 = time.perf_counter()
     ev_q0.record(stream)
-    for k in range(args.steps):
-        step(k)
+    step_graph.replay()
     ev_q1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    torch.cuda.nvtx.range_pop()
+    del step_graph
     ms_per_step = elapsed * 1e3 / args.steps
     value = step_bytes / (elapsed / args.steps) / 1e9
     # The dominant kernel's average launch duration: HIP events on its
     # stream around the timed region, which is K back-to-back launches of it
-    # and nothing else.
+    # (one graph replay) and nothing else.
     q_avg_ms = ev_q0.elapsed_time(ev_q1) / args.steps
     achieved = quant_bytes / (q_avg_ms * 1e-3) / 1e9
     traffic = recorded_traffic()
@@ -371,24 +451,50 @@ def main():
     if not args.no_rows:
         flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
 
-        def timed(fn, iters=args.row_iters):
-            fn()
+        def timed(name, fn, iters=2 * args.row_iters, copies=1, graph=True):
+            """Average time of one call of fn(k) over `iters` back-to-back
+            calls (k = 0, 1, ...: the call rotates over `copies` inputs whose
+            total exceeds the 256 MB Infinity Cache, so each call reads its
+            input from HBM), between two events on the launch stream. With
+            `graph` the calls are captured once in a HIP graph and the timed
+            region is one replay of it, so the host's call overhead does not
+            starve short kernels; the gaps between kernels stay in. The timed
+            calls run inside a ROCTx range named after the row, which
+            `--summarize-trace` uses to attribute rocprofv3 kernel durations
+            to the row. The cache is flushed (a 512 MiB read, no dirty lines)
+            before the timed region."""
+            for k in range(min(copies, 3)):
+                fn(k)
             torch.cuda.synchronize()
-            ts = []
-            for _ in range(iters):
-                flush.max()  # read 512 MiB: evicts the Infinity Cache, leaves no dirty lines
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
+            gr = None
+            if graph:
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    for k in range(iters):
+                        fn(k)
+                gr.replay()
                 torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1) * 1e3)
-            return statistics.median(ts)
+            flush.max()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.nvtx.range_push(f"row:{name}")
+            e0.record(stream)
+            if gr is not None:
+                gr.replay()
+            else:
+                for k in range(iters):
+                    fn(k)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            torch.cuda.nvtx.range_pop()
+            del gr
+            return e0.elapsed_time(e1) * 1e3 / iters
 
-        def row_hbm(name, us, nbytes, shape, note=None):
+        def row_hbm(name, fn, nbytes, shape, note=None, copies=1, iters=2 * args.row_iters):
+            us = timed(name, fn, iters=iters, copies=copies)
             gbs = nbytes / (us * 1e-6) / 1e9
-            rows[name] = {"shape": shape, "us": round(us, 2), "alg_bytes": nbytes,
+            rows[name] = {"shape": shape, "us": round(us, 2), "calls": iters, "alg_bytes": nbytes,
                           "GB/s": round(gbs, 1), "bound": "hbm", "peak": HBM_PEAK_GBS,
                           "frac": round(gbs / HBM_PEAK_GBS, 4)}
             if note:
@@ -398,105 +504,115 @@ def main():
         src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         src.fill_(1.0)
-        row_hbm("copy_256MiB_torch", timed(lambda: dst.copy_(src)), 2 * src.numel() * 4, [src.numel()],
+        row_hbm("copy_256MiB_torch", lambda k: dst.copy_(src), 2 * src.numel() * 4, [src.numel()],
                 note="device copy: practical streaming ceiling (read + write)")
-        row_hbm("fill_256MiB_torch", timed(lambda: dst.fill_(2.0)), src.numel() * 4, [src.numel()],
+        row_hbm("fill_256MiB_torch", lambda k: dst.fill_(2.0), src.numel() * 4, [src.numel()],
                 note="device fill: practical ceiling for write-only streams")
         del src, dst
         # The step on one input copy, back to back: the 64 MiB tensor stays in
         # the 256 MB Infinity Cache between steps (warm), unlike the headline
         # loop, which rotates copies so every step reads HBM.
-        w0 = torch.cuda.Event(enable_timing=True)
-        w1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(5):
-            F.nvfp4_quantize_1d_fused(xs[0], ws, rowwise=True, colwise=True, out=outs[0])
-        w0.record(stream)
-        for _ in range(50):
-            F.nvfp4_quantize_1d_fused(xs[0], ws, rowwise=True, colwise=True, out=outs[0])
-        w1.record(stream)
-        torch.cuda.synchronize()
-        row_hbm("step_warm_one_input_copy", w0.elapsed_time(w1) / 50 * 1e3, step_bytes, [R, C],
+        row_hbm("step_warm_one_input_copy",
+                lambda k: F.nvfp4_quantize_1d_fused(xs[0], ws, rowwise=True, colwise=True, out=outs[0]),
+                step_bytes, [R, C], iters=50,
                 note="the headline step on one input copy, 50 back-to-back launches: the input is "
                      "served from the Infinity Cache, so this is not an HBM figure")
         x = xs[0]
         n_x = R * C
-        row_hbm("amax_activation", timed(lambda: F.nvfp4_amax(x, out=amax)), 2 * n_x, [R, C])
-        row_hbm("amax_then_quantize_row_and_col_two_calls",
-                timed(lambda: (F.nvfp4_amax(x, out=amax),
-                               F.nvfp4_quantize_1d(x, amax, rowwise=True, colwise=True, out=outs[0]))),
-                n_x * 3.125, [R, C], note="nvfp4_amax + nvfp4_quantize_1d (the tensor is read twice)")
+        nc = len(xs)  # 5 activation copies: 320 MiB rotate past the Infinity Cache
         o = outs[0]
+        row_hbm("amax_activation", lambda k: F.nvfp4_amax(xs[k % nc], out=amax), 2 * n_x, [R, C], copies=nc,
+                note="two launches per call (a one-thread reset, then the reduction)")
+        row_hbm("amax_then_quantize_row_and_col_two_calls",
+                lambda k: (F.nvfp4_amax(xs[k % nc], out=amax),
+                           F.nvfp4_quantize_1d(xs[k % nc], amax, rowwise=True, colwise=True, out=o)),
+                n_x * 3.125, [R, C], copies=nc, note="nvfp4_amax + nvfp4_quantize_1d (the tensor is read twice)")
+        F.nvfp4_amax(x, out=amax)
         row_hbm("quantize_1d_rowwise_rne_activation",
-                timed(lambda: F.nvfp4_quantize_1d(x, amax, rowwise=True, colwise=False, out=o)),
-                n_x * 2.5625, [R, C])
+                lambda k: F.nvfp4_quantize_1d(xs[k % nc], amax, rowwise=True, colwise=False, out=o),
+                n_x * 2.5625, [R, C], copies=nc)
         row_hbm("quantize_1d_colwise_rne_activation",
-                timed(lambda: F.nvfp4_quantize_1d(x, amax, rowwise=False, colwise=True, out=o)),
-                n_x * 2.5625, [R, C])
+                lambda k: F.nvfp4_quantize_1d(xs[k % nc], amax, rowwise=False, colwise=True, out=o),
+                n_x * 2.5625, [R, C], copies=nc)
         row_hbm("quantize_1d_row_and_col_rne_activation",
-                timed(lambda: F.nvfp4_quantize_1d(x, amax, rowwise=True, colwise=True, out=o)),
-                n_x * 3.125, [R, C])
+                lambda k: F.nvfp4_quantize_1d(xs[k % nc], amax, rowwise=True, colwise=True, out=o),
+                n_x * 3.125, [R, C], copies=nc)
         mask = W.rht_sign_mask()
         a_rht = torch.empty(1, dtype=torch.float32, device=dev)
-        row_hbm("amax_rht_activation", timed(lambda: F.nvfp4_amax(x, rht=True, rht_mask=mask, out=a_rht)),
-                2 * n_x, [R, C])
+        row_hbm("amax_rht_activation", lambda k: F.nvfp4_amax(xs[k % nc], rht=True, rht_mask=mask, out=a_rht),
+                2 * n_x, [R, C], copies=nc, note="two launches per call (a one-thread reset, then the reduction)")
+        F.nvfp4_amax(x, rht=True, rht_mask=mask, out=a_rht)
         row_hbm("quantize_colwise_rht_sr_activation",
-                timed(lambda: F.nvfp4_quantize_1d(x, a_rht, rowwise=False, colwise=True, sr=True, rht=True,
-                                                  rht_mask=mask, seed=W.SR_SEED, out=o)),
-                n_x * 2.5625, [R, C], note=ALU_NOTE)
+                lambda k: F.nvfp4_quantize_1d(xs[k % nc], a_rht, rowwise=False, colwise=True, sr=True, rht=True,
+                                              rht_mask=mask, seed=W.SR_SEED, out=o),
+                n_x * 2.5625, [R, C], copies=nc, note=ALU_NOTE)
         deq = torch.empty((R, C), dtype=torch.float32, device=dev)
-        F.nvfp4_quantize_1d(x, amax, rowwise=True, colwise=False, out=o)
+        qo = [F.nvfp4_quantize_1d(xi, amax, rowwise=True, colwise=False) for xi in xs]
         row_hbm("dequantize_1d_fp32_activation",
-                timed(lambda: F.nvfp4_dequantize(o["codes_row"], o["scales_row"], 1, o["global_scale"], R, C,
-                                                 out=deq)), n_x * 4.5625, [R, C])
+                lambda k: F.nvfp4_dequantize(qo[k % nc]["codes_row"], qo[k % nc]["scales_row"], 1,
+                                             qo[k % nc]["global_scale"], R, C, out=deq), n_x * 4.5625, [R, C],
+                copies=nc, note="reads 18 MiB per call from 5 rotating copies (90 MiB, which the Infinity "
+                                "Cache can hold); 88% of the row's bytes are the writes")
         deq16 = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
         row_hbm("dequantize_1d_bf16_activation",
-                timed(lambda: F.nvfp4_dequantize(o["codes_row"], o["scales_row"], 1, o["global_scale"], R, C,
-                                                 out_dtype=torch.bfloat16, out=deq16)), n_x * 2.5625, [R, C])
-        del xs[1:], outs[1:], deq, deq16
+                lambda k: F.nvfp4_dequantize(qo[k % nc]["codes_row"], qo[k % nc]["scales_row"], 1,
+                                             qo[k % nc]["global_scale"], R, C, out_dtype=torch.bfloat16,
+                                             out=deq16), n_x * 2.5625, [R, C], copies=nc)
+        del xs[1:], outs[1:], deq, deq16, qo
 
         log("[bench] generating the 8192x14336 gradient")
         g_host = W.gradient()
-        g = to_dev(g_host)
+        gs = [to_dev(g_host), to_dev(g_host)]  # 448 MiB rotate past the Infinity Cache
+        g = gs[0]
         del g_host
         GR, GC = g.shape
         n_g = GR * GC
-        row_hbm("amax_rht_gradient", timed(lambda: F.nvfp4_amax(g, rht=True, rht_mask=mask, out=a_rht)),
-                2 * n_g, [GR, GC])
-        og = {}
+        row_hbm("amax_rht_gradient", lambda k: F.nvfp4_amax(gs[k % 2], rht=True, rht_mask=mask, out=a_rht),
+                2 * n_g, [GR, GC], copies=2, note="two launches per call (a one-thread reset, then the reduction)")
+        F.nvfp4_amax(g, rht=True, rht_mask=mask, out=a_rht)
         og = F.nvfp4_quantize_1d(g, a_rht, rowwise=False, colwise=True, sr=True, rht=True, rht_mask=mask,
                                  seed=W.SR_SEED)
         row_hbm("quantize_colwise_rht_sr_gradient",
-                timed(lambda: F.nvfp4_quantize_1d(g, a_rht, rowwise=False, colwise=True, sr=True, rht=True,
-                                                  rht_mask=mask, seed=W.SR_SEED, out=og)),
-                n_g * 2.5625, [GR, GC], note=ALU_NOTE)
+                lambda k: F.nvfp4_quantize_1d(gs[k % 2], a_rht, rowwise=False, colwise=True, sr=True, rht=True,
+                                              rht_mask=mask, seed=W.SR_SEED, out=og),
+                n_g * 2.5625, [GR, GC], copies=2, note=ALU_NOTE)
         y = torch.empty((GR, GC), dtype=torch.float32, device=dev)
-        row_hbm("rht16_axis0_gradient", timed(lambda: F.nvfp4_rht16(g, axis=0, rht_mask=mask, out=y)),
-                n_g * 6, [GR, GC])
+        row_hbm("rht16_axis0_gradient", lambda k: F.nvfp4_rht16(gs[k % 2], axis=0, rht_mask=mask, out=y),
+                n_g * 6, [GR, GC], copies=2)
         del y
         # What the fused transform costs: the same calls without it, and both
         # amaxes of the gradient (plain for dgrad, transformed for wgrad)
         # from one read.
         a_g = torch.empty(1, dtype=torch.float32, device=dev)
         a_both = torch.empty(2, dtype=torch.float32, device=dev)
-        row_hbm("amax_gradient", timed(lambda: F.nvfp4_amax(g, out=a_g)), 2 * n_g, [GR, GC])
+        row_hbm("amax_gradient", lambda k: F.nvfp4_amax(gs[k % 2], out=a_g), 2 * n_g, [GR, GC], copies=2,
+                note="two launches per call (a one-thread reset, then the reduction)")
         row_hbm("amax_plain_and_rht_gradient_one_read",
-                timed(lambda: F.nvfp4_amax(g, rht=True, rht_mask=mask, both=True, out=a_both)), 2 * n_g, [GR, GC],
+                lambda k: F.nvfp4_amax(gs[k % 2], rht=True, rht_mask=mask, both=True, out=a_both), 2 * n_g,
+                [GR, GC], copies=2,
                 note="nvfp4_amax(NVFP4_RHT | NVFP4_AMAX_BOTH): replaces amax_gradient + amax_rht_gradient")
+        F.nvfp4_amax(g, out=a_g)
         row_hbm("quantize_colwise_sr_gradient_no_rht",
-                timed(lambda: F.nvfp4_quantize_1d(g, a_g, rowwise=False, colwise=True, sr=True, seed=W.SR_SEED,
-                                                  out=og)),
-                n_g * 2.5625, [GR, GC], note="the RHT row's call without the transform")
-        del og
+                lambda k: F.nvfp4_quantize_1d(gs[k % 2], a_g, rowwise=False, colwise=True, sr=True,
+                                              seed=W.SR_SEED, out=og),
+                n_g * 2.5625, [GR, GC], copies=2, note="the RHT row's call without the transform")
+        del og, gs[1:]
 
         log("[bench] generating the 14336x4096 weight")
-        w = to_dev(W.weight())
+        w_host = W.weight()
+        wts = [to_dev(w_host) for _ in range(3)]  # 336 MiB rotate past the Infinity Cache
+        w = wts[0]
+        del w_host
         WR, WC = w.shape
         n_w = WR * WC
         a_w = F.nvfp4_amax(w)
         ow = F.nvfp4_quantize_2d(w, a_w)
-        row_hbm("amax_weight", timed(lambda: F.nvfp4_amax(w, out=a_w)), 2 * n_w, [WR, WC])
-        row_hbm("quantize_2d_weight", timed(lambda: F.nvfp4_quantize_2d(w, a_w, out=ow)),
-                n_w * (2 + 2 * 0.5 + 1 / 256), [WR, WC])
+        row_hbm("amax_weight", lambda k: F.nvfp4_amax(wts[k % 3], out=a_w), 2 * n_w, [WR, WC], copies=3,
+                note="two launches per call (a one-thread reset, then the reduction)")
+        F.nvfp4_amax(w, out=a_w)
+        row_hbm("quantize_2d_weight", lambda k: F.nvfp4_quantize_2d(wts[k % 3], a_w, out=ow),
+                n_w * (2 + 2 * 0.5 + 1 / 256), [WR, WC], copies=3)
+        del wts[1:]
 
         log("[bench] GEMM 8192x14336x4096")
         a_host, b_host = W.gemm_operands()
@@ -516,12 +632,12 @@ def main():
                          qb["scales"], 2, qb["global_scale"], M, N, K, out=c32)
         torch.cuda.synchronize()
         for name, cc, dt in (("gemm_fp32_out", c32, torch.float32), ("gemm_bf16_out", c16, torch.bfloat16)):
-            us = timed(lambda: F.nvfp4_gemm(qa["codes_row"], qa["scales_row"], 1, qa["global_scale"],
-                                            qb["codes_row"], qb["scales"], 2, qb["global_scale"], M, N, K,
-                                            out_dtype=dt, out=cc), iters=max(3, args.row_iters // 2))
+            us = timed(name, lambda k: F.nvfp4_gemm(qa["codes_row"], qa["scales_row"], 1, qa["global_scale"],
+                                                    qb["codes_row"], qb["scales"], 2, qb["global_scale"], M, N, K,
+                                                    out_dtype=dt, out=cc), iters=max(5, args.row_iters), graph=False)
             tf = flop / (us * 1e-6) / 1e12
-            rows[name] = {"shape": [M, N, K], "us": round(us, 1), "flop": flop, "TFLOP/s": round(tf, 1),
-                          "bound": "mfma", "peak": F16_MFMA_PEAK_TFLOPS,
+            rows[name] = {"shape": [M, N, K], "us": round(us, 1), "calls": max(5, args.row_iters), "flop": flop,
+                          "TFLOP/s": round(tf, 1), "bound": "mfma", "peak": F16_MFMA_PEAK_TFLOPS,
                           "frac": round(tf / F16_MFMA_PEAK_TFLOPS, 4)}
             log(f"[bench] {name}: {us:.0f} us {tf:.1f} TFLOP/s")
         gemm_tflops = rows["gemm_fp32_out"]["TFLOP/s"]
@@ -536,10 +652,12 @@ def main():
         for _ in range(50):
             torch.matmul(da, dbt, out=ch)
         torch.cuda.synchronize()
-        us = timed(lambda: torch.matmul(da, dbt, out=ch), iters=max(3, args.row_iters // 2))
+        us = timed("reference_hipblaslt_fp16_gemm_same_values", lambda k: torch.matmul(da, dbt, out=ch),
+                   iters=max(5, args.row_iters), graph=False)
         tf = flop / (us * 1e-6) / 1e12
         rows["reference_hipblaslt_fp16_gemm_same_values"] = {
-            "shape": [M, N, K], "us": round(us, 1), "flop": flop, "TFLOP/s": round(tf, 1),
+            "shape": [M, N, K], "us": round(us, 1), "calls": max(5, args.row_iters), "flop": flop,
+            "TFLOP/s": round(tf, 1),
             "note": "vendor fp16 GEMM on the decoded operand values (reads 4x the operand bytes, no "
                     "decode); context for gemm_fp32_out, not part of this library"}
         log(f"[bench] reference hipBLASLt fp16 GEMM on the same values: {us:.0f} us {tf:.1f} TFLOP/s")
@@ -568,8 +686,8 @@ def main():
              2.0 * R * C * WR),
             ("linear_forward_quantized_output_unfused", unfused_forward, 2.0 * R * C * WR))
         for name, fn, fl in parts:
-            us = timed(fn, iters=3)
-            rows[name] = {"shape": {"tokens": R, "in": C, "out": WR}, "us": round(us, 1)}
+            us = timed(name, lambda k: fn(), iters=5, graph=False)
+            rows[name] = {"shape": {"tokens": R, "in": C, "out": WR}, "us": round(us, 1), "calls": 5}
             if fl is not None:
                 rows[name].update({"flop": fl, "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1),
                                    "note": "GEMM flop only; the time includes the operands' quantization"})
@@ -582,19 +700,21 @@ def main():
         # the representation error of both formats.
         log("[bench] MXFP4 comparator")
         mo = F.mxfp4_quantize(x, rowwise=True, colwise=True)
-        row_hbm("mx_quantize_rowwise_activation", timed(lambda: F.mxfp4_quantize(x, out=mo)),
+        # (one input copy each: these rows read a tensor the Infinity Cache
+        # can partly hold between calls)
+        row_hbm("mx_quantize_rowwise_activation", lambda k: F.mxfp4_quantize(x, out=mo),
                 n_x * (2 + 0.5 + 1 / 32), [R, C])
         row_hbm("mx_quantize_row_and_col_activation",
-                timed(lambda: F.mxfp4_quantize(x, rowwise=True, colwise=True, out=mo)),
+                lambda k: F.mxfp4_quantize(x, rowwise=True, colwise=True, out=mo),
                 n_x * (2 + 2 * (0.5 + 1 / 32)), [R, C])
         mg = F.mxfp4_quantize(g, rowwise=False, colwise=True, rht=True, rht_mask=mask)
         row_hbm("mx_quantize_colwise_rht_gradient",
-                timed(lambda: F.mxfp4_quantize(g, rowwise=False, colwise=True, rht=True, rht_mask=mask, out=mg)),
+                lambda k: F.mxfp4_quantize(g, rowwise=False, colwise=True, rht=True, rht_mask=mask, out=mg),
                 n_g * (2 + 0.5 + 1 / 32), [GR, GC])
         mdq = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
         row_hbm("mx_dequantize_bf16_activation",
-                timed(lambda: F.mxfp4_dequantize(mo["codes_row"], mo["scales_row"], R, C, out_dtype=torch.bfloat16,
-                                                 out=mdq)), n_x * (0.5 + 1 / 32 + 2), [R, C])
+                lambda k: F.mxfp4_dequantize(mo["codes_row"], mo["scales_row"], R, C, out_dtype=torch.bfloat16,
+                                             out=mdq), n_x * (0.5 + 1 / 32 + 2), [R, C])
         del mdq
         ma = F.mxfp4_quantize(A)
         mb = F.mxfp4_quantize(Bm)
@@ -602,11 +722,12 @@ def main():
             F.mxfp4_gemm(ma["codes_row"], ma["scales_row"], mb["codes_row"], mb["scales_row"], M, N, K, out=c32)
         torch.cuda.synchronize()
         for name, cc, dt in (("mx_gemm_fp32_out", c32, torch.float32), ("mx_gemm_bf16_out", c16, torch.bfloat16)):
-            us = timed(lambda: F.mxfp4_gemm(ma["codes_row"], ma["scales_row"], mb["codes_row"], mb["scales_row"],
-                                            M, N, K, out_dtype=dt, out=cc), iters=max(3, args.row_iters // 2))
+            us = timed(name, lambda k: F.mxfp4_gemm(ma["codes_row"], ma["scales_row"], mb["codes_row"],
+                                                    mb["scales_row"], M, N, K, out_dtype=dt, out=cc),
+                       iters=max(5, args.row_iters), graph=False)
             tf = flop / (us * 1e-6) / 1e12
-            rows[name] = {"shape": [M, N, K], "us": round(us, 1), "flop": flop, "TFLOP/s": round(tf, 1),
-                          "bound": "mfma", "peak": FP4_MFMA_PEAK_TFLOPS,
+            rows[name] = {"shape": [M, N, K], "us": round(us, 1), "calls": max(5, args.row_iters), "flop": flop,
+                          "TFLOP/s": round(tf, 1), "bound": "mfma", "peak": FP4_MFMA_PEAK_TFLOPS,
                           "frac": round(tf / FP4_MFMA_PEAK_TFLOPS, 4)}
             log(f"[bench] {name}: {us:.0f} us {tf:.1f} TFLOP/s")
         del ma, mb, mo, mg
@@ -625,7 +746,8 @@ def main():
         ref = oracle.quantize_1d(sample, rowwise=True, colwise=True)
         t_cpu = time.perf_counter() - t0
         ns = sample.size
-        cpu = {"value": round(ns * (2 + 2 + 2 * 0.5625) / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
+        # the step's algorithmic bytes, as for the GPU value: the input once and both outputs
+        cpu = {"value": round(ns * 3.125 / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
                "kind": "oracle",
                "sample": f"first {args.cpu_rows} rows of the activation ({args.cpu_rows}x{C}), amax + rowwise "
                          f"+ columnwise 1D RNE quantize as one tensor; {t_cpu:.1f} s single-threaded",
