@@ -24,14 +24,6 @@
 #include "device.h"
 #include "kernels.h"
 
-// Wave grid of a workgroup (256 x 256 tile): 2 x 4 waves of 128 x 64.
-#ifndef MX_GEMM_WAVES_M
-#define MX_GEMM_WAVES_M 2
-#endif
-#ifndef MX_GEMM_WAVES_N
-#define MX_GEMM_WAVES_N 4
-#endif
-
 namespace nvfp4 {
 
 namespace {
@@ -334,7 +326,7 @@ int mx_gemm_capacity()
 template <bool BF16_OUT, bool ALIGNED>
 hipError_t launch_mx_variant(const MxGemmArgs& a, int tiles_m, int tiles_n, hipStream_t stream)
 {
-    constexpr int WM = MX_GEMM_WAVES_M, WN = MX_GEMM_WAVES_N;
+    constexpr int WM = 2, WN = 4;  // wave grid of the 256 x 256 tile: 2 x 4 waves of 128 x 64
     const int cap = mx_gemm_capacity<WM, WN, BF16_OUT, ALIGNED>();
     if (cap <= 0)
         return hipErrorInvalidDevice;
