@@ -781,6 +781,19 @@ def main():
         "cpu_baseline_all_cores": cpu_all,
         "cpu_gemm_reference": cpu_gemm,
         "rows": rows,
+        # The pages' own figures, with their hardware: context only, not
+        # targets, and not comparable to any row above (they measure NVFP4
+        # GEMM peak rates and end-to-end training on other parts).
+        "pages_context": {
+            "nvfp4_gemm_peak_vs_fp8": {"value": "2-3x", "hardware": "GB200, GB300",
+                                       "source": "page 'Melatih model dalam 4 bit', section 'Presisi sebagai "
+                                                 "tombol throughput'"},
+            "training_tflops_per_gpu_nvfp4_vs_fp8": {
+                "llama3_8b": {"GB200": "2017 vs 1497 (1.35x)", "GB300": "2301 vs 1759 (1.31x)"},
+                "llama3.1_405b": {"GB200": "2241 vs 1557 (1.44x)", "GB300": "3633 vs 2103 (1.73x)"},
+                "setup": "vendor JAX/MaxText measurement",
+                "source": "page 'Melatih model dalam 4 bit', section 'Angka yang dilaporkan'"},
+        },
     }
     print(json.dumps(line), flush=True)
 
