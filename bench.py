@@ -5,9 +5,9 @@ Timed step (the workload the metric is quoted on): the 8192x4096 bf16
 activation (tokens x hidden, N(0,1) with 8 outlier columns x100) goes
 through the whole 1D path -- tensor amax, global scale, E4M3 block scales,
 E2M1 round-to-nearest-even and packing -- emitting both the rowwise (fprop)
-and the columnwise (wgrad) layouts, in one call (nvfp4_quantize_1d with
-NVFP4_FUSED_AMAX: a single pass over the tensor, which stays in registers
-between the amax and the encoding). `value` is the step's algorithmic bytes
+and the columnwise (wgrad) layouts, in one call (nvfp4_quantize_1d_fused: a single
+pass over the tensor, which stays in registers between the amax and the
+encoding). `value` is the step's algorithmic bytes
 -- the input read once (2 B/element) plus the two outputs (2 x 0.5625
 B/element) -- per second.
 
