@@ -59,6 +59,7 @@ DOMINANT_SOURCES = [
     os.path.join(ROOT, "fp4_block_scaled_amax_amd", "csrc", "quantize.hip"),
     os.path.join(ROOT, "fp4_block_scaled_amax_amd", "csrc", "device.h"),
     os.path.join(ROOT, "fp4_block_scaled_amax_amd", "csrc", "encode.h"),
+    os.path.join(ROOT, "fp4_block_scaled_amax_amd", "csrc", "quant_item.h"),
 ]
 
 

@@ -51,6 +51,7 @@ EXPORTS = (
     "nvfp4_dequantize",
     "nvfp4_gemm",
     "nvfp4_gemm_amax",
+    "nvfp4_gemm_quantize",
     "mxfp4_quantize",
     "mxfp4_dequantize",
     "mxfp4_gemm",
@@ -101,6 +102,8 @@ def lib():
     L.nvfp4_gemm.argtypes = [P, P, I, P, P, P, I, P, P, I, I64, I64, I64, P]
     L.nvfp4_gemm_amax.restype = I
     L.nvfp4_gemm_amax.argtypes = [P, P, I, P, P, P, I, P, P, I, I64, I64, I64, P, P]
+    L.nvfp4_gemm_quantize.restype = I
+    L.nvfp4_gemm_quantize.argtypes = [P, P, I, P, P, P, I, P, I64, I64, I64, P, U32, P, P, P, P, P, P, P]
     L.mxfp4_quantize.restype = I
     L.mxfp4_quantize.argtypes = [P, I64, I64, U32, U16, P, P, P, P, P]
     L.mxfp4_dequantize.restype = I
@@ -190,10 +193,13 @@ def nvfp4_workspace(device=None):
 
 
 def _q1_outputs(x, rowwise, colwise, out):
-    torch = _torch()
     R, C = x.shape
+    return _q1_outputs_of(R, C, x.device, rowwise, colwise, out)
+
+
+def _q1_outputs_of(R, C, dev, rowwise, colwise, out):
+    torch = _torch()
     out = dict(out or {})
-    dev = x.device
     if rowwise:
         out["codes_row"] = _empty((R, C // 2), torch.uint8, dev, out.get("codes_row"))
         out["scales_row"] = _empty((R, C // 16), torch.uint8, dev, out.get("scales_row"))
@@ -348,6 +354,36 @@ def nvfp4_gemm(a_codes, a_scales, a_scale_mode: int, a_global_scale, b_codes, b_
     _check(lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), a_scale_mode, _ptr(a_global_scale),
                             _ptr(b_codes), _ptr(b_scales), b_scale_mode, _ptr(b_global_scale),
                             _ptr(out), dt, M, N, K, _stream(stream)))
+    return out
+
+
+def nvfp4_gemm_quantize(a_codes, a_scales, a_scale_mode: int, a_global_scale, b_codes, b_scales,
+                        b_scale_mode: int, b_global_scale, M: int, N: int, K: int, amax,
+                        rowwise: bool = True, colwise: bool = True, out: dict | None = None,
+                        out_amax=None, stream=None):
+    """The NVFP4 quantization of the bf16 product A * B^T, made by the GEMM's
+    epilogue (C is never stored): the dict nvfp4_quantize_1d(Y, amax, ...)
+    returns for Y = nvfp4_gemm(..., out_dtype=bfloat16). amax: float32 [1],
+    the tensor amax the quantization takes (for instance the previous
+    product's out_amax). out_amax: optional float32 [1] that receives max |Y|
+    of this product."""
+    torch = _torch()
+    for name, t in (("a_codes", a_codes), ("a_scales", a_scales), ("b_codes", b_codes),
+                    ("b_scales", b_scales)):
+        _dev_tensor(t, name, torch.uint8)
+    _dev_tensor(a_global_scale, "a_global_scale", torch.float32)
+    _dev_tensor(b_global_scale, "b_global_scale", torch.float32)
+    _dev_tensor(amax, "amax", torch.float32)
+    if out_amax is not None:
+        _dev_tensor(out_amax, "out_amax", torch.float32)
+    out = _q1_outputs_of(M, N, a_codes.device, rowwise, colwise, out)
+    flags = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
+    _check(lib().nvfp4_gemm_quantize(
+        _ptr(a_codes), _ptr(a_scales), a_scale_mode, _ptr(a_global_scale),
+        _ptr(b_codes), _ptr(b_scales), b_scale_mode, _ptr(b_global_scale), M, N, K,
+        _ptr(amax), flags, _ptr(out.get("codes_row")), _ptr(out.get("scales_row")),
+        _ptr(out.get("codes_col")), _ptr(out.get("scales_col")), _ptr(out["global_scale"]),
+        _ptr(out_amax), _stream(stream)))
     return out
 
 

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libnvfp4.so")
 
 SOURCES = ["api.hip", "amax.hip", "quantize.hip", "rht_dequant.hip", "gemm.hip", "mx_quantize.hip",
            "mx_gemm.hip"]
-HEADERS = ["device.h", "encode.h", "kernels.h"]
+HEADERS = ["device.h", "encode.h", "kernels.h", "quant_item.h"]
 
 ARCH = "gfx950"
 FLAGS = [

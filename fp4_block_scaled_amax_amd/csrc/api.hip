@@ -281,13 +281,17 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int scale_mode
 
 namespace {
 
+// Validation and arguments shared by the GEMM entry points; c == nullptr
+// only with a quantizing epilogue (q->q_flags != 0), whose fields q supplies.
 int gemm_common(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode,
                 const float* a_global_scale, const uint8_t* b_codes, const uint8_t* b_scales,
                 int b_scale_mode, const float* b_global_scale, void* c, int c_dtype, int64_t M,
-                int64_t N, int64_t K, float* c_amax, hipStream_t stream)
+                int64_t N, int64_t K, float* c_amax, hipStream_t stream,
+                const nvfp4::GemmArgs* q = nullptr)
 {
+    const bool quant = q != nullptr && q->q_flags != 0;
     if (a_codes == nullptr || a_scales == nullptr || a_global_scale == nullptr ||
-        b_codes == nullptr || b_scales == nullptr || b_global_scale == nullptr || c == nullptr)
+        b_codes == nullptr || b_scales == nullptr || b_global_scale == nullptr || (c == nullptr && !quant))
         return NVFP4_ERR_NULL;
     if (a_scale_mode < NVFP4_SCALE_1D || a_scale_mode > NVFP4_SCALE_2D_T ||
         b_scale_mode < NVFP4_SCALE_1D || b_scale_mode > NVFP4_SCALE_2D_T ||
@@ -298,9 +302,11 @@ int gemm_common(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mod
     if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N) || M / 128 >= 65535 ||
         N / 128 >= (1 << 30))
         return NVFP4_ERR_SIZE;
-    if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(c))
+    if (!aligned16(a_codes) || !aligned16(b_codes) || (!quant && !aligned16(c)))
         return NVFP4_ERR_ALIGN;
     nvfp4::GemmArgs g{};
+    if (quant)
+        g = *q;
     g.a_codes = a_codes;
     g.a_scales = a_scales;
     g.a_two_d = a_scale_mode != NVFP4_SCALE_1D;
@@ -342,6 +348,35 @@ int nvfp4_gemm_amax(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale
         return NVFP4_ERR_ALIGN;
     return gemm_common(a_codes, a_scales, a_scale_mode, a_global_scale, b_codes, b_scales, b_scale_mode,
                        b_global_scale, c, c_dtype, M, N, K, c_amax, stream);
+}
+
+int nvfp4_gemm_quantize(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode,
+                        const float* a_global_scale, const uint8_t* b_codes, const uint8_t* b_scales,
+                        int b_scale_mode, const float* b_global_scale, int64_t M, int64_t N,
+                        int64_t K, const float* y_amax, uint32_t flags, uint8_t* codes_row,
+                        uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                        float* global_scale, float* c_amax, hipStream_t stream)
+{
+    if ((flags & ~(NVFP4_ROWWISE | NVFP4_COLWISE)) != 0 || (flags & (NVFP4_ROWWISE | NVFP4_COLWISE)) == 0)
+        return NVFP4_ERR_FLAGS;
+    const bool row = (flags & NVFP4_ROWWISE) != 0, col = (flags & NVFP4_COLWISE) != 0;
+    if (y_amax == nullptr || (row && (codes_row == nullptr || scales_row == nullptr)) ||
+        (col && (codes_col == nullptr || scales_col == nullptr)))
+        return NVFP4_ERR_NULL;
+    if ((row && (!aligned16(codes_row) || !aligned16(scales_row))) ||
+        (col && (!aligned16(codes_col) || !aligned16(scales_col))) ||
+        (c_amax != nullptr && (reinterpret_cast<uintptr_t>(c_amax) & 3u) != 0))
+        return NVFP4_ERR_ALIGN;
+    nvfp4::GemmArgs q{};
+    q.q_flags = (row ? 1u : 0u) | (col ? 2u : 0u);
+    q.q_amax = y_amax;
+    q.q_codes_row = row ? codes_row : nullptr;
+    q.q_scales_row = row ? scales_row : nullptr;
+    q.q_codes_col = col ? codes_col : nullptr;
+    q.q_scales_col = col ? scales_col : nullptr;
+    q.q_global_scale = global_scale;
+    return gemm_common(a_codes, a_scales, a_scale_mode, a_global_scale, b_codes, b_scales, b_scale_mode,
+                       b_global_scale, nullptr, NVFP4_BF16, M, N, K, c_amax, stream, &q);
 }
 
 int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,

@@ -39,6 +39,7 @@
 
 #include "device.h"
 #include "kernels.h"
+#include "quant_item.h"
 
 namespace nvfp4 {
 
@@ -49,7 +50,7 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(16))) float floatx16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
-constexpr int kThreads = 512;
+constexpr int kGemmThreads = 512;
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kGroupM = 4;  // tile rows per group of the tile order
@@ -264,6 +265,105 @@ __device__ __forceinline__ void stage_tile_scales(uint8_t* dst, const uint8_t* s
     }
 }
 
+// Quantizing epilogue (QUANT: 1 rowwise, 2 columnwise, 3 both): the tile's
+// bf16 values go to LDS at a padded pitch, then each of the 512 threads
+// quantizes one 16 x 8 work item of it with the item code of the quantize
+// kernels (the 256 x 256 tile is two 128 x 256 quantize tiles, A above B),
+// so the codes equal those nvfp4_quantize_1d writes for the bf16 C.
+constexpr int kQuantPitch = 2 * kBN + 16;                    // bytes per tile row
+constexpr int kQuantRcp = kQuantPitch * kBM;                 // reciprocal table offset
+constexpr int kQuantLds = kQuantRcp + 128 * 4;
+constexpr int kQuantStageCodes = kTileC * kRowBlocks * 8;    // one quantize tile's staged codes
+static_assert(2 * kQuantStageCodes + 2 * kTileC * kRowBlocks <= kQuantRcp, "staging overlays the tile");
+static_assert(kQuantLds <= 160 * 1024, "LDS");
+static_assert(kBM == 2 * kTileR && kBN == kTileC, "a GEMM tile is a pair of quantize tiles");
+
+template <int QUANT>
+__device__ __forceinline__ void quant_epilogue(const GemmArgs& g, const floatx16 (&acc)[2][4], float scale,
+                                               int64_t m0, int64_t n0, int wm, int wn, int lane, int wave,
+                                               int round, uint8_t* lds_in, uint32_t& cmax)
+{
+    constexpr bool QROW = (QUANT & 1) != 0, QCOL = (QUANT & 2) != 0;
+    const int t = threadIdx.x;
+    // An opaque zero keeps this epilogue's addresses from being hoisted out
+    // of the tile loop (where they would stay live across the K loop).
+    uint32_t zero = 0u;
+    asm volatile("" : "+v"(zero));
+    uint8_t* const lds = lds_in + zero;
+    const int ln = lane + (int)zero;
+    const int mlim = (int)min(g.M - m0, (int64_t)kBM), nlim = (int)min(g.N - n0, (int64_t)kBN);
+    // 1. C x fl(S_gA S_gB), rounded to bf16 (nearest even), into LDS; the
+    //    K loop's last barrier has passed, so the stage buffers are free.
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int cl = wn + b * 32 + (ln & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int rl = wm + a * 32 + 8 * (i >> 2) + 4 * (ln >> 5) + (i & 3);
+                const uint32_t u = __float_as_uint(acc[a][b][i] * scale);
+                const uint16_t h = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                *reinterpret_cast<uint16_t*>(lds + rl * kQuantPitch + 2 * cl) = h;
+                if (rl < mlim && cl < nlim)
+                    cmax = max(cmax, (uint32_t)(h & 0x7FFFu) << 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 tile at a time
+        }
+    const ScaleCtx sc = scale_ctx(*g.q_amax);
+    float* const rcp = reinterpret_cast<float*>(lds + kQuantRcp);
+    build_reciprocal_table(rcp, sc.sg);
+    if (g.q_global_scale != nullptr && blockIdx.x == 0 && t == 0 && round == 0)
+        *g.q_global_scale = sc.sg;
+    __syncthreads();
+
+    // 2. One work item per thread: tile rows 16 rb .. 16 rb + 15 (rb = 2 wave
+    //    + half-wave; rb < 8 in quantize tile A, else B), columns 8 cg ..
+    //    8 cg + 7, read into registers before the staging overwrites the tile.
+    const int rb = 2 * wave + (ln >> 5), cg = ln & 31;
+    uint4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        v[i] = *reinterpret_cast<const uint4*>(lds + (rb * 16 + i) * kQuantPitch + cg * 16);
+    ItemPos q;
+    q.tile_r0 = m0 + (rb >> 3) * kTileR;
+    q.tile_c0 = n0;
+    q.rb = rb & 7;
+    q.cg = cg;
+    q.odd = (ln & 1) != 0;
+    q.r0 = m0 + rb * 16;
+    q.c0 = n0 + cg * 8;
+    q.valid = q.r0 < g.M && q.c0 < g.N;  // both lanes of a pair agree (N % 16 == 0)
+    Params p{};
+    p.rows = g.M;
+    p.cols = g.N;
+    p.codes_row = g.q_codes_row;
+    p.scales_row = g.q_scales_row;
+    p.codes_col = g.q_codes_col;
+    p.scales_col = g.q_scales_col;
+    uint2* const codes0 = reinterpret_cast<uint2*>(lds);
+    uint2* const codes1 = reinterpret_cast<uint2*>(lds + kQuantStageCodes);
+    uint8_t* const scales0 = lds + 2 * kQuantStageCodes;
+    uint8_t* const scales1 = scales0 + kTileC * kRowBlocks;
+    __syncthreads();
+    if (q.valid) {
+        BlockMax bm;
+        if (QCOL)
+            column_maxima(v, bm);
+        if (QROW)
+            row_maxima(v, q.odd, bm);
+        uint4 draws[16];  // unused: round to nearest
+        compute_item<QROW, QCOL, false, false, false>(p, q, v, bm, draws, sc, rcp, rb < 8 ? codes0 : codes1,
+                                                      rb < 8 ? scales0 : scales1, false);
+    }
+    if (QCOL) {
+        __syncthreads();
+        if (t < kThreads)  // the pair writer's 256 threads
+            write_col_pair(p, m0, n0, codes0, codes1, scales0, scales1);
+    }
+    __syncthreads();  // the next tile's first stage overwrites this LDS
+}
+
 // AMAX: also reduce max |C| over the values as stored (bf16 or fp32 bit
 // patterns, an integer maximum like nvfp4_amax's) into *g.c_amax, which the
 // launch has reset: a running maximum per lane over its tiles, one atomic
@@ -274,16 +374,22 @@ __device__ __forceinline__ void stage_tile_scales(uint8_t* dst, const uint8_t* s
 // unit u being half u & 1 of tile first + u / 2: a partial last round of
 // whole tiles, split so that it fills twice as many CUs. Every output
 // element is summed in the same order either way.
-template <bool BF16_OUT, bool WIDE, bool AMAX, int KS, int FN>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int first,
+template <bool BF16_OUT, bool WIDE, bool AMAX, int KS, int FN, int QUANT = 0>
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int first,
                                                         int count)
 {
     constexpr int kRowBytes = Geo<KS>::kRowBytes;
     constexpr int kStageBytes = Geo<KS>::kStageBytes;
     constexpr int kLdsScaleK = Geo<KS>::kLdsScaleK;
+    constexpr int kMainLds = 2 * kStageBytes + 2 * kLdsScaleK;
+    constexpr int kLdsBytes = (QUANT != 0 && kQuantLds > kMainLds) ? kQuantLds : kMainLds;
+    static_assert(QUANT == 0 || (FN == 4 && BF16_OUT && AMAX), "the quantizing epilogue takes whole tiles");
     uint32_t cmax = 0u;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2 * kLdsScaleK];  // A, B tile scales
+    // Two K stages, then the A and B tile-scale regions; the quantizing
+    // epilogue reuses the whole array once a tile's K loop is done.
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[kLdsBytes];
+    uint8_t* const lds = lds_all;
+    uint8_t* const lds_sc = lds_all + 2 * kStageBytes;  // A, B tile scales
 
     const int64_t K = g.K;
     const int t = threadIdx.x;
@@ -397,6 +503,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
             __syncthreads();  // buffer 0 is rewritten by the next tile
         }
 
+        if constexpr (QUANT != 0) {
+            quant_epilogue<QUANT>(g, acc, scale, m0, n0, wm, wn, lane, wave, round, lds, cmax);
+            continue;
+        }
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -424,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g, int tiles_m,
                 }
             }
     }
-    if (AMAX) {
+    if (AMAX && g.c_amax != nullptr) {
         cmax = wave_max_u32(cmax);
         if ((threadIdx.x & 63) == 0)
             atomicMax(reinterpret_cast<uint32_t*>(g.c_amax), cmax);
@@ -435,7 +545,7 @@ __global__ void gemm_amax_reset_kernel(float* a) { *reinterpret_cast<uint32_t*>(
 
 // Workgroups resident at once on the current device (one per CU at this
 // tile size), cached per device.
-template <bool BF16_OUT, bool WIDE, bool AMAX, int KS>
+template <bool BF16_OUT, bool WIDE, bool AMAX, int KS, int QUANT = 0>
 int gemm_capacity()
 {
     static std::atomic<int> cache[64];
@@ -447,7 +557,7 @@ int gemm_capacity()
         return c;
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(gemm_kernel<BF16_OUT, WIDE, AMAX, KS, 4>), kThreads, 0) !=
+            &per_cu, reinterpret_cast<const void*>(gemm_kernel<BF16_OUT, WIDE, AMAX, KS, 4, QUANT>), kGemmThreads, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
@@ -474,11 +584,37 @@ hipError_t launch_variant(const GemmArgs& a, int tiles_m, int tiles_n, hipStream
         hipLaunchKernelGGL(gemm_amax_reset_kernel, dim3(1), dim3(1), 0, stream, a.c_amax);
     if (whole > 0)
         hipLaunchKernelGGL((gemm_kernel<BF16_OUT, WIDE, AMAX, KS, 4>), dim3((unsigned)(whole < cap ? whole : cap)),
-                           dim3(kThreads), 0, stream, a, tiles_m, tiles_n, 0, whole);
+                           dim3(kGemmThreads), 0, stream, a, tiles_m, tiles_n, 0, whole);
     if (split_tail)
-        hipLaunchKernelGGL((gemm_kernel<BF16_OUT, WIDE, AMAX, KS, 2>), dim3((unsigned)(2 * rem)), dim3(kThreads), 0,
+        hipLaunchKernelGGL((gemm_kernel<BF16_OUT, WIDE, AMAX, KS, 2>), dim3((unsigned)(2 * rem)), dim3(kGemmThreads), 0,
                            stream, a, tiles_m, tiles_n, whole, 2 * rem);
     return hipGetLastError();
+}
+
+// The quantizing epilogue: whole tiles only, on a persistent grid.
+template <bool WIDE, int KS, int QUANT>
+hipError_t launch_quant_variant(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t stream)
+{
+    const int cap = gemm_capacity<true, WIDE, true, KS, QUANT>();
+    if (cap <= 0)
+        return hipErrorInvalidDevice;
+    const int nt = tiles_m * tiles_n;
+    if (a.c_amax != nullptr)
+        hipLaunchKernelGGL(gemm_amax_reset_kernel, dim3(1), dim3(1), 0, stream, a.c_amax);
+    hipLaunchKernelGGL((gemm_kernel<true, WIDE, true, KS, 4, QUANT>), dim3((unsigned)(nt < cap ? nt : cap)),
+                       dim3(kGemmThreads), 0, stream, a, tiles_m, tiles_n, 0, nt);
+    return hipGetLastError();
+}
+
+template <bool WIDE, int KS>
+hipError_t launch_quant(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t stream)
+{
+    switch (a.q_flags) {
+    case 1: return launch_quant_variant<WIDE, KS, 1>(a, tiles_m, tiles_n, stream);
+    case 2: return launch_quant_variant<WIDE, KS, 2>(a, tiles_m, tiles_n, stream);
+    case 3: return launch_quant_variant<WIDE, KS, 3>(a, tiles_m, tiles_n, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <bool BF16_OUT, bool WIDE, int KS>
@@ -500,6 +636,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream)
     const bool k64 = (a.K % 64) == 0 && ((reinterpret_cast<uintptr_t>(a.a_scales) & 3) == 0) &&
                      ((reinterpret_cast<uintptr_t>(a.b_scales) & 3) == 0);
     const bool wide = (a.K % 32) == 0;
+    if (a.q_flags != 0) {
+        if (k64)
+            return launch_quant<true, 64>(a, tiles_m, tiles_n, stream);
+        return wide ? launch_quant<true, 32>(a, tiles_m, tiles_n, stream)
+                    : launch_quant<false, 32>(a, tiles_m, tiles_n, stream);
+    }
     if (k64)
         return a.c_bf16 ? launch_amax_or_not<true, true, 64>(a, tiles_m, tiles_n, stream)
                         : launch_amax_or_not<false, true, 64>(a, tiles_m, tiles_n, stream);

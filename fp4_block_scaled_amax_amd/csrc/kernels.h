@@ -56,6 +56,17 @@ struct GemmArgs {
     bool c_bf16;
     int64_t M, N, K;
     float* c_amax;  // optional: max |C| of the stored values
+    // Quantizing epilogue (q_flags: 1 rowwise, 2 columnwise, 3 both; 0 to
+    // store C): C is not stored; its bf16 values are quantized to NVFP4 with
+    // the tensor amax *q_amax into the four outputs (nvfp4_quantize_1d's
+    // layouts), and *q_global_scale (optional) receives S_g.
+    uint32_t q_flags;
+    const float* q_amax;
+    uint8_t* q_codes_row;
+    uint8_t* q_scales_row;
+    uint8_t* q_codes_col;
+    uint8_t* q_scales_col;
+    float* q_global_scale;
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 

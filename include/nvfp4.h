@@ -291,6 +291,44 @@ int nvfp4_gemm_amax(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale
                     int b_scale_mode, const float* b_global_scale, void* c, int c_dtype, int64_t M,
                     int64_t N, int64_t K, float* c_amax, hipStream_t stream);
 
+/*
+ * nvfp4_gemm_quantize -- nvfp4_gemm whose epilogue quantizes the product
+ * instead of storing it: the output that a following NVFP4 quantization of
+ * the layer's output would write, produced by the GEMM that makes that
+ * output (the quantization fused into the producer's epilogue; in the
+ * pages' recipe the inputs of the MLP's three GEMMs are NVFP4, page
+ * "Melatih model dalam 4 bit", section "Empat pengaman yang membuat 4 bit
+ * bisa konvergen"). C is never written to memory.
+ * The result equals, byte for byte,
+ *   nvfp4_gemm(..., Y, NVFP4_BF16, ...) followed by
+ *   nvfp4_quantize_1d(Y, M, N, y_amax, flags, 0, 0, codes_row, scales_row,
+ *                     codes_col, scales_col, global_scale):
+ * the bf16 product (each element rounded to nearest even after the
+ * fl(S_gA * S_gB) multiply) quantized with round-to-nearest-even E2M1 codes
+ * and the global scale S_g derived from *y_amax.
+ * The tensor amax must be known before the first tile is quantized, so the
+ * caller supplies it: for instance the amax this call reported for the same
+ * layer's previous product (c_amax below), or any bound on max |Y|. Blocks
+ * whose maximum exceeds it saturate exactly as nvfp4_quantize_1d's do.
+ *   y_amax   device float: the amax the quantization takes
+ *   flags    NVFP4_ROWWISE and/or NVFP4_COLWISE (no stochastic rounding,
+ *            no transform)
+ *   codes_row [M][N/2], scales_row [M][N/16], codes_col [N][M/2],
+ *   scales_col [N][M/16] for the layouts flags selects (16-byte aligned)
+ *   global_scale  optional device float: receives S_g
+ *   c_amax   optional device float (4-byte aligned): receives max |Y| of
+ *            this product (as nvfp4_gemm_amax with a bf16 C reports it),
+ *            reset stream-ordered before the GEMM
+ * A, B, their scales and global scales, M, N, K: as nvfp4_gemm (M, N, K
+ * multiples of 16).
+ */
+int nvfp4_gemm_quantize(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_mode,
+                        const float* a_global_scale, const uint8_t* b_codes, const uint8_t* b_scales,
+                        int b_scale_mode, const float* b_global_scale, int64_t M, int64_t N,
+                        int64_t K, const float* y_amax, uint32_t flags, uint8_t* codes_row,
+                        uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                        float* global_scale, float* c_amax, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

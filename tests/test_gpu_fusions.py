@@ -6,6 +6,11 @@ against the unfused calls.
 - nvfp4_gemm_amax: the GEMM's epilogue reduces max |C| of the stored values;
   C is bit-identical to nvfp4_gemm's and the amax bit-equal to nvfp4_amax of
   C (bf16) or the host maximum (fp32).
+- nvfp4_gemm_quantize: the GEMM's epilogue quantizes the bf16 product with a
+  given amax instead of storing it; every output byte equals the unfused
+  nvfp4_gemm (bf16) + nvfp4_quantize_1d with that amax and the oracle's
+  quantization of that bf16 product, for the true amax, a smaller one
+  (saturating blocks) and a larger one; its reported amax is max |Y|.
 - linear.forward_quantized: Y's quantization from the epilogue amax equals
   the oracle's quantization of Y; linear.training_step (one read of dY for
   both amaxes) equals the calls composed without the fusion, bit for bit.
@@ -158,3 +163,59 @@ def test_training_step_equals_unfused_calls():
     dw = L.wgrad(dyd, xd, MASK, 42)              # its own transform amax
     for k, ref in (("y", y), ("dx", dx), ("dw", dw)):
         assert np.array_equal(host(out[k]).view(np.uint32), host(ref).view(np.uint32)), k
+
+
+GQ_CASES = [
+    # (M, N, K, b_scale_mode, layouts)
+    (272, 400, 528, 2, "both"),     # ragged tiles in M and N, 64-deep stages
+    (2064, 8208, 48, 1, "both"),    # K an odd multiple of 16 (32-deep stages, one-block tail)
+    (528, 784, 96, 1, "row"),
+    (528, 784, 96, 2, "col"),
+    (256, 256, 64, 2, "both"),      # one whole tile
+    (8192, 14336, 4096, 2, "both"),  # the linear layer's fprop shape
+]
+
+
+@pytest.mark.parametrize("M,N,K,bmode,layouts", GQ_CASES)
+def test_gemm_quantize_epilogue(M, N, K, bmode, layouts):
+    log(f"[test_gemm_quantize_epilogue] {M}x{N}x{K} b_mode {bmode} {layouts}")
+    rowwise, colwise = layouts in ("both", "row"), layouts in ("both", "col")
+    a = W.normal_tensor(M, K, seed=92)
+    b = W.normal_tensor(N, K, seed=93, std=0.02)
+    ad, bd = dev(a), dev(b)
+    qa = F.nvfp4_quantize_1d(ad, F.nvfp4_amax(ad))
+    if bmode == 2:
+        qb = F.nvfp4_quantize_2d(bd, F.nvfp4_amax(bd), colwise=False)
+        bc, bs = qb["codes_row"], qb["scales"]
+    else:
+        qb = F.nvfp4_quantize_1d(bd, F.nvfp4_amax(bd))
+        bc, bs = qb["codes_row"], qb["scales_row"]
+    args = (qa["codes_row"], qa["scales_row"], 1, qa["global_scale"], bc, bs, bmode, qb["global_scale"], M, N, K)
+    y = F.nvfp4_gemm(*args, out_dtype=torch.bfloat16)
+    y_amax = F.nvfp4_amax(y)
+    yh = host16(y)
+    for scale_by in (1.0, 0.25, 3.0):
+        # the oracle over every element (at the largest shape for the true amax only)
+        full = M * N <= 40 << 20 or scale_by == 1.0
+        given = y_amax * scale_by
+        out_amax = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+        got = F.nvfp4_gemm_quantize(*args, given, rowwise=rowwise, colwise=colwise, out_amax=out_amax)
+        ref = F.nvfp4_quantize_1d(y, given, rowwise=rowwise, colwise=colwise)
+        keys = ["global_scale"] + (["codes_row", "scales_row"] if rowwise else []) + \
+            (["codes_col", "scales_col"] if colwise else [])
+        for k in keys:
+            assert np.array_equal(host(got[k]), host(ref[k])), (k, scale_by)
+        assert bits(host(out_amax)[0]) == bits(host(y_amax)[0])
+        sg = oracle.global_scale(np.float32(host(given)[0]))
+        assert bits(host(got["global_scale"])[0]) == bits(sg)
+        if full:
+            if rowwise:
+                c, s_ = oracle.quantize_1d_rows_mt(yh, sg)
+                assert np.array_equal(host(got["codes_row"]), c) and np.array_equal(host(got["scales_row"]), s_)
+            if colwise:
+                c, s_ = oracle.quantize_1d_cols_mt(yh, sg)
+                assert np.array_equal(host(got["codes_col"]), c) and np.array_equal(host(got["scales_col"]), s_)
+        else:
+            rows = np.arange(0, M, 61)
+            c, s_ = oracle.quantize_1d_rows(yh[rows], sg)
+            assert np.array_equal(host(got["codes_row"])[rows], c) and np.array_equal(host(got["scales_row"])[rows], s_)

@@ -151,6 +151,27 @@ def test_rht_dequant_gemm_validation(L):
     assert ga(P(4098)) == -3
 
 
+def test_gemm_quantize_validation(L):
+    def gq(**k):
+        return L.nvfp4_gemm_quantize(k.get("ac", A), A, 1, A, A, A, 2, A, k.get("M", 32), k.get("N", 32),
+                                     k.get("K", 32), k.get("amax", A), k.get("f", F.ROWWISE | F.COLWISE),
+                                     k.get("cr", A), k.get("sr", A), k.get("cc", A), k.get("sc", A),
+                                     NULL, k.get("camax", NULL), NULL)
+    assert gq(f=0) == -4
+    assert gq(f=F.ROWWISE | F.SR) == -4  # round to nearest only
+    assert gq(amax=NULL) == -1
+    assert gq(cr=NULL) == -1
+    assert gq(f=F.COLWISE, cr=NULL, sr=NULL, M=24) == -2  # rowwise outputs not needed: the shape fails next
+    assert gq(f=F.ROWWISE, cc=NULL, sc=NULL, M=24) == -2  # nor columnwise ones
+    assert gq(cc=NULL) == -1
+    assert gq(ac=NULL) == -1
+    assert gq(M=24) == -2
+    assert gq(K=0) == -2
+    assert gq(cr=MIS) == -3
+    assert gq(sc=MIS) == -3
+    assert gq(camax=P(4098)) == -3
+
+
 def test_mxfp4_validation(L):
     q = lambda **k: L.mxfp4_quantize(k.get("x", A), k.get("R", 64), k.get("C", 64), k.get("f", F.ROWWISE), 0,
                                      k.get("cr", A), k.get("sr", A), k.get("cc", A), k.get("sc", A), NULL)
