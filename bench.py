@@ -682,10 +682,19 @@ def main():
             yy = L.fprop(x, wq, ws=ws_l, out_dtype=torch.bfloat16)
             return F.nvfp4_quantize_1d(yy, F.nvfp4_amax(yy), rowwise=True, colwise=True)
 
+        # the epilogue-quantized forward takes the amax of a previous
+        # product of the same layer (here: the same inputs' own max |Y|)
+        y0, _ = L.forward_quantized(x, wq, ws=ws_l)
+        y_amax0 = F.nvfp4_amax(y0)
+        del y0
+        next_amax = torch.empty(1, dtype=torch.float32, device=dev)
         parts = parts + (
             ("linear_forward_quantized_output_fused", lambda: L.forward_quantized(x, wq, ws=ws_l),
              2.0 * R * C * WR),
-            ("linear_forward_quantized_output_unfused", unfused_forward, 2.0 * R * C * WR))
+            ("linear_forward_quantized_output_unfused", unfused_forward, 2.0 * R * C * WR),
+            ("linear_forward_quantized_output_epilogue",
+             lambda: L.forward_quantized_delayed(x, wq, y_amax0, ws=ws_l, out_amax=next_amax),
+             2.0 * R * C * WR))
         for name, fn, fl in parts:
             us = timed(name, lambda k: fn(), iters=5, graph=False)
             rows[name] = {"shape": {"tokens": R, "in": C, "out": WR}, "us": round(us, 1), "calls": 5}

@@ -291,7 +291,6 @@ __device__ __forceinline__ void quant_epilogue(const GemmArgs& g, const floatx16
     asm volatile("" : "+v"(zero));
     uint8_t* const lds = lds_in + zero;
     const int ln = lane + (int)zero;
-    const int mlim = (int)min(g.M - m0, (int64_t)kBM), nlim = (int)min(g.N - n0, (int64_t)kBN);
     // 1. C x fl(S_gA S_gB), rounded to bf16 (nearest even), into LDS; the
     //    K loop's last barrier has passed, so the stage buffers are free.
 #pragma unroll
@@ -305,8 +304,6 @@ __device__ __forceinline__ void quant_epilogue(const GemmArgs& g, const floatx16
                 const uint32_t u = __float_as_uint(acc[a][b][i] * scale);
                 const uint16_t h = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
                 *reinterpret_cast<uint16_t*>(lds + rl * kQuantPitch + 2 * cl) = h;
-                if (rl < mlim && cl < nlim)
-                    cmax = max(cmax, (uint32_t)(h & 0x7FFFu) << 16);
             }
             __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 tile at a time
         }
@@ -348,8 +345,8 @@ __device__ __forceinline__ void quant_epilogue(const GemmArgs& g, const floatx16
     __syncthreads();
     if (q.valid) {
         BlockMax bm;
-        if (QCOL)
-            column_maxima(v, bm);
+        column_maxima(v, bm);  // also max |Y| of the item (the reported amax)
+        cmax = max(cmax, item_max(bm));
         if (QROW)
             row_maxima(v, q.odd, bm);
         uint4 draws[16];  // unused: round to nearest

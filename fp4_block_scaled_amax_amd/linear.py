@@ -23,7 +23,9 @@ Fused passes: dY's two amaxes (plain, for its rowwise dgrad operand, and of
 its Hadamard transform, for its columnwise wgrad operand) come from one read
 of dY (nvfp4_amax with both=True), and the forward can hand its output to
 the next layer already quantized, the output's amax reduced in the GEMM's
-epilogue (forward_quantized) so the quantization reads Y once.
+epilogue (forward_quantized) so the quantization reads Y once; with the amax
+known beforehand (the layer's previous max |Y|), the GEMM's epilogue
+quantizes Y itself and Y never reaches memory (forward_quantized_delayed).
 
 Every step runs in the library's kernels; this module only sequences calls
 on one stream. Shapes: x [tokens][in], w [out][in], dy [tokens][out], all
@@ -31,7 +33,7 @@ bf16 bit patterns (int16/uint16 tensors), every dimension a multiple of 16.
 """
 from __future__ import annotations
 
-from . import (SCALE_1D, SCALE_2D, SCALE_2D_T, _torch, nvfp4_amax, nvfp4_gemm,
+from . import (SCALE_1D, SCALE_2D, SCALE_2D_T, _torch, nvfp4_amax, nvfp4_gemm, nvfp4_gemm_quantize,
                nvfp4_quantize_1d, nvfp4_quantize_1d_fused, nvfp4_quantize_2d, nvfp4_workspace)
 
 
@@ -71,6 +73,27 @@ def forward_quantized(x, wq: dict, ws=None, stream=None):
                    tokens, n, k, out_dtype=torch.bfloat16, stream=stream, out_amax=y_amax)
     yq = nvfp4_quantize_1d(y, y_amax, rowwise=True, colwise=True, stream=stream)
     return y, yq
+
+
+def forward_quantized_delayed(x, wq: dict, y_amax, ws=None, stream=None, out_amax=None):
+    """Y's NVFP4 quantization (rowwise and columnwise 1D, round to nearest
+    even) made by the fprop GEMM's own epilogue, with the amax given (for
+    instance the previous step's max |Y| of this layer): Y is never stored.
+    Returns (yq, out_amax), out_amax = max |Y| of this product (float32 [1],
+    allocated if not given), the amax for the next call. With y_amax equal to
+    this product's own max |Y| the bytes equal forward_quantized's yq."""
+    torch = _torch()
+    tokens, k = x.shape
+    n = wq["codes_row"].shape[0]
+    ws = nvfp4_workspace(x.device) if ws is None else ws
+    xq = nvfp4_quantize_1d_fused(x, ws, rowwise=True, stream=stream)
+    if out_amax is None:
+        out_amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    yq = nvfp4_gemm_quantize(xq["codes_row"], xq["scales_row"], SCALE_1D, xq["global_scale"],
+                             wq["codes_row"], wq["scales"], SCALE_2D, wq["global_scale"],
+                             tokens, n, k, y_amax, rowwise=True, colwise=True, out_amax=out_amax,
+                             stream=stream)
+    return yq, out_amax
 
 
 def gradient_amaxes(dy, rht_mask: int, stream=None):

@@ -219,3 +219,19 @@ def test_gemm_quantize_epilogue(M, N, K, bmode, layouts):
             rows = np.arange(0, M, 61)
             c, s_ = oracle.quantize_1d_rows(yh[rows], sg)
             assert np.array_equal(host(got["codes_row"])[rows], c) and np.array_equal(host(got["scales_row"])[rows], s_)
+
+
+def test_forward_quantized_delayed_equals_forward_quantized():
+    """With the amax from a first call, the epilogue-quantized forward gives
+    forward_quantized's bytes, and reports the same max |Y|."""
+    T, N_IN, N_OUT = 272, 528, 784
+    x = W.activation(T, N_IN, seed=94, n_outlier_cols=2)
+    w = W.weight(N_OUT, N_IN, seed=95)
+    xd = dev(x)
+    wq = L.quantize_weight(dev(w))
+    y, yq = L.forward_quantized(xd, wq)
+    y_amax = F.nvfp4_amax(y)
+    dq, out_amax = L.forward_quantized_delayed(xd, wq, y_amax)
+    assert bits(host(out_amax)[0]) == bits(host(y_amax)[0])
+    for k in ("global_scale", "codes_row", "scales_row", "codes_col", "scales_col"):
+        assert np.array_equal(host(dq[k]), host(yq[k])), k
