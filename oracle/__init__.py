@@ -446,6 +446,40 @@ def quantize_1d_cols_mt(x: np.ndarray, sg, sr: bool = False, seed: int = 0, rht:
     return codes, scales
 
 
+def mx_quantize_rows_mt(x: np.ndarray, threads: int | None = None):
+    """mx_quantize_rows over the whole tensor, row ranges on threads."""
+    x = _c(x, np.uint16)
+    R, C = x.shape
+    codes = np.empty((R, C // 2), np.uint8)
+    scales = np.empty((R, C // 32), np.uint8)
+    lib = _load()
+    t = threads or host_threads()
+
+    def work(r):
+        lib.mxfp4_oracle_quantize_rows(_ptr(x), R, C, r[0], r[1], _at(codes, r[0] * (C // 2)),
+                                       _at(scales, r[0] * (C // 32)))
+
+    _run(work, _ranges(R, t), t)
+    return codes, scales
+
+
+def mx_quantize_cols_mt(x: np.ndarray, rht: bool = False, mask: int = 0, threads: int | None = None):
+    """mx_quantize_cols over the whole tensor, column ranges on threads."""
+    x = _c(x, np.uint16)
+    R, C = x.shape
+    codes = np.empty((C, R // 2), np.uint8)
+    scales = np.empty((C, R // 32), np.uint8)
+    lib = _load()
+    t = threads or host_threads()
+
+    def work(c):
+        lib.mxfp4_oracle_quantize_cols(_ptr(x), R, C, int(bool(rht)), mask, c[0], c[1],
+                                       _at(codes, c[0] * (R // 2)), _at(scales, c[0] * (R // 32)))
+
+    _run(work, _ranges(C, t), t)
+    return codes, scales
+
+
 def quantize_2d_mt(x: np.ndarray, sg, threads: int | None = None):
     """quantize_2d over the whole tensor, tile-row ranges on threads."""
     x = _c(x, np.uint16)

@@ -5,10 +5,10 @@ Codes and scale bytes must match bit for bit (rowwise, columnwise, both in
 one call, columnwise after the Hadamard transform), dequantization bit for
 bit in binary32 and bf16, and the GEMM on the block-scaled matrix cores must
 satisfy ||C - C_ref||_F / ||C_ref||_F <= 1e-5 (every row separately too)
-against the double product of the exactly reconstructed operands. Small
-and ragged shapes are compared in full; the full-size 8192x4096 activation,
-8192x14336 gradient and the 8192x14336x4096 product on sampled rows /
-columns, in the launch configuration the benchmark times.
+against the double product of the exactly reconstructed operands. Every
+byte is compared, at small and ragged shapes and at the full-size 8192x4096
+activation and 8192x14336 gradient; the 8192x14336x4096 product on sampled
+rows, in the launch configuration the benchmark times.
 """
 import sys
 
@@ -136,29 +136,26 @@ def test_quantize_layout_specific_shapes():
         assert np.array_equal(host(got["codes_col"]), c) and np.array_equal(host(got["scales_col"]), s)
 
 
-def test_quantize_full_activation_sampled():
-    """8192 x 4096 activation, both layouts in one call: sampled rows and
-    columns (whole, and spanning tile boundaries) against the oracle."""
+def test_quantize_full_activation():
+    """8192 x 4096 activation, both layouts in one call: every byte against
+    the oracle (threaded over row and column ranges)."""
     x = W.activation()
     log("[test_mx_quantize_full] 8192x4096 activation, row+col")
     q = F.mxfp4_quantize(dev(x), rowwise=True, colwise=True)
     cr, sr, cc, sc = (host(q[k]) for k in ("codes_row", "scales_row", "codes_col", "scales_col"))
-    for r0 in (0, 127, 128, 4095, 8160):
-        c, s = oracle.mx_quantize_rows(x, r0, r0 + 32)
-        assert np.array_equal(cr[r0:r0 + 32], c) and np.array_equal(sr[r0:r0 + 32], s), r0
-    for c0 in (0, 126, 2048, 4064):
-        c, s = oracle.mx_quantize_cols(x, c0=c0, c1=c0 + 32)
-        assert np.array_equal(cc[c0:c0 + 32], c) and np.array_equal(sc[c0:c0 + 32], s), c0
+    c, s = oracle.mx_quantize_rows_mt(x)
+    assert np.array_equal(cr, c) and np.array_equal(sr, s)
+    c, s = oracle.mx_quantize_cols_mt(x)
+    assert np.array_equal(cc, c) and np.array_equal(sc, s)
 
 
-def test_quantize_full_gradient_hadamard_sampled():
+def test_quantize_full_gradient_hadamard():
     x = W.gradient()
     log("[test_mx_quantize_full] 8192x14336 gradient, columnwise + Hadamard")
     q = F.mxfp4_quantize(dev(x), rowwise=False, colwise=True, rht=True, rht_mask=MASK)
     cc, sc = host(q["codes_col"]), host(q["scales_col"])
-    for c0 in (0, 127, 7168, 14304):
-        c, s = oracle.mx_quantize_cols(x, rht=True, mask=MASK, c0=c0, c1=c0 + 32)
-        assert np.array_equal(cc[c0:c0 + 32], c) and np.array_equal(sc[c0:c0 + 32], s), c0
+    c, s = oracle.mx_quantize_cols_mt(x, rht=True, mask=MASK)
+    assert np.array_equal(cc, c) and np.array_equal(sc, s)
 
 
 @pytest.mark.parametrize("name", ["ragged_act", "special"])

@@ -220,3 +220,15 @@ def test_gemm_reference_tiny_bruteforce():
         for n in (0, 3, 7):
             exact = sum(val(qa, sa, m, k) * val(qb, sb, n, k) for k in range(K))
             assert abs(float(exact) - ref[m, n]) <= 1e-12 * max(1.0, abs(float(exact)))
+
+
+def test_threaded_drivers_equal_single_thread():
+    """The threaded drivers the full-size GPU tests use split rows or
+    columns over threads and must give the single call's bytes."""
+    x = W.gradient(320, 96, seed=5)
+    for a, b in zip(oracle.mx_quantize_rows(x), oracle.mx_quantize_rows_mt(x, threads=4)):
+        assert np.array_equal(a, b)
+    for rht in (False, True):
+        single = oracle.mx_quantize_cols(x, rht=rht, mask=0x5A3C)
+        for a, b in zip(single, oracle.mx_quantize_cols_mt(x, rht=rht, mask=0x5A3C, threads=5)):
+            assert np.array_equal(a, b)
