@@ -389,20 +389,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int tile
     uint8_t* const lds_sc = lds_all + 2 * kStageBytes;  // A, B tile scales
 
     const int64_t K = g.K;
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * (32 * FN);
     const int nstages = (int)((K + KS - 1) / KS);
     const int last = nstages - 1;
-    const int frow = lane & 31;
-    const int fk = (lane >> 5) * 16;  // byte offset of the lane's 8 K-elements
-    const bool is_b = t >= kBM;
-    const int64_t rows = is_b ? g.N : g.M;
-    const bool two_d = is_b ? g.b_two_d : g.a_two_d;
-    const bool scales_t = is_b ? g.b_scales_t : g.a_scales_t;
-    const uint8_t* codes = is_b ? g.b_codes : g.a_codes;
-    const uint8_t* scales = is_b ? g.b_scales : g.a_scales;
-    uint8_t* my_row0 = lds + t * kRowBytes;
     const float scale = (*g.a_sg) * (*g.b_sg);
     // 2D operands read their tile scales from LDS (K small enough, 16-byte
     // aligned scale arrays); the flags are uniform over the workgroup.
@@ -411,10 +399,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int tile
     const bool b_al = g.b_two_d && ((reinterpret_cast<uintptr_t>(g.b_scales) & 15) == 0);
     const bool a_stage = a_al && (K <= kLdsScaleK || (!b_al && K <= 2 * kLdsScaleK));
     const bool b_stage = b_al && (K <= kLdsScaleK || (!a_al && K <= 2 * kLdsScaleK));
-    const bool my_stage = is_b ? b_stage : a_stage;
-    uint8_t* const my_sc = lds_sc + (is_b && a_stage ? kLdsScaleK : 0);
-    // Half tiles need 128 B rows: the last two waves fetch nothing.
-    const bool loads = FN == 4 || !is_b || t - kBM < 64 * FN;
 
     // Persistent: each workgroup walks tiles; a tile's output stores drain
     // while the next tile's first stages load and decode.
@@ -422,6 +406,29 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int tile
         const int unit = gemm_tile_index(round);
         if (unit >= count)
             break;
+        // The thread's per-tile constants. With the quantizing epilogue they
+        // are recomputed every round (an opaque copy of the lane index keeps
+        // them from being hoisted out of the tile loop), so that none of
+        // them is live while the epilogue runs.
+        int lane = threadIdx.x & 63;
+        if constexpr (QUANT != 0)
+            asm volatile("" : "+v"(lane));
+        const int wave = threadIdx.x >> 6;
+        const int t = wave * 64 + lane;
+        const int wm = (wave >> 1) * 64, wn = (wave & 1) * (32 * FN);
+        const int frow = lane & 31;
+        const int fk = (lane >> 5) * 16;  // byte offset of the lane's 8 K-elements
+        const bool is_b = wave >= kBM / 64;
+        const int64_t rows = is_b ? g.N : g.M;
+        const bool two_d = is_b ? g.b_two_d : g.a_two_d;
+        const bool scales_t = is_b ? g.b_scales_t : g.a_scales_t;
+        const uint8_t* codes = is_b ? g.b_codes : g.a_codes;
+        const uint8_t* scales = is_b ? g.b_scales : g.a_scales;
+        uint8_t* my_row0 = lds + t * kRowBytes;
+        const bool my_stage = is_b ? b_stage : a_stage;
+        uint8_t* const my_sc = lds_sc + (is_b && a_stage ? kLdsScaleK : 0);
+        // Half tiles need 128 B rows: the last two waves fetch nothing.
+        const bool loads = FN == 4 || !is_b || t - kBM < 64 * FN;
         const int tile = FN == 4 ? unit : first + (unit >> 1);
         const int half = FN == 4 ? 0 : (unit & 1);
         // Tiles are ordered in groups of kGroupM tile rows, column by column
