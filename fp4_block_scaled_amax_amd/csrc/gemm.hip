@@ -186,10 +186,14 @@ __device__ __forceinline__ f16x8 lds_fragment(const uint8_t* lds, int row, int k
 }
 
 // The MFMAs of one stage for this wave's 64 x (32 FN) sub-tile.
+// The wave runs its MFMAs at raised priority, so that of the two waves on a
+// SIMD the one with matrix work issues first and the other's decode fills
+// the gaps (measured: 2-3% on 8192x14336x4096).
 template <int KS, int FN>
 __device__ __forceinline__ void stage_mfma(const uint8_t* buf, int wm, int wn, int frow, int fk,
                                            floatx16 (&acc)[2][4])
 {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS / 16; ++ks) {
         f16x8 fa[2], fb[FN];
@@ -205,6 +209,7 @@ __device__ __forceinline__ void stage_mfma(const uint8_t* buf, int wm, int wn, i
             for (int b = 0; b < FN; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[a], fb[b], acc[a][b], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // Position in the tile order of this workgroup's tile in round `round`.
