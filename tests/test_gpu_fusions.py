@@ -235,3 +235,26 @@ def test_forward_quantized_delayed_equals_forward_quantized():
     assert bits(host(out_amax)[0]) == bits(host(y_amax)[0])
     for k in ("global_scale", "codes_row", "scales_row", "codes_col", "scales_col"):
         assert np.array_equal(host(dq[k]), host(yq[k])), k
+
+
+@pytest.mark.parametrize("given", [0.0, float("inf"), float("nan"), 1e-30])
+def test_gemm_quantize_epilogue_degenerate_amax(given):
+    """A given amax of 0, infinity, NaN or a tiny value: the epilogue's bytes
+    still equal nvfp4_quantize_1d's of the bf16 product with that amax (both
+    run the same item code, here down its exact and non-finite paths)."""
+    M, N, K = 272, 400, 96
+    log(f"[test_gemm_quantize_epilogue_degenerate_amax] amax {given}")
+    a = W.normal_tensor(M, K, seed=96)
+    b = W.normal_tensor(N, K, seed=97, std=0.02)
+    ad, bd = dev(a), dev(b)
+    qa = F.nvfp4_quantize_1d(ad, F.nvfp4_amax(ad))
+    qb = F.nvfp4_quantize_2d(bd, F.nvfp4_amax(bd), colwise=False)
+    args = (qa["codes_row"], qa["scales_row"], 1, qa["global_scale"], qb["codes_row"], qb["scales"], 2,
+            qb["global_scale"], M, N, K)
+    y = F.nvfp4_gemm(*args, out_dtype=torch.bfloat16)
+    amax = torch.full((1,), given, dtype=torch.float32, device="cuda")
+    got = F.nvfp4_gemm_quantize(*args, amax)
+    ref = F.nvfp4_quantize_1d(y, amax, rowwise=True, colwise=True)
+    for k in ("global_scale", "codes_row", "scales_row", "codes_col", "scales_col"):
+        g_, r_ = host(got[k]), host(ref[k])
+        assert np.array_equal(g_.view(np.uint8), r_.view(np.uint8)), k
