@@ -73,8 +73,16 @@ __device__ __forceinline__ bool finite_bits(float r)
 // Row-and/or-column encoding of a whole item in 2x2 groups: elements
 // (i, 2k), (i, 2k+1), (i+1, 2k), (i+1, 2k+1) are unpacked once and feed byte
 // k of the two row words and byte (i/2 mod 4) of the two column words.
-template <int MODE, int IP, bool ROW, bool COL>
-__device__ __forceinline__ void encode_row_pair(const uint4 (&v)[16], const float (&rr)[16],
+template <bool PAIR, int I>
+__device__ __forceinline__ float row_multiplier(const float (&rm)[8])
+{
+    if (!PAIR)
+        return rm[I & 7];
+    return I < 8 ? from_even_lane(rm[I & 7]) : from_odd_lane(rm[I & 7]);
+}
+
+template <int MODE, int IP, bool ROW, bool COL, bool PAIR>
+__device__ __forceinline__ void encode_row_pair(const uint4 (&v)[16], const float (&rm)[8],
                                                 const float (&rc)[8], const uint4 (&draws)[16],
                                                 uint32_t (&roww)[2], uint32_t (&colw)[8][2])
 {
@@ -87,9 +95,16 @@ __device__ __forceinline__ void encode_row_pair(const uint4 (&v)[16], const floa
         for (int j = 0; j < 8; ++j)
             colw[j][ch] = fresh_word();
     }
+    // The rare encoders (non-finite multipliers, software rounding) take
+    // their words through an empty asm statement: the compiler then cannot
+    // share their unpacking with the common encoder's and hoist it above the
+    // branch between them, which would keep every unpacked value of the item
+    // live at once.
 #define NVFP4_GROUP(K)                                                                      \
     {                                                                                       \
-        const uint32_t w0 = word_at(v[i], K), w1 = word_at(v[i + 1], K);                    \
+        uint32_t w0 = word_at(v[i], K), w1 = word_at(v[i + 1], K);                          \
+        if (MODE == kEncHwSafe || MODE == kEncSr)                                           \
+            asm volatile("" : "+v"(w0), "+v"(w1)); /* see below */                          \
         const float a = bf16_lo(w0), b = bf16_hi(w0), c = bf16_lo(w1), d = bf16_hi(w1);     \
         uint32_t ha = 0u, hb = 0u, hc = 0u, hd = 0u;                                        \
         if (is_sr(MODE)) {                                                                  \
@@ -99,20 +114,22 @@ __device__ __forceinline__ void encode_row_pair(const uint4 (&v)[16], const floa
             hd = sr_input<MODE>(draws[i + 1], 2 * K + 1);                                   \
         }                                                                                   \
         if (ROW) {                                                                          \
-            roww[0] = put_pair<MODE, K>(roww[0], a, b, rr[i], ha, hb);                      \
-            roww[1] = put_pair<MODE, K>(roww[1], c, d, rr[i + 1], hc, hd);                  \
+            roww[0] = put_pair<MODE, K>(roww[0], a, b, rr0, ha, hb);                        \
+            roww[1] = put_pair<MODE, K>(roww[1], c, d, rr1, hc, hd);                        \
         }                                                                                   \
         if (COL) {                                                                          \
             colw[2 * K][ch] = put_pair<MODE, cb>(colw[2 * K][ch], a, c, rc[2 * K], ha, hc);         \
             colw[2 * K + 1][ch] = put_pair<MODE, cb>(colw[2 * K + 1][ch], b, d, rc[2 * K + 1], hb, hd); \
         }                                                                                   \
     }
+    const float rr0 = ROW ? row_multiplier<PAIR, i>(rm) : 0.0f;
+    const float rr1 = ROW ? row_multiplier<PAIR, i + 1>(rm) : 0.0f;
     NVFP4_GROUP(0) NVFP4_GROUP(1) NVFP4_GROUP(2) NVFP4_GROUP(3)
 #undef NVFP4_GROUP
 }
 
-template <int MODE, bool ROW, bool COL>
-__device__ __forceinline__ void encode_item(const uint4 (&v)[16], const float (&rr)[16],
+template <int MODE, bool ROW, bool COL, bool PAIR, int IP0, int IP1>
+__device__ __forceinline__ void encode_item(const uint4 (&v)[16], const float (&rm)[8],
                                             const float (&rc)[8], const uint4 (&draws)[16],
                                             uint8_t* row_dst, int64_t row_pitch,
                                             uint32_t (&colw)[8][2])
@@ -120,12 +137,14 @@ __device__ __forceinline__ void encode_item(const uint4 (&v)[16], const float (&
     // A half-wave's rowwise codes of one row are a whole 128-byte line:
     // stream them past the caches.
     uint32_t roww[2];
-#define NVFP4_ROWS(IP)                                                                   \
-    encode_row_pair<MODE, IP, ROW, COL>(v, rr, rc, draws, roww, colw);                    \
-    if (ROW) {                                                                           \
-        uint8_t* d = row_dst + (2 * IP) * row_pitch;                                     \
-        __builtin_nontemporal_store(roww[0], reinterpret_cast<uint32_t*>(d));            \
-        __builtin_nontemporal_store(roww[1], reinterpret_cast<uint32_t*>(d + row_pitch)); \
+#define NVFP4_ROWS(IP)                                                                       \
+    if constexpr (IP >= IP0 && IP < IP1) {                                                   \
+        encode_row_pair<MODE, IP, ROW, COL, PAIR>(v, rm, rc, draws, roww, colw);             \
+        if (ROW) {                                                                           \
+            uint8_t* d = row_dst + (2 * IP) * row_pitch;                                     \
+            __builtin_nontemporal_store(roww[0], reinterpret_cast<uint32_t*>(d));            \
+            __builtin_nontemporal_store(roww[1], reinterpret_cast<uint32_t*>(d + row_pitch)); \
+        }                                                                                    \
     }
     NVFP4_ROWS(0) NVFP4_ROWS(1) NVFP4_ROWS(2) NVFP4_ROWS(3)
     NVFP4_ROWS(4) NVFP4_ROWS(5) NVFP4_ROWS(6) NVFP4_ROWS(7)
@@ -139,11 +158,11 @@ struct ItemPos {
     bool odd, valid;
 };
 
-__device__ __forceinline__ ItemPos item_pos(int tr, int tc, int64_t rows, int64_t cols)
+__device__ __forceinline__ ItemPos item_pos(int tr, int tc, int64_t rows, int64_t cols, int tid)
 {
     ItemPos q;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     q.tile_r0 = (int64_t)tr * kTileR;
     q.tile_c0 = (int64_t)tc * kTileC;
     q.cg = lane & 31;
@@ -156,6 +175,11 @@ __device__ __forceinline__ ItemPos item_pos(int tr, int tc, int64_t rows, int64_
     return q;
 }
 
+__device__ __forceinline__ ItemPos item_pos(int tr, int tc, int64_t rows, int64_t cols)
+{
+    return item_pos(tr, tc, rows, cols, threadIdx.x);
+}
+
 __device__ __forceinline__ void load_item(const Params& p, const ItemPos& q, uint4 (&v)[16])
 {
     if (q.valid) {
@@ -164,6 +188,18 @@ __device__ __forceinline__ void load_item(const Params& p, const ItemPos& q, uin
         for (int i = 0; i < 16; ++i)
             v[i] = load16_stream(src + i * p.cols);
     }
+}
+
+// The same loads, unconditional: an item outside the tensor reads the first
+// item instead (always present, as rows and cols are positive multiples of
+// 16), so the data is defined on every path and no join of loaded and
+// undefined values splits its registers; the caller skips such items.
+__device__ __forceinline__ void load_item_any(const Params& p, const ItemPos& q, uint4 (&v)[16])
+{
+    const uint16_t* src = p.x + (q.valid ? q.r0 * p.cols + q.c0 : 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        v[i] = load16_stream(src + i * p.cols);
 }
 
 // Block maxima of an item as packed pairs of |bf16| patterns (16 bits each,
@@ -191,15 +227,11 @@ __device__ __forceinline__ void column_maxima(const uint4 (&v)[16], BlockMax& bm
     }
 }
 
-// Row maxima trade halves through DPP with the pair lane: every lane of the
-// pair must be active (both are, as the item validity is pairwise).
-__device__ __forceinline__ void row_maxima(const uint4 (&v)[16], bool odd, BlockMax& bm)
+// Row maxima from each row's packed maxima of the lane's 4 column pairs.
+// They trade halves through DPP with the pair lane: every lane of the pair
+// must be active (both are, as the item validity is pairwise).
+__device__ __forceinline__ void row_maxima_of(const uint32_t (&pm)[16], bool odd, BlockMax& bm)
 {
-    uint32_t pm[16];  // per row: packed maxima of the lane's 4 column pairs
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        pm[i] = pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
-                           pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu));
 #pragma unroll
     for (int k = 0; k < 8; k += 2) {
         // This lane's maxima of rows k, k+1 (low, high half) and of rows
@@ -213,6 +245,37 @@ __device__ __forceinline__ void row_maxima(const uint4 (&v)[16], bool odd, Block
         const uint32_t send = odd ? lo : hi;
         bm.row[k >> 1] = pk_max_u16(own, swap_lane1(send));
     }
+}
+
+__device__ __forceinline__ void row_maxima(const uint4 (&v)[16], bool odd, BlockMax& bm)
+{
+    uint32_t pm[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        pm[i] = pk_max_u16(pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
+                           pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu));
+    row_maxima_of(pm, odd, bm);
+}
+
+// Column and row maxima in one pass: each magnitude word feeds both at
+// once, so the masked words are never all live together.
+__device__ __forceinline__ void block_maxima(const uint4 (&v)[16], bool odd, BlockMax& bm)
+{
+    uint32_t pm[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        bm.col[k] = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t w0 = v[i].x & 0x7FFF7FFFu, w1 = v[i].y & 0x7FFF7FFFu;
+        const uint32_t w2 = v[i].z & 0x7FFF7FFFu, w3 = v[i].w & 0x7FFF7FFFu;
+        bm.col[0] = pk_max_u16(bm.col[0], w0);
+        bm.col[1] = pk_max_u16(bm.col[1], w1);
+        bm.col[2] = pk_max_u16(bm.col[2], w2);
+        bm.col[3] = pk_max_u16(bm.col[3], w3);
+        pm[i] = pk_max_u16(pk_max_u16(w0, w1), pk_max_u16(w2, w3));
+    }
+    row_maxima_of(pm, odd, bm);
 }
 
 // Binary32 bits of a packed half: the low (H = 0) or high (H = 1) 16 bits.
@@ -363,8 +426,9 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
     }
 
     // ----------------------------- rowwise, rowwise + columnwise, 2D
-    float rc[8];   // columnwise multipliers (1D), or the tile's (2D)
-    float rr[16];  // rowwise multipliers (1D), or the tile's (2D)
+    float rc[8];  // columnwise multipliers (1D), or the tile's (2D)
+    float rm[8];  // this lane's rowwise multipliers (1D: rows 0..7 on even
+                  // lanes, 8..15 on odd ones), or the tile's (2D)
     uint32_t col_byte[8];
     bool fin = true;
     if (TWO_D) {
@@ -376,8 +440,8 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
         for (int j = 0; j < 8; ++j)
             rc[j] = r;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            rr[i] = r;
+        for (int i = 0; i < 8; ++i)
+            rm[i] = r;
         fin = finite_bits(r);
         if (!odd) {
             p.scales_row[(r0 >> 4) * (cols >> 4) + (c0 >> 4)] = (uint8_t)byte;
@@ -403,14 +467,36 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
         fin = sc.table_ok;
         if (!__all(sc.fast && vote.ok())) {
             uint32_t mb = 0u;
-            if (COL) {
+            if constexpr (COL) {
+                // Rows and columns: one block at a time, through this
+                // thread's own 16 words of the columnwise staging (untouched
+                // until its encode), so that this rare path needs few
+                // registers of its own.
+                uint32_t* const stage = reinterpret_cast<uint32_t*>(lds_codes);
+                const int base = 2 * ((cg * 8) * kRowBlocks + (rb ^ (cg & 7)));
+                auto word = [&](int n) -> uint32_t& {
+                    return stage[base + 2 * kRowBlocks * (n >> 1) + (n & 1)];
+                };
+#pragma unroll
+                for (int n = 0; n < 4; ++n) {
+                    word(n) = bm.col[n];
+                    word(4 + n) = bm.row[n];
+                }
+#pragma unroll 1
+                for (int b = 0; b < 16; ++b) {
+                    // b < 8: column block b; b >= 8: row block b - 8.
+                    const uint32_t pk = word(b >> 1);
+                    const uint32_t byte = scale_byte((b & 1) ? (pk & 0xFFFF0000u) : (pk << 16), sc);
+                    reinterpret_cast<uint8_t*>(&word(8 + (b >> 2)))[b & 3] = (uint8_t)byte;
+                    mb = max(mb, byte);
+                }
+                const uint32_t cw0 = word(8), cw1 = word(9), rw0 = word(10), rw1 = word(11);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    col_byte[j] = scale_byte(col_max_bits(bm, j), sc);
-                    mb = max(mb, col_byte[j]);
+                    col_byte[j] = ((j < 4 ? cw0 : cw1) >> (8 * (j & 3))) & 0xFFu;
+                    row_byte[j] = ((j < 4 ? rw0 : rw1) >> (8 * (j & 3))) & 0xFFu;
                 }
-            }
-            if (ROW) {
+            } else {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     row_byte[k] = scale_byte(row_max_bits(bm, k), sc);
@@ -421,8 +507,10 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
         }
         if (COL) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 8; ++j) {
                 rc[j] = lds_rcp[col_byte[j]];
+                lds_scales[(cg * 8 + j) * kRowBlocks + rb] = (uint8_t)col_byte[j];
+            }
         }
         if (ROW) {
             // Even lanes own rows 0..7 of the pair's blocks, odd lanes 8..15.
@@ -431,9 +519,7 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 sdst[k * (cols >> 4)] = (uint8_t)row_byte[k];
-                const float mine = lds_rcp[row_byte[k]];
-                rr[k] = from_even_lane(mine);     // rows 0..7: settled by the even lane
-                rr[k + 8] = from_odd_lane(mine);  // rows 8..15: by the odd lane
+                rm[k] = lds_rcp[row_byte[k]];
             }
         }
         if (!sc.table_ok) {
@@ -444,8 +530,8 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
             for (int j = 0; j < 8; ++j)
                 fin = fin && (!COL || finite_bits(rc[j]));
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
-                fin = fin && (!ROW || finite_bits(rr[k]));
+            for (int k = 0; k < 8; ++k)
+                fin = fin && (!ROW || finite_bits(rm[k]));  // the wave's vote covers the pair
         }
     }
     uint32_t colw[8][2];
@@ -454,23 +540,32 @@ __device__ __forceinline__ void compute_item(const Params& p, const ItemPos& q,
         colw[j][0] = colw[j][1] = 0u;
     uint8_t* row_dst = ROW ? p.codes_row + r0 * (cols >> 1) + (c0 >> 1) : nullptr;
     const int64_t row_pitch = cols >> 1;
-    if (SR && __all(fin))
-        encode_item<kEncSrHw, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
-    else if (SR)
-        encode_item<kEncSr, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
-    else if (__all(fin))
-        encode_item<kEncHw, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
-    else
-        encode_item<kEncHwSafe, ROW, COL>(v, rr, rc, draws, row_dst, row_pitch, colw);
-    if (COL) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int col = cg * 8 + j;
-            lds_codes[col * kRowBlocks + (rb ^ (cg & 7))] = make_uint2(colw[j][0], colw[j][1]);
-            if (!TWO_D)
-                lds_scales[col * kRowBlocks + rb] = (uint8_t)col_byte[j];
-        }
+    constexpr bool kPair = !TWO_D;
+    const bool all_fin = __all(fin);
+    uint32_t* const lds_words = reinterpret_cast<uint32_t*>(lds_codes);
+    // Rows 0..7, then 8..15: each half's column words go to the staging as
+    // soon as they are complete.
+#define NVFP4_ENC(MODE, H) \
+    encode_item<MODE, ROW, COL, kPair, 4 * H, 4 * H + 4>(v, rm, rc, draws, row_dst, row_pitch, colw)
+#define NVFP4_HALF(H)                                                                              \
+    {                                                                                              \
+        if (SR && all_fin)                                                                         \
+            NVFP4_ENC(kEncSrHw, H);                                                                \
+        else if (SR)                                                                               \
+            NVFP4_ENC(kEncSr, H);                                                                  \
+        else if (all_fin)                                                                          \
+            NVFP4_ENC(kEncHw, H);                                                                  \
+        else                                                                                       \
+            NVFP4_ENC(kEncHwSafe, H);                                                              \
+        if (COL) {                                                                                 \
+            _Pragma("unroll") for (int j = 0; j < 8; ++j)                                          \
+                lds_words[2 * ((cg * 8 + j) * kRowBlocks + (rb ^ (cg & 7))) + H] = colw[j][H];   \
+        }                                                                                          \
     }
+    NVFP4_HALF(0)
+    NVFP4_HALF(1)
+#undef NVFP4_HALF
+#undef NVFP4_ENC
 }
 
 // Write a tile's staged columnwise codes (and 1D column scales) to memory.
@@ -517,6 +612,7 @@ __device__ __forceinline__ void write_col_tile(const Params& p, int64_t tile_r0,
 // rows tile_r0.., B below it; B may be absent or ragged). Per column the
 // pair covers 256 rows: 128 bytes of codes, one whole line, written by 8
 // lanes as 16-byte streaming stores, and 16 scale bytes.
+template <int NT = kThreads>
 __device__ __forceinline__ void write_col_pair(const Params& p, int64_t tile_r0, int64_t tile_c0,
                                                const uint2* codes_a, const uint2* codes_b,
                                                const uint8_t* scales_a, const uint8_t* scales_b)
@@ -526,8 +622,8 @@ __device__ __forceinline__ void write_col_pair(const Params& p, int64_t tile_r0,
     const int64_t pitch = rows >> 1;
     const bool wide = (pitch & 15) == 0;  // 16-byte chunks are aligned
 #pragma unroll
-    for (int k = 0; k < kTileC * 8 / kThreads; ++k) {
-        const int q = k * kThreads + threadIdx.x;
+    for (int k = 0; k < kTileC * 8 / NT; ++k) {
+        const int q = k * NT + threadIdx.x;
         const int col = q >> 3, part = q & 7;  // part: 32 rows = two row blocks
         const int64_t c = tile_c0 + col, r = tile_r0 + part * 32;
         if (c >= cols || r >= rows)
@@ -553,7 +649,7 @@ __device__ __forceinline__ void write_col_pair(const Params& p, int64_t tile_r0,
     // Scales: one column's 16 bytes (8 per tile) per thread.
     const int col = threadIdx.x;
     const int64_t c = tile_c0 + col;
-    if (c < cols) {
+    if (col < kTileC && c < cols) {
         const int64_t spitch = rows >> 4;
         uint8_t* dst = p.scales_col + c * spitch + (tile_r0 >> 4);
         const int64_t nb64 = (rows - tile_r0) >> 4;

@@ -155,6 +155,7 @@ __device__ __forceinline__ void slot_store(uint32_t* a, uint32_t gen, uint32_t v
 }
 
 // Maximum over the workgroup; every thread gets the result.
+template <int NT>
 __device__ __forceinline__ uint32_t workgroup_max(uint32_t m, uint32_t* red)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -165,24 +166,25 @@ __device__ __forceinline__ uint32_t workgroup_max(uint32_t m, uint32_t* red)
     __syncthreads();
     uint32_t r = red[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w)
+    for (int w = 1; w < NT / 64; ++w)
         r = max(r, red[w]);
     return r;
 }
 
 // Exact amax of the whole tensor by this workgroup alone (slow path).
+template <int NT>
 __device__ uint32_t direct_amax(const Params& p, uint32_t* red)
 {
     const int64_t n = p.rows * p.cols;
     uint32_t pm = 0u;
-    for (int64_t i = (int64_t)threadIdx.x * 8; i < n; i += (int64_t)kThreads * 8) {
+    for (int64_t i = (int64_t)threadIdx.x * 8; i < n; i += (int64_t)NT * 8) {
         const uint4 v = load16(p.x + i);
         pm = pk_max_u16(pm, v.x & 0x7FFF7FFFu);
         pm = pk_max_u16(pm, v.y & 0x7FFF7FFFu);
         pm = pk_max_u16(pm, v.z & 0x7FFF7FFFu);
         pm = pk_max_u16(pm, v.w & 0x7FFF7FFFu);
     }
-    return workgroup_max(max(pm & 0xFFFFu, pm >> 16) << 16, red);
+    return workgroup_max<NT>(max(pm & 0xFFFFu, pm >> 16) << 16, red);
 }
 
 // This call's generation: one more than the last completed call's. Read at
@@ -217,11 +219,12 @@ __device__ __forceinline__ uint32_t call_generation(const uint32_t* ws)
 // workgroup returns the same result. gen0 and wait0 (workspace word 3: the
 // bound on each wait in 100 MHz ticks, 0 for the default) are read by
 // thread 0 at the start of the kernel.
+template <int NT>
 __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t* ws, const Params& p)
 {
-    __shared__ uint32_t red[kThreads / 64];
+    __shared__ uint32_t red[NT / 64];
     __shared__ uint32_t gen_s, wait_s, result_s, ok_s;
-    m = workgroup_max(m, red);
+    m = workgroup_max<NT>(m, red);
     if (threadIdx.x == 0) {
         gen_s = gen0;
         wait_s = wait0;
@@ -235,19 +238,19 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
         // Collect every workgroup's maximum. Each thread watches the slots
         // t, t + 256, ...; every round re-reads all of its pending slots at
         // once, so their round trips overlap.
-        constexpr int kPer = kMaxFusedGrid / kThreads;
+        constexpr int kPer = kMaxFusedGrid / NT;
         uint32_t mm = 0u;
         bool ok = true;
         uint32_t pending = 0u;
 #pragma unroll
         for (int k = 0; k < kPer; ++k)
-            if ((int)threadIdx.x + k * kThreads < (int)gridDim.x)
+            if ((int)threadIdx.x + k * NT < (int)gridDim.x)
                 pending |= 1u << k;
         while (pending != 0u) {
             uint64_t w[kPer];
 #pragma unroll
             for (int k = 0; k < kPer; ++k)
-                w[k] = (pending >> k) & 1u ? slot_load(&ws[kWsArrive + 2 * (threadIdx.x + k * kThreads)]) : 0u;
+                w[k] = (pending >> k) & 1u ? slot_load(&ws[kWsArrive + 2 * (threadIdx.x + k * NT)]) : 0u;
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
                 if (((pending >> k) & 1u) && (uint32_t)w[k] == gen) {
@@ -268,9 +271,9 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
         __syncthreads();
         if (!ok)
             ok_s = 0u;
-        const uint32_t r = workgroup_max(mm, red);
+        const uint32_t r = workgroup_max<NT>(mm, red);
         if (ok_s == 0u) {
-            result_s = direct_amax(p, red);
+            result_s = direct_amax<NT>(p, red);
         } else if (threadIdx.x == 0) {
             result_s = r;
         }
@@ -284,7 +287,7 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
                 __hip_atomic_fetch_add(&ws[kWsSlow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         const uint32_t flag = ok_s != 0u ? 0u : kExpiredFlag;
-        for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads)
+        for (int i = threadIdx.x; i < (int)gridDim.x; i += NT)
             slot_store(&ws[kWsRelease + 2 * i], gen, amax | flag);
         if (threadIdx.x == 0) {
             if (ok_s != 0u)
@@ -309,7 +312,7 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
     }
     __syncthreads();
     if (ok_s == 0u) {
-        const uint32_t amax = direct_amax(p, red);
+        const uint32_t amax = direct_amax<NT>(p, red);
         if (threadIdx.x == 0) {
             __hip_atomic_fetch_add(&ws[kWsSlow], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             count_expired(ws, gen);
@@ -322,9 +325,20 @@ __device__ uint32_t grid_max(uint32_t m, uint32_t gen0, uint32_t wait0, uint32_t
     return v & ~kExpiredFlag;
 }
 
+// Threads of the fused kernel. With round to nearest, 512: the first 256
+// take tile A and the rest tile B, one item each, at four waves per SIMD
+// (128 VGPRs), so two workgroups share each CU. With stochastic rounding an
+// item's draws need 64 more registers, so 256 threads hold both tiles.
+template <bool SR>
+constexpr int kFusedThreads = SR ? 256 : 512;
+template <bool SR>
+constexpr int kFusedWaves = SR ? 1 : 4;  // minimum waves per SIMD
+
 template <bool ROW, bool COL, bool SR>
-__global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint32_t* ws)
+__global__ __launch_bounds__(kFusedThreads<SR>) __attribute__((amdgpu_waves_per_eu(kFusedWaves<SR>)))
+void quantize_fused_kernel(Params p, uint32_t* ws)
 {
+    constexpr int NT = kFusedThreads<SR>;
     // Columnwise staging for the two tiles.
     __shared__ uint2 lds_codes[2][COL ? kTileC * kRowBlocks : 1];
     __shared__ uint8_t lds_scales[2][COL ? kTileC * kRowBlocks : 16];
@@ -333,70 +347,97 @@ __global__ __launch_bounds__(kThreads) void quantize_fused_kernel(Params p, uint
     // Two vertically adjacent tiles per workgroup (B below A), so a
     // column's codes of the pair form whole 128-byte lines.
     const int tra = 2 * (blockIdx.x / p.tiles_c), tc = blockIdx.x % p.tiles_c;
-    const bool has_b = tra + 1 < p.tiles_r;  // uniform over the workgroup
-    const ItemPos qa = item_pos(tra, tc, p.rows, p.cols);
-    const ItemPos qb = item_pos(tra + 1, tc, p.rows, p.cols);
     uint32_t gen = 0u, wait = 0u;
     if (!p.amax_given && threadIdx.x == 0) {
         gen = call_generation(ws);
         wait = ws_load(&ws[kWsWait]);
     }
-    uint4 va[16], vb[16];
-    load_item(p, qa, va);
-    if (has_b)
-        load_item(p, qb, vb);
-
     // Block maxima while the data arrives; the workgroup's maximum follows.
     // (With stochastic rounding the row maxima wait until after the
     // exchange: holding them across it would cost occupancy.)
     constexpr bool kEarlyRows = ROW && !SR;
-    BlockMax ba, bb;
     uint32_t m = 0u;
-    if (qa.valid) {
-        column_maxima(va, ba);
-        if (kEarlyRows)
-            row_maxima(va, qa.odd, ba);
-        m = item_max(ba);
-    }
-    if (has_b && qb.valid) {
-        column_maxima(vb, bb);
-        if (kEarlyRows)
-            row_maxima(vb, qb.odd, bb);
-        m = max(m, item_max(bb));
-    }
-    const uint32_t amax_bits = p.amax_given ? __float_as_uint(*p.amax) : grid_max(m, gen, wait, ws, p);
+    if constexpr (NT == 512) {
+        const int half = threadIdx.x >> 8;  // 0: tile A, 1: tile B
+        const ItemPos q = item_pos(tra + half, tc, p.rows, p.cols, threadIdx.x & 255);
+        uint4 v[16];
+        load_item_any(p, q, v);
+        BlockMax bm;
+        if (q.valid) {
+            if (kEarlyRows)
+                block_maxima(v, q.odd, bm);
+            else
+                column_maxima(v, bm);
+            m = item_max(bm);
+        }
+        const uint32_t amax_bits = p.amax_given ? __float_as_uint(*p.amax) : grid_max<NT>(m, gen, wait, ws, p);
+        const ScaleCtx sc = scale_ctx(__uint_as_float(amax_bits));
+        if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+            *p.sg_out = sc.sg;
+        build_reciprocal_table(lds_rcp, sc.sg);
+        __syncthreads();
+        if (q.valid) {
+            if (ROW && !kEarlyRows)
+                row_maxima(v, q.odd, bm);
+            uint4 draws[16];  // unused: round to nearest
+            compute_item<ROW, COL, false, false, false>(p, q, v, bm, draws, sc, lds_rcp, lds_codes[half],
+                                                        lds_scales[half], false);
+        }
+    } else {
+        const bool has_b = tra + 1 < p.tiles_r;  // uniform over the workgroup
+        const ItemPos qa = item_pos(tra, tc, p.rows, p.cols);
+        const ItemPos qb = item_pos(tra + 1, tc, p.rows, p.cols);
+        uint4 va[16], vb[16];
+        load_item(p, qa, va);
+        if (has_b)
+            load_item(p, qb, vb);
+        BlockMax ba, bb;
+        if (qa.valid) {
+            column_maxima(va, ba);
+            if (kEarlyRows)
+                row_maxima(va, qa.odd, ba);
+            m = item_max(ba);
+        }
+        if (has_b && qb.valid) {
+            column_maxima(vb, bb);
+            if (kEarlyRows)
+                row_maxima(vb, qb.odd, bb);
+            m = max(m, item_max(bb));
+        }
+        const uint32_t amax_bits = p.amax_given ? __float_as_uint(*p.amax) : grid_max<NT>(m, gen, wait, ws, p);
+        const ScaleCtx sc = scale_ctx(__uint_as_float(amax_bits));
+        if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+            *p.sg_out = sc.sg;
+        // Columnwise-only stochastic rounding: the converter's 2^23 goes into
+        // the multipliers where that is exact (uniform).
+        constexpr bool kCanFold = COL && !ROW && SR;
+        const bool fold = kCanFold && fold_sr_scale_ok<0>(sc.sg);
+        build_reciprocal_table(lds_rcp, sc.sg, fold ? kFoldFactor<SR, false> : 1.0f);
+        __syncthreads();
 
-    const ScaleCtx sc = scale_ctx(__uint_as_float(amax_bits));
-    if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
-        *p.sg_out = sc.sg;
-    // Columnwise-only stochastic rounding: the converter's 2^23 goes into
-    // the multipliers where that is exact (uniform).
-    constexpr bool kCanFold = COL && !ROW && SR;
-    const bool fold = kCanFold && fold_sr_scale_ok<0>(sc.sg);
-    build_reciprocal_table(lds_rcp, sc.sg, fold ? kFoldFactor<SR, false> : 1.0f);
-    __syncthreads();
-
-    if (qa.valid) {
-        if (ROW && !kEarlyRows)
-            row_maxima(va, qa.odd, ba);
-        uint4 draws[16];
-        if (SR)
-            item_draws(p, qa, draws, false);
-        compute_item<ROW, COL, false, SR, false>(p, qa, va, ba, draws, sc, lds_rcp, lds_codes[0], lds_scales[0],
-                                                 fold);
-    }
-    if (has_b && qb.valid) {
-        if (ROW && !kEarlyRows)
-            row_maxima(vb, qb.odd, bb);
-        uint4 draws[16];
-        if (SR)
-            item_draws(p, qb, draws, false);
-        compute_item<ROW, COL, false, SR, false>(p, qb, vb, bb, draws, sc, lds_rcp, lds_codes[1], lds_scales[1],
-                                                 fold);
+        if (qa.valid) {
+            if (ROW && !kEarlyRows)
+                row_maxima(va, qa.odd, ba);
+            uint4 draws[16];
+            if (SR)
+                item_draws(p, qa, draws, false);
+            compute_item<ROW, COL, false, SR, false>(p, qa, va, ba, draws, sc, lds_rcp, lds_codes[0],
+                                                     lds_scales[0], fold);
+        }
+        if (has_b && qb.valid) {
+            if (ROW && !kEarlyRows)
+                row_maxima(vb, qb.odd, bb);
+            uint4 draws[16];
+            if (SR)
+                item_draws(p, qb, draws, false);
+            compute_item<ROW, COL, false, SR, false>(p, qb, vb, bb, draws, sc, lds_rcp, lds_codes[1],
+                                                     lds_scales[1], fold);
+        }
     }
     if (COL) {
         __syncthreads();
-        write_col_pair(p, qa.tile_r0, qa.tile_c0, lds_codes[0], lds_codes[1], lds_scales[0], lds_scales[1]);
+        write_col_pair<NT>(p, (int64_t)tra * kTileR, (int64_t)tc * kTileC, lds_codes[0], lds_codes[1],
+                           lds_scales[0], lds_scales[1]);
     }
 }
 
@@ -413,7 +454,7 @@ int fused_capacity()
         return c;
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(quantize_fused_kernel<ROW, COL, SR>), kThreads, 0) !=
+            &per_cu, reinterpret_cast<const void*>(quantize_fused_kernel<ROW, COL, SR>), kFusedThreads<SR>, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
@@ -430,7 +471,7 @@ hipError_t launch_fused_variant(Params p, uint32_t* ws, hipStream_t stream, bool
     const int grid = ((p.tiles_r + 1) / 2) * p.tiles_c;
     if (grid > kMaxFusedGrid || grid > fused_capacity<ROW, COL, SR>())
         return hipSuccess;
-    hipLaunchKernelGGL((quantize_fused_kernel<ROW, COL, SR>), dim3(grid), dim3(kThreads), 0, stream, p,
+    hipLaunchKernelGGL((quantize_fused_kernel<ROW, COL, SR>), dim3(grid), dim3(kFusedThreads<SR>), 0, stream, p,
                        ws);
     launched = true;
     return hipGetLastError();
@@ -442,7 +483,7 @@ hipError_t launch_paired(Params p, hipStream_t stream)
 {
     p.amax_given = 1;
     const int64_t grid = (int64_t)((p.tiles_r + 1) / 2) * p.tiles_c;
-    hipLaunchKernelGGL((quantize_fused_kernel<ROW, COL, SR>), dim3((unsigned)grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((quantize_fused_kernel<ROW, COL, SR>), dim3((unsigned)grid), dim3(kFusedThreads<SR>), 0,
                        stream, p, nullptr);
     return hipGetLastError();
 }
