@@ -612,8 +612,8 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
     }
     // Both layouts: the paired-tile kernel (whole-line columnwise stores,
     // here without its exchange) for round-to-nearest on tensors up to 2^25
-    // elements (8192x4096: 25 against 26.6 us); the one-tile kernel on
-    // larger ones (8192x14336: 78 against 88 us) and with stochastic
+    // elements (8192x4096: 22.2 against 23.9 us); the one-tile kernel on
+    // larger ones (8192x14336: 81-82 against 83-86 us) and with stochastic
     // rounding at every size (8192x4096: 43 against 57 us; 8192x14336: 144
     // against 204 us).
     if (a.rowwise && a.colwise) {
@@ -622,10 +622,15 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
         return a.sr ? launch_variant<true, true, false, true, false>(p, stream)
                     : launch_variant<true, true, false, false, false>(p, stream);
     }
-    // One layout: one tile per workgroup measured faster than the pairs.
+    // One layout: the rowwise codes leave as whole lines from either
+    // kernel, and one tile per workgroup measured faster (8192x4096: 16.9
+    // against 18.8 us); the columnwise-only output gains the pair's whole
+    // lines (17.5-17.9 against 18.5-18.6 us).
     if (a.rowwise)
         return a.sr ? launch_variant<true, false, false, true, false>(p, stream)
                     : launch_variant<true, false, false, false, false>(p, stream);
+    if (!a.sr && a.rows * a.cols <= ((int64_t)1 << 25))
+        return launch_paired<false, true, false>(p, stream);
     return a.sr ? launch_variant<false, true, false, true, false>(p, stream)
                 : launch_variant<false, true, false, false, false>(p, stream);
 }

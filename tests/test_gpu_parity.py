@@ -178,6 +178,7 @@ CASES_SMALL = [
     ("act_small", False, True, False, False),
     ("act_small", True, True, False, False),
     ("ragged_act", True, True, False, False),
+    ("ragged_act", False, True, False, False),
     ("ragged_act", True, False, True, False),
     ("ragged_act", False, True, True, False),
     ("ragged_act", True, True, True, False),
@@ -198,9 +199,9 @@ def test_quantize_1d_small(case):
 
 FULL_CASES = [
     # (workload, rowwise, colwise, sr, rht): the activation's layouts as the
-    # bench rows time them (both layouts with round-to-nearest take the
-    # paired-tile kernel, single layouts and stochastic rounding the
-    # one-tile kernel), the gradient path of the wgrad operands (transform +
+    # bench rows time them (round-to-nearest with columnwise output takes the
+    # paired-tile kernel, rowwise only and stochastic rounding the one-tile
+    # kernel), the gradient path of the wgrad operands (transform +
     # stochastic rounding, columnwise, seed 42, gradient and activation),
     # the transform with round-to-nearest, stochastic rounding without the
     # transform, and the gradient's rowwise dgrad operand.
