@@ -142,7 +142,7 @@ struct ScaleVote {
     uint32_t max_byte = 0u;
     __device__ __forceinline__ bool ok() const
     {
-        return min_y >= 0x3C800000u && min_guard >= 7u && max_byte <= 0x7Eu;
+        return min_y >= 0x3C800000u && min_guard >= (7u << 12) && max_byte <= 0x7Eu;
     }
 };
 
@@ -155,7 +155,9 @@ __device__ __forceinline__ uint32_t block_scale_byte_approx(uint32_t b_bits, flo
 {
     const uint32_t u = __float_as_uint(__uint_as_float(b_bits) * inv_t);
     vote.min_y = min(vote.min_y, u);
-    vote.min_guard = min(vote.min_guard, (u & 0xFFFFFu) - 0x7FFFDu);
+    // (low 20 bits of u) - 0x7FFFD, taken modulo 2^20 in the top 20 bits (one
+    // shift-add): below 7 << 12 exactly when that difference is 0..6.
+    vote.min_guard = min(vote.min_guard, (u << 12) - (0x7FFFDu << 12));
     const uint32_t byte = (u + (0x7FFFFu - (960u << 20)) + ((u >> 20) & 1u)) >> 20;
     vote.max_byte = max(vote.max_byte, byte);
     return byte;

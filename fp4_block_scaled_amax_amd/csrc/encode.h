@@ -129,7 +129,16 @@ __device__ __forceinline__ uint32_t cvt_pair(uint32_t old, float a, float b)
 
 // A fresh word whose bytes will all be written: its initial contents do not
 // matter, so let the compiler pick any register (no zero-fill).
-__device__ __forceinline__ uint32_t fresh_word() { return __builtin_nondeterministic_value(0u); }
+// A word whose every byte the caller writes before using it. The converter
+// writes one byte and keeps the register's others, so its destination is an
+// input: an empty asm statement defines the register without an instruction
+// (an undefined value folds to a zero that costs a move per word).
+__device__ __forceinline__ uint32_t fresh_word()
+{
+    uint32_t w;
+    asm volatile("" : "=v"(w));
+    return w;
+}
 
 template <int MODE, int BYTE>
 __device__ __forceinline__ uint32_t put_pair(uint32_t word, float a, float b, float r, uint32_t ha,

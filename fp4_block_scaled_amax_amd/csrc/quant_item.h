@@ -89,7 +89,8 @@ __device__ __forceinline__ void encode_row_pair(const uint4 (&v)[16], const floa
     constexpr int i = 2 * IP;
     constexpr int cb = IP & 3;     // byte within the column word
     constexpr int ch = IP >> 2;    // which column word (rows 0..7 or 8..15)
-    roww[0] = roww[1] = MODE == kEncSr ? 0u : fresh_word();
+    roww[0] = MODE == kEncSr ? 0u : fresh_word();
+    roww[1] = MODE == kEncSr ? 0u : fresh_word();
     if (MODE != kEncSr && COL && cb == 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
