@@ -711,22 +711,28 @@ def main():
         # block-scaled matrix cores with operands from the same values, and
         # the representation error of both formats.
         log("[bench] MXFP4 comparator")
-        mo = F.mxfp4_quantize(x, rowwise=True, colwise=True)
-        # (one input copy each: these rows read a tensor the Infinity Cache
-        # can partly hold between calls)
-        row_hbm("mx_quantize_rowwise_activation", lambda k: F.mxfp4_quantize(x, out=mo),
-                n_x * (2 + 0.5 + 1 / 32), [R, C])
+        # Like the NVFP4 rows, each call reads the next of the rotating input
+        # copies (more than the Infinity Cache holds) and writes that copy's
+        # own outputs.
+        xm = [x] + [to_dev(x_host) for _ in range(nc - 1)]
+        mos = [F.mxfp4_quantize(xm[k], rowwise=True, colwise=True) for k in range(nc)]
+        row_hbm("mx_quantize_rowwise_activation", lambda k: F.mxfp4_quantize(xm[k % nc], out=mos[k % nc]),
+                n_x * (2 + 0.5 + 1 / 32), [R, C], copies=nc)
         row_hbm("mx_quantize_row_and_col_activation",
-                lambda k: F.mxfp4_quantize(x, rowwise=True, colwise=True, out=mo),
-                n_x * (2 + 2 * (0.5 + 1 / 32)), [R, C])
-        mg = F.mxfp4_quantize(g, rowwise=False, colwise=True, rht=True, rht_mask=mask)
+                lambda k: F.mxfp4_quantize(xm[k % nc], rowwise=True, colwise=True, out=mos[k % nc]),
+                n_x * (2 + 2 * (0.5 + 1 / 32)), [R, C], copies=nc)
+        del xm[1:]
+        mgs = [F.mxfp4_quantize(gs[k], rowwise=False, colwise=True, rht=True, rht_mask=mask) for k in range(2)]
         row_hbm("mx_quantize_colwise_rht_gradient",
-                lambda k: F.mxfp4_quantize(g, rowwise=False, colwise=True, rht=True, rht_mask=mask, out=mg),
-                n_g * (2 + 0.5 + 1 / 32), [GR, GC])
+                lambda k: F.mxfp4_quantize(gs[k % 2], rowwise=False, colwise=True, rht=True, rht_mask=mask,
+                                           out=mgs[k % 2]),
+                n_g * (2 + 0.5 + 1 / 32), [GR, GC], copies=2)
+        del mgs
         mdq = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
         row_hbm("mx_dequantize_bf16_activation",
-                lambda k: F.mxfp4_dequantize(mo["codes_row"], mo["scales_row"], R, C, out_dtype=torch.bfloat16,
-                                             out=mdq), n_x * (0.5 + 1 / 32 + 2), [R, C])
+                lambda k: F.mxfp4_dequantize(mos[k % nc]["codes_row"], mos[k % nc]["scales_row"], R, C,
+                                             out_dtype=torch.bfloat16, out=mdq), n_x * (0.5 + 1 / 32 + 2), [R, C],
+                copies=nc)
         del mdq
         ma = F.mxfp4_quantize(A)
         mb = F.mxfp4_quantize(Bm)
@@ -742,7 +748,7 @@ def main():
                           "TFLOP/s": round(tf, 1), "bound": "mfma", "peak": FP4_MFMA_PEAK_TFLOPS,
                           "frac": round(tf / FP4_MFMA_PEAK_TFLOPS, 4)}
             log(f"[bench] {name}: {us:.0f} us {tf:.1f} TFLOP/s")
-        del ma, mb, mo, mg
+        del ma, mb, mos
         rows["error_study"] = error_study(F, {"activation": x, "weight": w, "gradient": g}, mask, dev)
         del g
         del flush

@@ -13,21 +13,22 @@
 // scale (nearest even, saturating at 6). In a NaN-scale block only the
 // elements' sign bits are kept, so every code has magnitude 0.
 //
-// Rowwise alone runs without LDS (mx_quantize_rows_kernel). Otherwise one
-// workgroup (256 threads) stages a 128 x 128 bf16 tile in LDS with
-// full-line loads, then:
-//   - rowwise: a thread takes one 32-element block of a row per pass (two
-//     passes); lanes 0..15 of a wave take 16 consecutive rows, so each
-//     group of 8 lanes' 16-byte LDS reads hits distinct banks (rows 272
-//     bytes apart);
-//   - columnwise: wave w takes row block w (32 rows) of all 128 columns,
-//     each lane a column pair read as 32 LDS words (256 contiguous bytes per
-//     wave read); with the Hadamard transform each 16-row half of a column
-//     is transformed in registers first (sign mask on the packed words,
-//     butterflies, 1/4), exactly as the NVFP4 columnwise path does.
-// Tiles are dealt to XCDs in runs that go down the rows, so the column
-// codes of vertically adjacent tiles (halves of one 128-byte line) meet in
-// one L2.
+// Three kernels:
+//   - rowwise alone, without LDS (mx_quantize_rows_kernel);
+//   - columnwise without the transform, alone or with the rowwise layout
+//     (mx_quantize_pair_kernel): 512 threads take a 256 x 256 block, one
+//     16 x 8 work item per thread in registers; a columnwise block is one
+//     column of lanes l and l ^ 32, a rowwise block one row of a lane quad;
+//     the columnwise codes are staged in LDS and leave as whole 128-byte
+//     lines;
+//   - columnwise with the Hadamard transform (mx_quantize_rht_kernel): a
+//     128 x 128 bf16 tile staged in LDS with full-line loads; wave w takes
+//     row block w (32 rows) of all 128 columns, each lane a column pair read
+//     as 32 LDS words, each 16-row half of a column transformed in registers
+//     (sign mask on the packed words, butterflies, 1/4) exactly as the
+//     NVFP4 columnwise path does. Its tiles are dealt to XCDs in runs that go
+//     down the rows, so the column codes of vertically adjacent tiles
+//     (halves of one 128-byte line) meet in one L2.
 #include "device.h"
 #include "kernels.h"
 
@@ -73,32 +74,6 @@ __device__ __forceinline__ uint32_t mx_word(const float (&v)[8])
     return w;
 }
 
-// One block of 32 bf16 held as 16 packed words -> 16 code bytes + scale.
-__device__ __forceinline__ uint4 mx_encode_bf16_block(const uint32_t (&w)[16], uint32_t& byte)
-{
-    uint32_t pm = 0u;
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-        pm = pk_max_u16(pm, w[k] & 0x7FFF7FFFu);
-    const uint32_t m = max(pm & 0xFFFFu, pm >> 16) << 16;
-    byte = mx_scale_byte(m);
-    const float inv = mx_inverse_scale(byte);
-    const uint32_t keep = byte == 0xFFu ? 0x80008000u : 0xFFFFFFFFu;
-    uint32_t out[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t x = w[4 * q + k] & keep;
-            v[2 * k] = bf16_lo(x) * inv;
-            v[2 * k + 1] = bf16_hi(x) * inv;
-        }
-        out[q] = mx_word(v);
-    }
-    return make_uint4(out[0], out[1], out[2], out[3]);
-}
-
 // One block of 32 binary32 values -> 16 code bytes + scale.
 __device__ __forceinline__ uint4 mx_encode_f32_block(const float (&y)[32], uint32_t& byte)
 {
@@ -131,8 +106,10 @@ __device__ __forceinline__ void mx_tile_of_block(int tiles_r, int tiles_c, int& 
     tc = t / tiles_r;
 }
 
-template <bool ROW, bool COL, bool RHT>
-__global__ __launch_bounds__(kThreads) void mx_quantize_kernel(MxQuantizeArgs p, int tiles_r, int tiles_c)
+// Columnwise with the axis-0 transform: the tile (128 x 128 bf16) is staged
+// in LDS, then each thread takes one column pair of one 32-row block, whose
+// two 16-row halves each go through the 16-point transform.
+__global__ __launch_bounds__(kThreads) void mx_quantize_rht_kernel(MxQuantizeArgs p, int tiles_r, int tiles_c)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kPitch];
     const int t = threadIdx.x;
@@ -140,9 +117,8 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(MxQuantizeArgs p,
     int tr, tc;
     mx_tile_of_block(tiles_r, tiles_c, tr, tc);
     const int64_t r0 = (int64_t)tr * kTR, c0 = (int64_t)tc * kTC;
-    // Rows / columns of this tile inside the tensor: the rowwise layout has
-    // whole 32-column blocks, the columnwise one whole 32-row blocks and
-    // 8-column chunks (16-byte loads); the other extent may be ragged.
+    // Rows / columns of this tile inside the tensor: whole 32-row blocks and
+    // 8-column chunks (16-byte loads); either extent may be ragged.
     const int nr = (int)min((int64_t)kTR, p.rows - r0);
     const int nc = (int)min((int64_t)kTC, p.cols - c0);
 
@@ -159,73 +135,315 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(MxQuantizeArgs p,
     }
     __syncthreads();
 
-    if (ROW) {
-        const int blk = lane >> 4;
+    const int rb = wave;       // row block of 32
+    const int cp = lane;       // column pair
+    if (rb * 32 < nr && cp * 2 < nc) {
+        uint32_t u[32];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = 16 * (wave + 4 * j) + (lane & 15);
-            if (r < nr && blk * 32 < nc) {
-                const uint8_t* src = tile + r * kPitch + blk * 64;
-                uint32_t w[16];
+        for (int i = 0; i < 32; ++i)
+            u[i] = *reinterpret_cast<const uint32_t*>(tile + (rb * 32 + i) * kPitch + cp * 4) ^
+                   rht_row_sign(p.mask, i & 15);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * i);
-                    w[4 * i] = v.x;
-                    w[4 * i + 1] = v.y;
-                    w[4 * i + 2] = v.z;
-                    w[4 * i + 3] = v.w;
-                }
-                uint32_t byte;
-                const uint4 codes = mx_encode_bf16_block(w, byte);
-                const int64_t row = r0 + r;
-                *reinterpret_cast<uint4*>(p.codes_row + row * (p.cols >> 1) + ((c0 >> 1) + blk * 16)) = codes;
-                p.scales_row[row * (p.cols >> 5) + (c0 >> 5) + blk] = (uint8_t)byte;
+        for (int h = 0; h < 2; ++h) {   // column 2cp + h: low / high halves
+            float y[32];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                float z[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    z[i] = h ? bf16_hi(u[16 * s + i]) : bf16_lo(u[16 * s + i]);
+                rht16_signed(z);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    y[16 * s + i] = z[i];
             }
+            uint32_t byte;
+            const uint4 codes = mx_encode_f32_block(y, byte);
+            const int64_t col = c0 + 2 * cp + h;
+            *reinterpret_cast<uint4*>(p.codes_col + col * (p.rows >> 1) + ((r0 >> 1) + rb * 16)) = codes;
+            p.scales_col[col * (p.rows >> 5) + (r0 >> 5) + rb] = (uint8_t)byte;
+        }
+    }
+}
+
+// ------------------------------------------------------------ paired tiles
+// Columnwise output without the transform (with or without the rowwise
+// layout): one workgroup of 512 threads takes a 256 x 256 block, one work
+// item of 16 rows x 8 columns per thread, loaded straight into registers.
+// Lane l of wave w holds rows 16 (2w + (l >> 5)) .. +15 and columns
+// 8 (l & 31) .. +7 of the block, so a columnwise block (32 rows) is one
+// column of lanes l and l ^ 32 (a permlane32 swap joins their maxima) and a
+// rowwise block (32 columns) is one row of the lane quad 4q .. 4q + 3 (two
+// DPP steps). Rowwise codes leave straight from registers (a half-wave
+// writes one 128-byte row segment); columnwise codes are staged in LDS and
+// leave as whole 128-byte lines per column.
+constexpr int kPairThreads = 512;
+constexpr int kPairRows = 256;
+constexpr int kPairCols = 256;
+
+// A word whose every byte is written before use (an empty asm statement
+// defines the register without an instruction).
+__device__ __forceinline__ uint32_t mx_fresh()
+{
+    uint32_t w;
+    asm volatile("" : "=v"(w));
+    return w;
+}
+
+// Scale byte n of four packed in a word.
+__device__ __forceinline__ uint32_t packed_byte(const uint32_t (&w)[4], int n)
+{
+    return (w[n >> 2] >> (8 * (n & 3))) & 0xFFu;
+}
+
+// The value of lane K of each lane quad, on all four lanes.
+template <int K>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, K | (K << 2) | (K << 4) | (K << 6), 0xF, 0xF, false);
+}
+
+// Row I's multiplier (and, SAFE, its mask): lane I & 3 of the quad holds
+// rows 4m + (I & 3) in slot m = I >> 2.
+template <int I>
+__device__ __forceinline__ float row_mult(const float (&rm)[4])
+{
+    return __uint_as_float(quad_bcast<I & 3>(__float_as_uint(rm[I >> 2])));
+}
+template <int I>
+__device__ __forceinline__ uint32_t row_keep(uint32_t rown)
+{
+    const uint32_t own = ((rown >> (8 * (I >> 2))) & 0xFFu) == 0xFFu ? 0x80008000u : 0xFFFFFFFFu;
+    return quad_bcast<I & 3>(own);
+}
+
+// Encode rows 2 IP, 2 IP + 1 of an item: byte K of the two row words
+// (columns 2K, 2K+1) and byte IP & 3 of column words 2K, 2K+1. SAFE: some
+// blocks may have a non-finite maximum (byte 0xFF, multiplier 1), whose
+// values become signed zeros; the masks come from the packed row bytes rb
+// (rows 4m .. 4m + 3 in word m) and column bytes cb (columns likewise).
+template <int IP, bool ROW, bool SAFE>
+__device__ __forceinline__ void mx_pair_rows(const uint4 (&v)[16], const float (&rm)[4], const float (&rc)[8],
+                                             uint32_t rown, const uint32_t (&cbt)[4],
+                                             uint32_t (&roww)[2], uint32_t (&colw)[8][2])
+{
+    constexpr int i = 2 * IP, cb = IP & 3, ch = IP >> 2;
+    uint32_t kr0 = 0xFFFFFFFFu, kr1 = 0xFFFFFFFFu;
+    float rr0 = 1.0f, rr1 = 1.0f;
+    if (ROW) {
+        rr0 = row_mult<i>(rm);
+        rr1 = row_mult<i + 1>(rm);
+        if (SAFE) {
+            kr0 = row_keep<i>(rown);
+            kr1 = row_keep<i + 1>(rown);
+        }
+    }
+    if (ROW) {
+        roww[0] = mx_fresh();
+        roww[1] = mx_fresh();
+    }
+    if (cb == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            colw[j][ch] = mx_fresh();
+    }
+#define MX_GROUP(K)                                                                                     \
+    {                                                                                                   \
+        uint32_t w0 = word_at(v[i], K), w1 = word_at(v[i + 1], K);                                      \
+        uint32_t kcw = 0xFFFFFFFFu;                                                                     \
+        if (SAFE) {                                                                                     \
+            asm volatile("" : "+v"(w0), "+v"(w1));                                                      \
+            kcw = (packed_byte(cbt, 2 * K) == 0xFFu ? 0x8000u : 0xFFFFu) |                              \
+                  (packed_byte(cbt, 2 * K + 1) == 0xFFu ? 0x80000000u : 0xFFFF0000u);                   \
+        }                                                                                               \
+        if (ROW) {                                                                                      \
+            const uint32_t x0 = SAFE ? (w0 & kr0) : w0, x1 = SAFE ? (w1 & kr1) : w1;                    \
+            roww[0] = mx_pair<K>(roww[0], bf16_lo(x0) * rr0, bf16_hi(x0) * rr0);                        \
+            roww[1] = mx_pair<K>(roww[1], bf16_lo(x1) * rr1, bf16_hi(x1) * rr1);                        \
+        }                                                                                               \
+        const uint32_t y0 = SAFE ? (w0 & kcw) : w0, y1 = SAFE ? (w1 & kcw) : w1;                        \
+        colw[2 * K][ch] = mx_pair<cb>(colw[2 * K][ch], bf16_lo(y0) * rc[2 * K], bf16_lo(y1) * rc[2 * K]); \
+        colw[2 * K + 1][ch] =                                                                           \
+            mx_pair<cb>(colw[2 * K + 1][ch], bf16_hi(y0) * rc[2 * K + 1], bf16_hi(y1) * rc[2 * K + 1]);   \
+    }
+    MX_GROUP(0) MX_GROUP(1) MX_GROUP(2) MX_GROUP(3)
+#undef MX_GROUP
+}
+
+template <bool ROW, bool SAFE>
+__device__ __forceinline__ void mx_encode_item(const uint4 (&v)[16], const float (&rm)[4], const float (&rc)[8],
+                                               uint32_t rown, const uint32_t (&cbt)[4],
+                                               uint8_t* row_dst, int64_t row_pitch, uint32_t* lds_words,
+                                               int col_slot)
+{
+    uint32_t roww[2];
+    uint32_t colw[8][2];
+#define MX_ROWS(IP)                                                                                  \
+    mx_pair_rows<IP, ROW, SAFE>(v, rm, rc, rown, cbt, roww, colw);                                 \
+    if (ROW) {                                                                                       \
+        __builtin_nontemporal_store(roww[0], reinterpret_cast<uint32_t*>(row_dst + (2 * IP) * row_pitch)); \
+        __builtin_nontemporal_store(roww[1], reinterpret_cast<uint32_t*>(row_dst + (2 * IP + 1) * row_pitch)); \
+    }
+#define MX_HALF(H)                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                    \
+        lds_words[2 * (col_slot + 16 * j) + H] = colw[j][H];  /* column 8 cg + j */
+    MX_ROWS(0) MX_ROWS(1) MX_ROWS(2) MX_ROWS(3)
+    MX_HALF(0)
+    MX_ROWS(4) MX_ROWS(5) MX_ROWS(6) MX_ROWS(7)
+    MX_HALF(1)
+#undef MX_HALF
+#undef MX_ROWS
+}
+
+template <bool ROW>
+__global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void mx_quantize_pair_kernel(MxQuantizeArgs p, int blocks_c)
+{
+    __shared__ uint2 lds_codes[kPairCols * 16];    // [column][16-row group, swizzled]
+    __shared__ uint8_t lds_scales[kPairCols * 8];  // [column][32-row block]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cg = lane & 31;
+    const int rg = 2 * wave + (lane >> 5);  // 16-row group of the block, 0..15
+    const int64_t br0 = (int64_t)(blockIdx.x / blocks_c) * kPairRows;
+    const int64_t bc0 = (int64_t)(blockIdx.x % blocks_c) * kPairCols;
+    const int64_t r0 = br0 + 16 * rg, c0 = bc0 + 8 * cg;
+    // rows % 32 == 0 and cols % 8 == 0 (32 with the rowwise layout): an item
+    // is whole or absent, and lanes l, l ^ 32 and each quad agree. Every lane
+    // takes part in the cross-lane steps; an absent item loads the first one
+    // (always present) and stores nothing.
+    const bool valid = r0 < p.rows && c0 < p.cols;
+    uint4 v[16];
+    {
+        const uint16_t* src = p.x + (valid ? r0 * p.cols + c0 : 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            v[i] = load16_stream(src + i * p.cols);
+    }
+
+    // Block maxima as |bf16| patterns: colm[k] packs columns 2k, 2k+1 over
+    // the item's 16 rows; rowm[k] packs rows 2k, 2k+1 over its 8 columns.
+    uint32_t colm[4] = {0u, 0u, 0u, 0u};
+    uint32_t rowm[8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t w0 = v[i].x & 0x7FFF7FFFu, w1 = v[i].y & 0x7FFF7FFFu;
+        const uint32_t w2 = v[i].z & 0x7FFF7FFFu, w3 = v[i].w & 0x7FFF7FFFu;
+        colm[0] = pk_max_u16(colm[0], w0);
+        colm[1] = pk_max_u16(colm[1], w1);
+        colm[2] = pk_max_u16(colm[2], w2);
+        colm[3] = pk_max_u16(colm[3], w3);
+        if (ROW) {
+            const uint32_t pm = pk_max_u16(pk_max_u16(w0, w1), pk_max_u16(w2, w3));
+            const uint32_t m = max(pm & 0xFFFFu, pm >> 16);
+            rowm[i >> 1] = (i & 1) ? (rowm[i >> 1] | (m << 16)) : m;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const auto r = __builtin_amdgcn_permlane32_swap(colm[k], colm[k], false, false);
+        colm[k] = pk_max_u16(r[0], r[1]);  // this lane's and lane l ^ 32's
+    }
+    if (ROW) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t t = rowm[k];
+            t = pk_max_u16(t, (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0xB1, 0xF, 0xF, false));  // lane ^ 1
+            t = pk_max_u16(t, (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0x4E, 0xF, 0xF, false));  // lane ^ 2
+            rowm[k] = t;
         }
     }
 
-    if (COL) {
-        const int rb = wave;       // row block of 32
-        const int cp = lane;       // column pair
-        if (rb * 32 < nr && cp * 2 < nc) {
-            uint32_t u[32];
+    // Scale bytes and multipliers: all eight column blocks; of the 16
+    // rowwise blocks, which the four lanes of a quad share, lane t computes
+    // and stores rows 4m + t (slot m) and lends them to the others by DPP.
+    float rc[8], rm[4];
+    uint32_t cbytes[4] = {0u, 0u, 0u, 0u};  // columns 4m .. 4m + 3 in word m (m < 2)
+    uint32_t rown = 0u;                      // rows 4m + t in byte m
+    bool any_ff = false;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                u[i] = *reinterpret_cast<const uint32_t*>(tile + (rb * 32 + i) * kPitch + cp * 4);
-                if (RHT)
-                    u[i] ^= rht_row_sign(p.mask, i & 15);
-            }
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t bits = (j & 1) ? (colm[j >> 1] & 0xFFFF0000u) : (colm[j >> 1] << 16);
+        const uint32_t byte = mx_scale_byte(bits);
+        rc[j] = mx_inverse_scale(byte);
+        any_ff = any_ff || byte == 0xFFu;
+        cbytes[j >> 2] |= byte << (8 * (j & 3));
+    }
+    if (ROW) {
+        const int t = lane & 3;
+        // row 4m + t: half t & 1 of rowm[2m + (t >> 1)], picked by masks (a
+        // select here becomes an indexed load from a stack copy of rowm)
+        const uint32_t hi_word = 0u - (uint32_t)(t >> 1);
+        const int half_shift = (t & 1) ? 0 : 16;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {   // column 2cp + h: low / high halves
-                uint32_t byte;
-                uint4 codes;
-                if (RHT) {
-                    float y[32];
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t w = (rowm[2 * m] & ~hi_word) | (rowm[2 * m + 1] & hi_word);
+            const uint32_t bits = (w << half_shift) & 0xFFFF0000u;
+            const uint32_t byte = mx_scale_byte(bits);
+            rm[m] = mx_inverse_scale(byte);
+            any_ff = any_ff || byte == 0xFFu;
+            rown |= byte << (8 * m);
+        }
+        if (valid) {
+            uint8_t* sdst = p.scales_row + (r0 + t) * (p.cols >> 5) + (c0 >> 5);
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        float z[16];
+            for (int m = 0; m < 4; ++m)
+                sdst[4 * m * (p.cols >> 5)] = (uint8_t)(rown >> (8 * m));
+        }
+    } else {
 #pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            z[i] = h ? bf16_hi(u[16 * s + i]) : bf16_lo(u[16 * s + i]);
-                        rht16_signed(z);
+        for (int m = 0; m < 4; ++m)
+            rm[m] = 1.0f;
+    }
+    if (lane < 32) {  // the lower lane of each l, l ^ 32 pair stages the column scales
 #pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            y[16 * s + i] = z[i];
-                    }
-                    codes = mx_encode_f32_block(y, byte);
-                } else {
-                    // this column's 32 values as 16 packed words
-                    uint32_t w[16];
+        for (int j = 0; j < 8; ++j)
+            lds_scales[(8 * cg + j) * 8 + (rg >> 1)] = (uint8_t)packed_byte(cbytes, j);
+    }
+
+    uint8_t* const row_dst = ROW ? p.codes_row + r0 * (p.cols >> 1) + (c0 >> 1) : nullptr;
+    uint32_t* const lds_words = reinterpret_cast<uint32_t*>(lds_codes);
+    const int col_slot = (8 * cg) * 16 + (rg ^ (cg & 15));
+    if (valid) {
+        if (__any(any_ff))
+            mx_encode_item<ROW, true>(v, rm, rc, rown, cbytes, row_dst, p.cols >> 1, lds_words, col_slot);
+        else
+            mx_encode_item<ROW, false>(v, rm, rc, rown, cbytes, row_dst, p.cols >> 1, lds_words, col_slot);
+    }
+    __syncthreads();
+
+    // Columnwise codes: per column 256 rows = 128 bytes, written by 8 lanes
+    // as 16-byte streaming stores (rows % 32 == 0 keeps every chunk whole and
+    // aligned).
+    typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+    const int64_t pitch = p.rows >> 1;
 #pragma unroll
-                    for (int k = 0; k < 16; ++k) {
-                        const uint32_t a = u[2 * k], b = u[2 * k + 1];
-                        w[k] = h ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-                    }
-                    codes = mx_encode_bf16_block(w, byte);
-                }
-                const int64_t col = c0 + 2 * cp + h;
-                *reinterpret_cast<uint4*>(p.codes_col + col * (p.rows >> 1) + ((r0 >> 1) + rb * 16)) = codes;
-                p.scales_col[col * (p.rows >> 5) + (r0 >> 5) + rb] = (uint8_t)byte;
+    for (int k = 0; k < kPairCols * 8 / kPairThreads; ++k) {
+        const int q = k * kPairThreads + threadIdx.x;
+        const int col = q >> 3, part = q & 7;  // part: rows 32 part .. + 31
+        const int64_t c = bc0 + col, r = br0 + 32 * part;
+        if (c < p.cols && r < p.rows) {
+            const int swz = (col >> 3) & 15;
+            const uint2 lo = lds_codes[col * 16 + ((2 * part) ^ swz)];
+            const uint2 hi = lds_codes[col * 16 + ((2 * part + 1) ^ swz)];
+            __builtin_nontemporal_store(u32x4_nt{lo.x, lo.y, hi.x, hi.y},
+                                        reinterpret_cast<u32x4_nt*>(p.codes_col + c * pitch + (r >> 1)));
+        }
+    }
+    // Columnwise scales: one column's 8 bytes per thread.
+    if (threadIdx.x < kPairCols) {
+        const int col = threadIdx.x;
+        const int64_t c = bc0 + col;
+        if (c < p.cols) {
+            const int64_t spitch = p.rows >> 5;
+            uint8_t* dst = p.scales_col + c * spitch + (br0 >> 5);
+            const int64_t nb64 = (p.rows - br0) >> 5;
+            const int nb = nb64 < 8 ? (int)nb64 : 8;
+            const uint8_t* src = &lds_scales[col * 8];
+            if (nb == 8 && (reinterpret_cast<uintptr_t>(dst) & 7) == 0) {
+                *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+            } else {
+                for (int b = 0; b < nb; ++b)
+                    dst[b] = src[b];
             }
         }
     }
@@ -337,16 +555,6 @@ __global__ __launch_bounds__(kThreads) void mx_dequantize_kernel(const uint8_t* 
     }
 }
 
-template <bool ROW, bool COL, bool RHT>
-hipError_t launch_mx_variant(const MxQuantizeArgs& a, hipStream_t stream)
-{
-    const int tiles_r = (int)((a.rows + kTR - 1) / kTR);
-    const int tiles_c = (int)((a.cols + kTC - 1) / kTC);
-    hipLaunchKernelGGL((mx_quantize_kernel<ROW, COL, RHT>), dim3((unsigned)(tiles_r * tiles_c)),
-                       dim3(kThreads), 0, stream, a, tiles_r, tiles_c);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_mx_quantize(const MxQuantizeArgs& a, hipStream_t stream)
@@ -361,12 +569,23 @@ hipError_t launch_mx_quantize(const MxQuantizeArgs& a, hipStream_t stream)
                            a.codes_row, a.scales_row);
         return hipGetLastError();
     }
-    if (a.rowwise && a.colwise)
-        return a.rht ? hipErrorInvalidValue : launch_mx_variant<true, true, false>(a, stream);
+    if (a.colwise && !a.rht) {
+        const int blocks_r = (int)((a.rows + kPairRows - 1) / kPairRows);
+        const int blocks_c = (int)((a.cols + kPairCols - 1) / kPairCols);
+        const dim3 grid((unsigned)((int64_t)blocks_r * blocks_c));
+        if (a.rowwise)
+            hipLaunchKernelGGL(mx_quantize_pair_kernel<true>, grid, dim3(kPairThreads), 0, stream, a, blocks_c);
+        else
+            hipLaunchKernelGGL(mx_quantize_pair_kernel<false>, grid, dim3(kPairThreads), 0, stream, a, blocks_c);
+        return hipGetLastError();
+    }
     if (a.rowwise)
-        return a.rht ? hipErrorInvalidValue : launch_mx_variant<true, false, false>(a, stream);
-    return a.rht ? launch_mx_variant<false, true, true>(a, stream)
-                 : launch_mx_variant<false, true, false>(a, stream);
+        return hipErrorInvalidValue;  // the transform is columnwise only
+    const int tiles_r = (int)((a.rows + kTR - 1) / kTR);
+    const int tiles_c = (int)((a.cols + kTC - 1) / kTC);
+    hipLaunchKernelGGL(mx_quantize_rht_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(kThreads), 0, stream, a,
+                       tiles_r, tiles_c);
+    return hipGetLastError();
 }
 
 hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
