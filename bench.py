@@ -722,12 +722,13 @@ def main():
                 lambda k: F.mxfp4_quantize(xm[k % nc], rowwise=True, colwise=True, out=mos[k % nc]),
                 n_x * (2 + 2 * (0.5 + 1 / 32)), [R, C], copies=nc)
         del xm[1:]
-        mgs = [F.mxfp4_quantize(gs[k], rowwise=False, colwise=True, rht=True, rht_mask=mask) for k in range(2)]
+        gm = [g, g.clone()]  # 448 MiB rotate past the Infinity Cache
+        mgs = [F.mxfp4_quantize(gm[k], rowwise=False, colwise=True, rht=True, rht_mask=mask) for k in range(2)]
         row_hbm("mx_quantize_colwise_rht_gradient",
-                lambda k: F.mxfp4_quantize(gs[k % 2], rowwise=False, colwise=True, rht=True, rht_mask=mask,
+                lambda k: F.mxfp4_quantize(gm[k % 2], rowwise=False, colwise=True, rht=True, rht_mask=mask,
                                            out=mgs[k % 2]),
                 n_g * (2 + 0.5 + 1 / 32), [GR, GC], copies=2)
-        del mgs
+        del mgs, gm
         mdq = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
         row_hbm("mx_dequantize_bf16_activation",
                 lambda k: F.mxfp4_dequantize(mos[k % nc]["codes_row"], mos[k % nc]["scales_row"], R, C,

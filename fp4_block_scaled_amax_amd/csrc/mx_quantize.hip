@@ -460,14 +460,18 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_rows_kernel(const uint16
                                                                    uint8_t* __restrict__ codes,
                                                                    uint8_t* __restrict__ scales)
 {
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    // Each pass of a workgroup takes U * 256 consecutive vectors, one
+    // contiguous span (its U loads per thread are 4 KB runs side by side),
+    // read past the caches.
+    constexpr int64_t stride = kThreads;
     const bool first = (threadIdx.x & 3) == 0;
-    for (int64_t v0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; v0 < nvec; v0 += U * stride) {
+    for (int64_t v0 = (int64_t)blockIdx.x * kThreads * U + threadIdx.x; v0 < nvec;
+         v0 += (int64_t)gridDim.x * kThreads * U) {
         uint4 w[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t v = v0 + u * stride;
-            w[u] = load16(x + 8 * (v < nvec ? v : 0));  // a quad is all in or all out
+            w[u] = load16_stream(x + 8 * (v < nvec ? v : 0));  // a quad is all in or all out
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
