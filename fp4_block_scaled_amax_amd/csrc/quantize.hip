@@ -83,9 +83,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
 }
 
 // ---------------------------------------------------------------------------
-// Fused amax + quantize: one persistent launch in which every thread keeps
-// two work items (2 x 256 bytes of bf16) in registers, so the tensor is read
-// from HBM once. The workgroups exchange their block-local maxima through a
+// Fused amax + quantize: one persistent launch in which each workgroup keeps
+// two vertically adjacent tiles in registers (one 256-byte work item per
+// thread with round to nearest, two with stochastic rounding), so the
+// tensor is read from HBM once. The workgroups exchange their block-local maxima through a
 // small workspace without read-modify-write atomics: each workgroup posts
 // (generation, max) in its own arrival slot, workgroup 0 collects them all
 // and posts (generation, amax) in every workgroup's own release slot, so no
