@@ -82,6 +82,112 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(Params p)
     }
 }
 
+// Rowwise only: the tensor read as a flat array of 16-byte vectors (8
+// elements each). A lane takes one vector, so the lane pair (2k, 2k + 1)
+// holds one 16-element block (cols is a multiple of 16, so no block
+// straddles two rows) and one DPP swap gives its maximum. A workgroup takes
+// kFlatU x 256 consecutive vectors (kFlatU 4 KB runs side by side) with
+// streaming loads, issued before it builds its multiplier table; the codes
+// leave as one 32-bit store per lane (1 KB contiguous per wave), the scale
+// byte from the even lane of each pair. With stochastic rounding a vector's
+// 8 draws are one Philox call whose counter is the vector's index (the
+// flat index / 8, as everywhere), computed while the loads are in flight.
+constexpr int kFlatU = 4;
+
+template <int MODE>
+__device__ __forceinline__ uint32_t encode_vector8(uint4 w, float r, const uint4& d)
+{
+    if (MODE == kEncHwSafe || MODE == kEncSr)  // keep the rare encoders' unpacking their own
+        asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+    uint32_t word = MODE == kEncSr ? 0u : fresh_word();
+#define NVFP4_FLAT_PAIR(K, X)                                                                         \
+    word = put_pair<MODE, K>(word, bf16_lo(w.X), bf16_hi(w.X), r,                                     \
+                             is_sr(MODE) ? sr_input<MODE>(d, 2 * K) : 0u,                             \
+                             is_sr(MODE) ? sr_input<MODE>(d, 2 * K + 1) : 0u);
+    NVFP4_FLAT_PAIR(0, x) NVFP4_FLAT_PAIR(1, y) NVFP4_FLAT_PAIR(2, z) NVFP4_FLAT_PAIR(3, w)
+#undef NVFP4_FLAT_PAIR
+    return word;
+}
+
+template <bool SR>
+__global__ __launch_bounds__(kThreads) void quantize_rows_flat_kernel(Params p, int64_t nvec)
+{
+    __shared__ float lds_rcp[128];
+    const int64_t v0 = (int64_t)blockIdx.x * kThreads * kFlatU + threadIdx.x;
+    uint4 w[kFlatU];
+#pragma unroll
+    for (int u = 0; u < kFlatU; ++u) {
+        const int64_t v = v0 + u * kThreads;
+        w[u] = load16_stream(p.x + 8 * (v < nvec ? v : 0));  // a lane pair is all in or all out
+    }
+    uint4 draws[kFlatU];
+    if (SR) {
+#pragma unroll
+        for (int u = 0; u < kFlatU; ++u) {
+            const uint64_t v = (uint64_t)(v0 + u * kThreads);
+            draws[u] = philox4x32_10((uint32_t)v, (uint32_t)(v >> 32), p.seed_lo, p.seed_hi);
+        }
+    }
+    const ScaleCtx sc = scale_ctx(*p.amax);
+    if (p.sg_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+        *p.sg_out = sc.sg;
+    build_reciprocal_table(lds_rcp, sc.sg);
+    __syncthreads();
+
+    // Block maxima and scale bytes by the approximate chain, checked once
+    // for the wave (as in the item code); the exact chain where it cannot
+    // settle them.
+    uint32_t bits[kFlatU], byte[kFlatU];
+    ScaleVote vote;
+#pragma unroll
+    for (int u = 0; u < kFlatU; ++u) {
+        const uint32_t pm = pk_max_u16(pk_max_u16(w[u].x & 0x7FFF7FFFu, w[u].y & 0x7FFF7FFFu),
+                                       pk_max_u16(w[u].z & 0x7FFF7FFFu, w[u].w & 0x7FFF7FFFu));
+        uint32_t m = max(pm & 0xFFFFu, pm >> 16);
+        m = max(m, swap_lane1(m));
+        bits[u] = m << 16;
+        byte[u] = block_scale_byte_approx(bits[u], sc.inv_t6, vote);
+    }
+    bool fin = sc.table_ok;
+    if (!__all(sc.fast && vote.ok())) {
+        uint32_t mb = 0u;
+#pragma unroll
+        for (int u = 0; u < kFlatU; ++u) {
+            byte[u] = scale_byte(bits[u], sc);
+            mb = max(mb, byte[u]);
+        }
+        fin = fin && mb <= 0x7Eu;  // 0x7F (a NaN block) has no finite multiplier
+    }
+    float r[kFlatU];
+#pragma unroll
+    for (int u = 0; u < kFlatU; ++u)
+        r[u] = lds_rcp[byte[u]];
+    if (!sc.table_ok) {
+        fin = true;
+#pragma unroll
+        for (int u = 0; u < kFlatU; ++u)
+            fin = fin && finite_bits(r[u]);
+    }
+    const bool all_fin = __all(fin);
+    const bool even = (threadIdx.x & 1) == 0;
+#pragma unroll
+    for (int u = 0; u < kFlatU; ++u) {
+        const int64_t v = v0 + u * kThreads;
+        if (v < nvec) {
+            uint32_t code;
+            if (SR)
+                code = all_fin ? encode_vector8<kEncSrHw>(w[u], r[u], draws[u])
+                               : encode_vector8<kEncSr>(w[u], r[u], draws[u]);
+            else
+                code = all_fin ? encode_vector8<kEncHw>(w[u], r[u], draws[u])
+                               : encode_vector8<kEncHwSafe>(w[u], r[u], draws[u]);
+            __builtin_nontemporal_store(code, reinterpret_cast<uint32_t*>(p.codes_row) + v);
+            if (even)
+                p.scales_row[v >> 1] = (uint8_t)byte[u];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Fused amax + quantize: one persistent launch in which each workgroup keeps
 // two vertically adjacent tiles in registers (one 256-byte work item per
@@ -623,13 +729,21 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
         return a.sr ? launch_variant<true, true, false, true, false>(p, stream)
                     : launch_variant<true, true, false, false, false>(p, stream);
     }
-    // One layout: the rowwise codes leave as whole lines from either
-    // kernel, and one tile per workgroup measured faster (8192x4096: 16.9
-    // against 18.8 us); the columnwise-only output gains the pair's whole
-    // lines (17.5-17.9 against 18.5-18.6 us).
-    if (a.rowwise)
-        return a.sr ? launch_variant<true, false, false, true, false>(p, stream)
-                    : launch_variant<true, false, false, false, false>(p, stream);
+    // One layout. Rowwise: the flat kernel (8192x4096: 15.4 against 16.9 us
+    // for one tile per workgroup and 18.8 for the pairs; with stochastic
+    // rounding 23-24 against 27-27.5 us). Columnwise: the pairs' whole lines
+    // (17.5-17.9 against 18.5-18.6 us for one tile per workgroup).
+    if (a.rowwise) {
+        const int64_t nvec = a.rows * a.cols / 8;
+        const int64_t grid = (nvec + kThreads * kFlatU - 1) / (kThreads * kFlatU);
+        if (a.sr)
+            hipLaunchKernelGGL(quantize_rows_flat_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p,
+                               nvec);
+        else
+            hipLaunchKernelGGL(quantize_rows_flat_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p,
+                               nvec);
+        return hipGetLastError();
+    }
     if (!a.sr && a.rows * a.cols <= ((int64_t)1 << 25))
         return launch_paired<false, true, false>(p, stream);
     return a.sr ? launch_variant<false, true, false, true, false>(p, stream)
