@@ -13,22 +13,16 @@
 // scale (nearest even, saturating at 6). In a NaN-scale block only the
 // elements' sign bits are kept, so every code has magnitude 0.
 //
-// Three kernels:
+// Two kernels:
 //   - rowwise alone, without LDS (mx_quantize_rows_kernel);
-//   - columnwise without the transform, alone or with the rowwise layout
-//     (mx_quantize_pair_kernel): 512 threads take a 256 x 256 block, one
-//     16 x 8 work item per thread in registers; a columnwise block is one
-//     column of lanes l and l ^ 32, a rowwise block one row of a lane quad;
-//     the columnwise codes are staged in LDS and leave as whole 128-byte
-//     lines;
-//   - columnwise with the Hadamard transform (mx_quantize_rht_kernel): a
-//     128 x 128 bf16 tile staged in LDS with full-line loads; wave w takes
-//     row block w (32 rows) of all 128 columns, each lane a column pair read
-//     as 32 LDS words, each 16-row half of a column transformed in registers
-//     (sign mask on the packed words, butterflies, 1/4) exactly as the
-//     NVFP4 columnwise path does. Its tiles are dealt to XCDs in runs that go
-//     down the rows, so the column codes of vertically adjacent tiles
-//     (halves of one 128-byte line) meet in one L2.
+//   - any columnwise output (mx_quantize_pair_kernel): 512 threads take a
+//     256 x 256 block, one 16 x 8 work item per thread in registers; a
+//     columnwise block is one column of lanes l and l ^ 32, a rowwise block
+//     one row of a lane quad; with the Hadamard transform (columnwise only)
+//     each column of an item, one 16-row group, is sign-flipped on the packed
+//     words, butterflied and scaled by 1/4 in registers exactly as the NVFP4
+//     columnwise path does; the columnwise codes are staged in LDS and leave
+//     as whole 128-byte lines.
 #include "device.h"
 #include "kernels.h"
 
@@ -37,9 +31,6 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTR = 128;                 // tile rows
-constexpr int kTC = 128;                 // tile columns (bf16)
-constexpr int kPitch = kTC * 2 + 16;     // LDS row pitch in bytes
 
 // E8M0 byte of a block from the bit pattern of its maximum |x| (binary32).
 __device__ __forceinline__ uint32_t mx_scale_byte(uint32_t m)
@@ -72,98 +63,6 @@ __device__ __forceinline__ uint32_t mx_word(const float (&v)[8])
     w = mx_pair<2>(w, v[4], v[5]);
     w = mx_pair<3>(w, v[6], v[7]);
     return w;
-}
-
-// One block of 32 binary32 values -> 16 code bytes + scale.
-__device__ __forceinline__ uint4 mx_encode_f32_block(const float (&y)[32], uint32_t& byte)
-{
-    uint32_t m = 0u;
-#pragma unroll
-    for (int k = 0; k < 32; ++k)
-        m = max(m, __float_as_uint(y[k]) & 0x7FFFFFFFu);
-    byte = mx_scale_byte(m);
-    const float inv = mx_inverse_scale(byte);
-    const uint32_t keep = byte == 0xFFu ? 0x80000000u : 0xFFFFFFFFu;
-    uint32_t out[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            v[k] = __uint_as_float(__float_as_uint(y[8 * q + k]) & keep) * inv;
-        out[q] = mx_word(v);
-    }
-    return make_uint4(out[0], out[1], out[2], out[3]);
-}
-
-__device__ __forceinline__ void mx_tile_of_block(int tiles_r, int tiles_c, int& tr, int& tc)
-{
-    const int nt = tiles_r * tiles_c;
-    int t = blockIdx.x;
-    if ((nt & 7) == 0)
-        t = (t & 7) * (nt >> 3) + (t >> 3);
-    tr = t % tiles_r;
-    tc = t / tiles_r;
-}
-
-// Columnwise with the axis-0 transform: the tile (128 x 128 bf16) is staged
-// in LDS, then each thread takes one column pair of one 32-row block, whose
-// two 16-row halves each go through the 16-point transform.
-__global__ __launch_bounds__(kThreads) void mx_quantize_rht_kernel(MxQuantizeArgs p, int tiles_r, int tiles_c)
-{
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kPitch];
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    int tr, tc;
-    mx_tile_of_block(tiles_r, tiles_c, tr, tc);
-    const int64_t r0 = (int64_t)tr * kTR, c0 = (int64_t)tc * kTC;
-    // Rows / columns of this tile inside the tensor: whole 32-row blocks and
-    // 8-column chunks (16-byte loads); either extent may be ragged.
-    const int nr = (int)min((int64_t)kTR, p.rows - r0);
-    const int nc = (int)min((int64_t)kTC, p.cols - c0);
-
-    // Stage the tile: 128 rows x 16 chunks of 16 bytes; 8 chunks per thread,
-    // 16 consecutive threads per row (one 256-byte span).
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int q = t + kThreads * i;
-        const int r = q >> 4, part = q & 15;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (r < nr && part * 8 < nc)
-            v = load16(p.x + (r0 + r) * p.cols + c0 + part * 8);
-        *reinterpret_cast<uint4*>(tile + r * kPitch + part * 16) = v;
-    }
-    __syncthreads();
-
-    const int rb = wave;       // row block of 32
-    const int cp = lane;       // column pair
-    if (rb * 32 < nr && cp * 2 < nc) {
-        uint32_t u[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-            u[i] = *reinterpret_cast<const uint32_t*>(tile + (rb * 32 + i) * kPitch + cp * 4) ^
-                   rht_row_sign(p.mask, i & 15);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {   // column 2cp + h: low / high halves
-            float y[32];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                float z[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    z[i] = h ? bf16_hi(u[16 * s + i]) : bf16_lo(u[16 * s + i]);
-                rht16_signed(z);
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    y[16 * s + i] = z[i];
-            }
-            uint32_t byte;
-            const uint4 codes = mx_encode_f32_block(y, byte);
-            const int64_t col = c0 + 2 * cp + h;
-            *reinterpret_cast<uint4*>(p.codes_col + col * (p.rows >> 1) + ((r0 >> 1) + rb * 16)) = codes;
-            p.scales_col[col * (p.rows >> 5) + (r0 >> 5) + rb] = (uint8_t)byte;
-        }
-    }
 }
 
 // ------------------------------------------------------------ paired tiles
@@ -295,10 +194,45 @@ __device__ __forceinline__ void mx_encode_item(const uint4 (&v)[16], const float
 #undef MX_ROWS
 }
 
-template <bool ROW>
+// Columnwise with the transform, in the paired kernel: column j of an item
+// (its 16 rows are one 16-row group of the transform) is sign-flipped on the
+// packed words, butterflied and scaled by 1/4 in registers, its half-block
+// maximum joined with lane l ^ 32's, then scaled and encoded into two code
+// words (rows 0..7, 8..15), one column at a time.
+__device__ __forceinline__ void mx_rht_column(const uint4 (&v)[16], int j, uint32_t mask, uint32_t& byte,
+                                              uint32_t (&words)[2])
+{
+    float y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t w = word_at(v[i], j >> 1) ^ rht_row_sign(mask, i);
+        y[i] = (j & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+    rht16_signed(y);
+    uint32_t m = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        m = max(m, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+    const auto sw = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    m = max(sw[0], sw[1]);  // the whole 32-row block
+    byte = mx_scale_byte(m);
+    const float inv = mx_inverse_scale(byte);
+    const uint32_t keep = byte == 0xFFu ? 0x80000000u : 0xFFFFFFFFu;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float f[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            f[k] = __uint_as_float(__float_as_uint(y[8 * h + k]) & keep) * inv;
+        words[h] = mx_word(f);
+    }
+}
+
+template <bool ROW, bool RHT>
 __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void mx_quantize_pair_kernel(MxQuantizeArgs p, int blocks_c)
 {
+    static_assert(!(ROW && RHT), "the transform is columnwise only");
     __shared__ uint2 lds_codes[kPairCols * 16];    // [column][16-row group, swizzled]
     __shared__ uint8_t lds_scales[kPairCols * 8];  // [column][32-row block]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -320,6 +254,23 @@ void mx_quantize_pair_kernel(MxQuantizeArgs p, int blocks_c)
             v[i] = load16_stream(src + i * p.cols);
     }
 
+    const int col_slot = (8 * cg) * 16 + (rg ^ (cg & 15));
+    uint32_t* const lds_words = reinterpret_cast<uint32_t*>(lds_codes);
+    if constexpr (RHT) {
+        // Every lane takes part (the swap joins lanes l and l ^ 32); absent
+        // items stage nothing.
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t byte, words[2];
+            mx_rht_column(v, j, p.mask, byte, words);
+            if (valid) {
+                lds_words[2 * (col_slot + 16 * j)] = words[0];
+                lds_words[2 * (col_slot + 16 * j) + 1] = words[1];
+            }
+            if (lane < 32)
+                lds_scales[(8 * cg + j) * 8 + (rg >> 1)] = (uint8_t)byte;
+        }
+    } else {
     // Block maxima as |bf16| patterns: colm[k] packs columns 2k, 2k+1 over
     // the item's 16 rows; rowm[k] packs rows 2k, 2k+1 over its 8 columns.
     uint32_t colm[4] = {0u, 0u, 0u, 0u};
@@ -401,14 +352,13 @@ void mx_quantize_pair_kernel(MxQuantizeArgs p, int blocks_c)
     }
 
     uint8_t* const row_dst = ROW ? p.codes_row + r0 * (p.cols >> 1) + (c0 >> 1) : nullptr;
-    uint32_t* const lds_words = reinterpret_cast<uint32_t*>(lds_codes);
-    const int col_slot = (8 * cg) * 16 + (rg ^ (cg & 15));
     if (valid) {
         if (__any(any_ff))
             mx_encode_item<ROW, true>(v, rm, rc, rown, cbytes, row_dst, p.cols >> 1, lds_words, col_slot);
         else
             mx_encode_item<ROW, false>(v, rm, rc, rown, cbytes, row_dst, p.cols >> 1, lds_words, col_slot);
     }
+    }  // not RHT
     __syncthreads();
 
     // Columnwise codes: per column 256 rows = 128 bytes, written by 8 lanes
@@ -573,23 +523,24 @@ hipError_t launch_mx_quantize(const MxQuantizeArgs& a, hipStream_t stream)
                            a.codes_row, a.scales_row);
         return hipGetLastError();
     }
-    if (a.colwise && !a.rht) {
+    if (a.colwise) {
+        if (a.rht && a.rowwise)
+            return hipErrorInvalidValue;  // the transform is columnwise only
         const int blocks_r = (int)((a.rows + kPairRows - 1) / kPairRows);
         const int blocks_c = (int)((a.cols + kPairCols - 1) / kPairCols);
         const dim3 grid((unsigned)((int64_t)blocks_r * blocks_c));
-        if (a.rowwise)
-            hipLaunchKernelGGL(mx_quantize_pair_kernel<true>, grid, dim3(kPairThreads), 0, stream, a, blocks_c);
+        if (a.rht)
+            hipLaunchKernelGGL((mx_quantize_pair_kernel<false, true>), grid, dim3(kPairThreads), 0, stream, a,
+                               blocks_c);
+        else if (a.rowwise)
+            hipLaunchKernelGGL((mx_quantize_pair_kernel<true, false>), grid, dim3(kPairThreads), 0, stream, a,
+                               blocks_c);
         else
-            hipLaunchKernelGGL(mx_quantize_pair_kernel<false>, grid, dim3(kPairThreads), 0, stream, a, blocks_c);
+            hipLaunchKernelGGL((mx_quantize_pair_kernel<false, false>), grid, dim3(kPairThreads), 0, stream, a,
+                               blocks_c);
         return hipGetLastError();
     }
-    if (a.rowwise)
-        return hipErrorInvalidValue;  // the transform is columnwise only
-    const int tiles_r = (int)((a.rows + kTR - 1) / kTR);
-    const int tiles_c = (int)((a.cols + kTC - 1) / kTC);
-    hipLaunchKernelGGL(mx_quantize_rht_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(kThreads), 0, stream, a,
-                       tiles_r, tiles_c);
-    return hipGetLastError();
+    return hipErrorInvalidValue;  // the transform is columnwise only
 }
 
 hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
