@@ -3,8 +3,8 @@
 //
 // Every operand element e2m1(code) * e4m3(scale) has at most 6 significant
 // bits and lies in [2^-10, 2688], so it is exact in fp16; products are summed
-// in fp32 by v_mfma_f32_32x32x16_f16. One MFMA consumes K = 16, exactly one
-// NVFP4 scale block.
+// in fp32 by v_mfma_f32_16x16x32_f16. One MFMA consumes K = 32, two NVFP4
+// scale blocks.
 //
 // Structure (one workgroup = 8 waves, a 256 x 256 tile of C at a time):
 //   - K advances 64 at a time (32 when K is not a multiple of 64). Each of
@@ -17,9 +17,9 @@
 //   - LDS rows are 144 bytes apart (64 fp16 + 16 bytes of padding; 80 for
 //     32-element stages) so the 16-byte operand reads of 8 consecutive rows
 //     hit distinct banks.
-//   - Waves form a 4 x 2 grid; each computes a 64 x 128 sub-tile (2 x 4 MFMA
-//     tiles, 128 fp32 accumulators per lane), so two waves share a SIMD and
-//     one's decode overlaps the other's MFMAs. Stages are double-buffered in
+//   - Waves form a 4 x 2 grid; each computes a 64 x 128 sub-tile (4 x 8 MFMA
+//     tiles of 16 x 16, 128 fp32 accumulators per lane), so two waves share a
+//     SIMD and one's decode overlaps the other's MFMAs. Stages are double-buffered in
 //     LDS, and the packed codes are fetched two stages ahead into two
 //     alternating register sets.
 //   - A 2D-scaled operand's tile scales (16 row groups x K/16 bytes) are
@@ -47,7 +47,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
-typedef __attribute__((ext_vector_type(16))) float floatx16;
+typedef __attribute__((ext_vector_type(4))) float floatx4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int kGemmThreads = 512;
@@ -185,29 +185,37 @@ __device__ __forceinline__ f16x8 lds_fragment(const uint8_t* lds, int row, int k
     return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(lds + row * Geo<KS>::kRowBytes + kbyte));
 }
 
-// The MFMAs of one stage for this wave's 64 x (32 FN) sub-tile.
+// The MFMAs of one stage for this wave's 64 x (32 FN) sub-tile: 4 x 2 FN
+// tiles of 16 x 16, lane l holding row (A) or column (B) l % 16 of a tile
+// and K elements 8 (l / 16) .. + 7 of each 32-element step. The four A
+// fragments of a step stay in registers; the B fragments are read one ahead.
 // The wave runs its MFMAs at raised priority, so that of the two waves on a
 // SIMD the one with matrix work issues first and the other's decode fills
 // the gaps (measured: 2-3% on 8192x14336x4096).
 template <int KS, int FN>
 __device__ __forceinline__ void stage_mfma(const uint8_t* buf, int wm, int wn, int frow, int fk,
-                                           floatx16 (&acc)[2][4])
+                                           floatx4 (&acc)[4][8])
 {
+    const uint8_t* const bbuf = buf + kBM * Geo<KS>::kRowBytes;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int ks = 0; ks < KS / 16; ++ks) {
-        f16x8 fa[2], fb[FN];
+    for (int ks = 0; ks < KS / 32; ++ks) {
+        f16x8 fa[4];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-            fa[a] = lds_fragment<KS>(buf, wm + a * 32 + frow, ks * 32 + fk);
+        for (int a = 0; a < 4; ++a)
+            fa[a] = lds_fragment<KS>(buf, wm + a * 16 + frow, ks * 64 + fk);
+        f16x8 fb = lds_fragment<KS>(bbuf, wn + frow, ks * 64 + fk);
 #pragma unroll
-        for (int b = 0; b < FN; ++b)
-            fb[b] = lds_fragment<KS>(buf + kBM * Geo<KS>::kRowBytes, wn + b * 32 + frow, ks * 32 + fk);
+        for (int b = 0; b < 2 * FN; ++b) {
+            f16x8 next;
+            if (b + 1 < 2 * FN)
+                next = lds_fragment<KS>(bbuf, wn + (b + 1) * 16 + frow, ks * 64 + fk);
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+            for (int a = 0; a < 4; ++a)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[a], fb, acc[a][b], 0, 0, 0);
+            fb = next;
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     __builtin_amdgcn_s_setprio(0);
 }
@@ -284,7 +292,7 @@ static_assert(kQuantLds <= 160 * 1024, "LDS");
 static_assert(kBM == 2 * kTileR && kBN == kTileC, "a GEMM tile is a pair of quantize tiles");
 
 template <int QUANT>
-__device__ __forceinline__ void quant_epilogue(const GemmArgs& g, const floatx16 (&acc)[2][4], float scale,
+__device__ __forceinline__ void quant_epilogue(const GemmArgs& g, const floatx4 (&acc)[4][8], float scale,
                                                int64_t m0, int64_t n0, int wm, int wn, int lane, int wave,
                                                int round, uint8_t* lds_in, uint32_t& cmax)
 {
@@ -299,18 +307,18 @@ __device__ __forceinline__ void quant_epilogue(const GemmArgs& g, const floatx16
     // 1. C x fl(S_gA S_gB), rounded to bf16 (nearest even), into LDS; the
     //    K loop's last barrier has passed, so the stage buffers are free.
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int cl = wn + b * 32 + (ln & 31);
+        for (int b = 0; b < 8; ++b) {
+            const int cl = wn + b * 16 + (ln & 15);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int rl = wm + a * 32 + 8 * (i >> 2) + 4 * (ln >> 5) + (i & 3);
+            for (int i = 0; i < 4; ++i) {
+                const int rl = wm + a * 16 + 4 * (ln >> 4) + i;
                 const uint32_t u = __float_as_uint(acc[a][b][i] * scale);
                 const uint16_t h = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
                 *reinterpret_cast<uint16_t*>(lds + rl * kQuantPitch + 2 * cl) = h;
             }
-            __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 tile at a time
+            __builtin_amdgcn_sched_barrier(0);  // one 16 x 16 tile at a time
         }
     const ScaleCtx sc = scale_ctx(*g.q_amax);
     float* const rcp = reinterpret_cast<float*>(lds + kQuantRcp);
@@ -421,8 +429,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int tile
         const int wave = threadIdx.x >> 6;
         const int t = wave * 64 + lane;
         const int wm = (wave >> 1) * 64, wn = (wave & 1) * (32 * FN);
-        const int frow = lane & 31;
-        const int fk = (lane >> 5) * 16;  // byte offset of the lane's 8 K-elements
+        const int frow = lane & 15;
+        const int fk = (lane >> 4) * 16;  // byte offset of the lane's 8 K-elements
         const bool is_b = wave >= kBM / 64;
         const int64_t rows = is_b ? g.N : g.M;
         const bool two_d = is_b ? g.b_two_d : g.a_two_d;
@@ -466,12 +474,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int tile
         if (a_stage || b_stage)
             __syncthreads();
 
-        floatx16 acc[2][4];
+        floatx4 acc[4][8];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[a][b] = floatx16{};
+            for (int b = 0; b < 8; ++b)
+                acc[a][b] = floatx4{};
 
         RowStage<KS> sa, sb;
         if (loads) {
@@ -516,16 +524,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int tile
             quant_epilogue<QUANT>(g, acc, scale, m0, n0, wm, wn, lane, wave, round, lds, cmax);
             continue;
         }
+        // An opaque copy of the lane index keeps the store addresses from
+        // being computed before the K loop (where they would stay live).
+        int el = lane;
+        asm volatile("" : "+v"(el));
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int64_t col = n0 + wn + b * 32 + (lane & 31);
+            for (int b = 0; b < 2 * FN; ++b) {
+                const int64_t col = n0 + wn + b * 16 + (el & 15);
                 if (col >= g.N)
                     continue;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int64_t r = m0 + wm + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t r = m0 + wm + a * 16 + 4 * (el >> 4) + i;
                     if (r >= g.M)
                         continue;
                     const float v = acc[a][b][i] * scale;
