@@ -14,9 +14,11 @@
 //     three exact hardware steps: both scale bytes to fp16 in one E4M3
 //     convert, two codes to fp16 per E2M1 convert, one packed fp16 multiply
 //     per two codes. Each element is decoded once per workgroup.
-//   - LDS rows are 144 bytes apart (64 fp16 + 16 bytes of padding; 80 for
-//     32-element stages) so the 16-byte operand reads of 8 consecutive rows
-//     hit distinct banks.
+//   - A stage in LDS is K-chunk major: for each chunk of 8 K-elements, the
+//     16 bytes of all 512 rows side by side (A rows, then B rows). The 16
+//     lanes of a fragment read that share a chunk read 16 consecutive rows,
+//     256 contiguous bytes, and the decode's 16-byte writes of consecutive
+//     threads are contiguous too: both without bank conflicts or padding.
 //   - Waves form a 4 x 2 grid; each computes a 64 x 128 sub-tile (4 x 8 MFMA
 //     tiles of 16 x 16, 128 fp32 accumulators per lane), so two waves share a
 //     SIMD and one's decode overlaps the other's MFMAs. Stages are double-buffered in
@@ -55,14 +57,14 @@ constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kGroupM = 4;  // tile rows per group of the tile order
 
-// Stage geometry for a stage of KS = 32 or 64 K-elements: padded LDS rows
-// of fp16 (80 or 144 bytes: the 16-byte reads of 8 consecutive rows hit
-// distinct banks), two stages of A rows then B rows, and the largest K whose
-// 2D tile scales a tile stages in LDS next to them (160 KB in all).
+// Stage geometry for a stage of KS = 32 or 64 K-elements: KS / 8 chunk
+// arrays of 512 rows x 16 bytes (fp16 K-elements 8c .. 8c + 7 of every row,
+// A rows then B rows), two stages, and the largest K whose 2D tile scales a
+// tile stages in LDS next to them.
 template <int KS>
 struct Geo {
-    static constexpr int kRowBytes = KS * 2 + 16;
-    static constexpr int kStageBytes = (kBM + kBN) * kRowBytes;
+    static constexpr int kChunkStride = (kBM + kBN) * 16;
+    static constexpr int kStageBytes = (KS / 8) * kChunkStride;
     static constexpr int kLdsScaleK = KS == 32 ? 16384 : 8192;
     static_assert(2 * kStageBytes + 2 * kLdsScaleK <= 160 * 1024, "LDS");
 };
@@ -154,7 +156,8 @@ __device__ __forceinline__ RowStage<KS> fetch_stage(const uint8_t* code_row, con
     return st;
 }
 
-// Decode one row's stage and write its KS fp16 (2 KS bytes) to LDS.
+// Decode one row's stage and write its KS fp16 to LDS: chunk c (16 bytes)
+// at lds_row + c * kChunkStride.
 template <int KS>
 __device__ __forceinline__ void decode_stage_to_lds(const RowStage<KS>& st, uint8_t* lds_row)
 {
@@ -174,15 +177,17 @@ __device__ __forceinline__ void decode_stage_to_lds(const RowStage<KS>& st, uint
             const f16x2 sq = sc[2 * h + (q >> 1)];
             const u32x4 o = {decode_pair<0>(w[q], sq), decode_pair<1>(w[q], sq), decode_pair<2>(w[q], sq),
                              decode_pair<3>(w[q], sq)};
-            *reinterpret_cast<u32x4*>(lds_row + 64 * h + 16 * q) = o;
+            *reinterpret_cast<u32x4*>(lds_row + (4 * h + q) * Geo<KS>::kChunkStride) = o;
         }
     }
 }
 
+// Row `row`'s 8 fp16 at byte kbyte (a multiple of 16) of its KS-element stage.
 template <int KS>
 __device__ __forceinline__ f16x8 lds_fragment(const uint8_t* lds, int row, int kbyte)
 {
-    return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(lds + row * Geo<KS>::kRowBytes + kbyte));
+    return __builtin_bit_cast(f16x8,
+                              *reinterpret_cast<const u32x4*>(lds + (kbyte >> 4) * Geo<KS>::kChunkStride + row * 16));
 }
 
 // The MFMAs of one stage for this wave's 64 x (32 FN) sub-tile: 4 x 2 FN
@@ -196,7 +201,7 @@ template <int KS, int FN>
 __device__ __forceinline__ void stage_mfma(const uint8_t* buf, int wm, int wn, int frow, int fk,
                                            floatx4 (&acc)[4][8])
 {
-    const uint8_t* const bbuf = buf + kBM * Geo<KS>::kRowBytes;
+    const uint8_t* const bbuf = buf + kBM * 16;  // B rows follow the A rows in every chunk
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS / 32; ++ks) {
@@ -388,7 +393,6 @@ template <bool BF16_OUT, bool WIDE, bool AMAX, int KS, int FN, int QUANT = 0>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int first,
                                                         int count)
 {
-    constexpr int kRowBytes = Geo<KS>::kRowBytes;
     constexpr int kStageBytes = Geo<KS>::kStageBytes;
     constexpr int kLdsScaleK = Geo<KS>::kLdsScaleK;
     constexpr int kMainLds = 2 * kStageBytes + 2 * kLdsScaleK;
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int tile
         const bool scales_t = is_b ? g.b_scales_t : g.a_scales_t;
         const uint8_t* codes = is_b ? g.b_codes : g.a_codes;
         const uint8_t* scales = is_b ? g.b_scales : g.a_scales;
-        uint8_t* my_row0 = lds + t * kRowBytes;
+        uint8_t* my_row0 = lds + t * 16;
         const bool my_stage = is_b ? b_stage : a_stage;
         uint8_t* const my_sc = lds_sc + (is_b && a_stage ? kLdsScaleK : 0);
         // Half tiles need 128 B rows: the last two waves fetch nothing.
