@@ -374,7 +374,7 @@ __device__ __forceinline__ void quant_epilogue(const GemmArgs& g, const floatx4 
     if (QCOL) {
         __syncthreads();
         if (t < kThreads)  // the pair writer's 256 threads
-            write_col_pair(p, m0, n0, codes0, codes1, scales0, scales1);
+            write_col_pair(p, m0, n0, codes0, codes1, scales0, scales1, t + (int)zero);
     }
     __syncthreads();  // the next tile's first stage overwrites this LDS
 }

@@ -612,11 +612,14 @@ __device__ __forceinline__ void write_col_tile(const Params& p, int64_t tile_r0,
 // Write the staged columnwise output of two vertically adjacent tiles (A at
 // rows tile_r0.., B below it; B may be absent or ragged). Per column the
 // pair covers 256 rows: 128 bytes of codes, one whole line, written by 8
-// lanes as 16-byte streaming stores, and 16 scale bytes.
+// lanes as 16-byte streaming stores, and 16 scale bytes. tid: the thread's
+// index among the NT writers (a caller inside a loop can pass an opaque copy,
+// so that the addresses are not computed ahead of the loop).
 template <int NT = kThreads>
 __device__ __forceinline__ void write_col_pair(const Params& p, int64_t tile_r0, int64_t tile_c0,
                                                const uint2* codes_a, const uint2* codes_b,
-                                               const uint8_t* scales_a, const uint8_t* scales_b)
+                                               const uint8_t* scales_a, const uint8_t* scales_b,
+                                               int tid = (int)threadIdx.x)
 {
     typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
     const int64_t rows = p.rows, cols = p.cols;
@@ -624,7 +627,7 @@ __device__ __forceinline__ void write_col_pair(const Params& p, int64_t tile_r0,
     const bool wide = (pitch & 15) == 0;  // 16-byte chunks are aligned
 #pragma unroll
     for (int k = 0; k < kTileC * 8 / NT; ++k) {
-        const int q = k * NT + threadIdx.x;
+        const int q = k * NT + tid;
         const int col = q >> 3, part = q & 7;  // part: 32 rows = two row blocks
         const int64_t c = tile_c0 + col, r = tile_r0 + part * 32;
         if (c >= cols || r >= rows)
@@ -648,7 +651,7 @@ __device__ __forceinline__ void write_col_pair(const Params& p, int64_t tile_r0,
         }
     }
     // Scales: one column's 16 bytes (8 per tile) per thread.
-    const int col = threadIdx.x;
+    const int col = tid;
     const int64_t c = tile_c0 + col;
     if (col < kTileC && c < cols) {
         const int64_t spitch = rows >> 4;
