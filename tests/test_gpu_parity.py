@@ -136,6 +136,35 @@ def test_amax_odd_length_tail():
     assert got == 77.0 and f32_bits(got) == f32_bits(oracle.amax(x))
 
 
+@pytest.mark.parametrize("pos", ["first", "middle", "last"])
+def test_amax_planted_max_reused_output(pos):
+    """The one-workgroup-per-CU amax launches read the running maximum before
+    their atomic and skip it when it cannot raise the output. A maximum
+    planted at either end of an 8192x4096 tensor (the first or last
+    workgroup's span), with the output buffer holding a larger value from the
+    previous call, must still come out exact: the plain amax, the transform's
+    amax and both amaxes of the one-read variant."""
+    x = W.normal_tensor(8192, 4096, seed=31)
+    r, c = {"first": (0, 0), "middle": (4100, 2049), "last": (8191, 4095)}[pos]
+    x[r, c] = W.f32_to_bf16_bits(np.array([-640.0], np.float32))[0]
+    big = x.copy()
+    big[17, 5] = W.f32_to_bf16_bits(np.array([1.0e6], np.float32))[0]
+    log(f"[test_amax_planted_max_reused_output] {pos}")
+    out = torch.empty(1, dtype=torch.float32, device="cuda")
+    F.nvfp4_amax(dev(big), out=out)
+    got = host(F.nvfp4_amax(dev(x), out=out))[0]
+    assert got == 640.0 and f32_bits(got) == f32_bits(oracle.amax(x))
+    rht_ref = oracle.amax_rht_mt(x, MASK)
+    F.nvfp4_amax(dev(big), rht=True, rht_mask=MASK, out=out)
+    got_rht = host(F.nvfp4_amax(dev(x), rht=True, rht_mask=MASK, out=out))[0]
+    assert f32_bits(got_rht) == f32_bits(rht_ref)
+    out2 = torch.empty(2, dtype=torch.float32, device="cuda")
+    F.nvfp4_amax(dev(big), rht=True, rht_mask=MASK, both=True, out=out2)
+    got2 = host(F.nvfp4_amax(dev(x), rht=True, rht_mask=MASK, both=True, out=out2))
+    assert f32_bits(got2[0]) == f32_bits(oracle.amax(x))
+    assert f32_bits(got2[1]) == f32_bits(rht_ref)
+
+
 @pytest.mark.parametrize("name", ["ragged_grad", "grad", "act"])
 def test_amax_rht(name):
     x = wl(name)
