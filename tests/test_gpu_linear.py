@@ -209,15 +209,30 @@ def test_training_step_outputs():
         assert torch.isfinite(out[k].float()).all()
 
 
-@pytest.mark.parametrize("mode", [2, 3])
-def test_gemm_2d_scales_beyond_the_lds_staged_k(mode):
-    """K = 16400 is past the K whose tile scales a workgroup stages in LDS:
-    the per-row scale loads serve 2D and transposed 2D operands."""
-    M, N, K = 48, 64, 16400
+def quantize_operand_2d(x):
+    """2D codes and tile scales of a [R][K] operand, and its double reconstruction."""
+    sg = oracle.global_scale(oracle.amax(x))
+    codes, _, scales = oracle.quantize_2d(x, sg)
+    return codes, scales, sg, recon(codes, scales, 2, sg, x.shape[0], x.shape[1])
+
+
+@pytest.mark.parametrize("mode, K, a_mode", [(2, 16400, 1), (3, 16400, 1), (2, 16448, 1), (3, 16448, 1),
+                                              (2, 16400, 2)])
+def test_gemm_2d_scales_beyond_the_lds_staged_k(mode, K, a_mode):
+    """2D and transposed 2D B operands around the K whose tile scales a
+    workgroup stages in LDS. With 32-deep stages (K = 16400, an odd multiple
+    of 16) the region holds 16384 scale columns per operand, twice that for a
+    lone 2D operand: a 1D A keeps B staged, a 2D A (both operands 2D) sends
+    both to the per-row scale loads. With 64-deep stages (K = 16448) a lone 2D
+    operand is staged up to K = 16384, so B takes the per-row loads."""
+    M, N = 48, 64
     a = W.activation(M, K, seed=36, n_outlier_cols=1)
-    sga = oracle.global_scale(oracle.amax(a))
-    ac, as_ = oracle.quantize_1d_rows(a, sga)
-    a_hat = recon(ac, as_, 1, sga, M, K)
+    if a_mode == 1:
+        sga = oracle.global_scale(oracle.amax(a))
+        ac, as_ = oracle.quantize_1d_rows(a, sga)
+        a_hat = recon(ac, as_, 1, sga, M, K)
+    else:
+        ac, as_, sga, a_hat = quantize_operand_2d(a)
     if mode == 2:
         w = W.weight(N, K, seed=37)                     # B = W [N][K], 2D scales [N/16][K/16]
         sgw = oracle.global_scale(oracle.amax(w))
@@ -228,6 +243,6 @@ def test_gemm_2d_scales_beyond_the_lds_staged_k(mode):
         sgw = oracle.global_scale(oracle.amax(w))
         w_rows, b_codes, b_scales = oracle.quantize_2d(w, sgw)
         b_hat = recon(w_rows, b_scales, 2, sgw, K, N).T
-    c = host(F.nvfp4_gemm(to_gpu(ac), to_gpu(as_), 1, sg_gpu(sga),
+    c = host(F.nvfp4_gemm(to_gpu(ac), to_gpu(as_), a_mode, sg_gpu(sga),
                           to_gpu(b_codes), to_gpu(b_scales), mode, sg_gpu(sgw), M, N, K))
     assert rel_fro(c, a_hat @ b_hat.T) <= 1e-5
