@@ -193,10 +193,12 @@ __device__ __forceinline__ f16x8 lds_fragment(const uint8_t* lds, int row, int k
 // The MFMAs of one stage for this wave's 64 x (32 FN) sub-tile: 4 x 2 FN
 // tiles of 16 x 16, lane l holding row (A) or column (B) l % 16 of a tile
 // and K elements 8 (l / 16) .. + 7 of each 32-element step. The four A
-// fragments of a step stay in registers; the B fragments are read one ahead.
-// The wave runs its MFMAs at raised priority, so that of the two waves on a
-// SIMD the one with matrix work issues first and the other's decode fills
-// the gaps (measured: 2-3% on 8192x14336x4096).
+// fragments of a step stay in registers; the B fragments are read one ahead,
+// and a scheduling barrier after each B column's MFMAs keeps the compiler
+// from hoisting the later reads (which was 4% slower). The wave runs its
+// MFMAs at raised priority, so that of the two waves on a SIMD the one with
+// matrix work issues first and the other's decode fills the gaps (measured:
+// 0-3% on 8192x14336x4096).
 template <int KS, int FN>
 __device__ __forceinline__ void stage_mfma(const uint8_t* buf, int wm, int wn, int frow, int fk,
                                            floatx4 (&acc)[4][8])
