@@ -12,11 +12,11 @@ constexpr int kThreads = 256;
 // so a few hundred atomics on one address instead of thousands).
 constexpr int kAmaxThreads = 1024;
 constexpr int kAmaxMaxBlocks = 256;
-// The transform's amax: the pipelined loop (two register sets, one
-// workgroup per CU) where the butterflies would otherwise wait for the
+// The transform's amax: the pipelined loop (two register sets, two
+// workgroups per CU) where the butterflies would otherwise wait for the
 // loads, the plain loop (more waves per SIMD) for large tensors.
 constexpr int64_t kRhtPipeItems = (int64_t)1 << 18;
-constexpr int kRhtPipeBlocks = 256;
+constexpr int kRhtPipeBlocks = 512;
 
 __global__ void amax_reset_kernel(uint32_t* out, int n)
 {
@@ -27,11 +27,11 @@ __global__ void amax_reset_kernel(uint32_t* out, int n)
 // Reduce a per-thread maximum (binary32 bits) over the workgroup and merge
 // it into *out. PEEK: read *out first and skip the atomic when it cannot
 // raise the value (*out only grows during the launch, so the result is the
-// same). For launches of one workgroup per CU, whose maxima all arrive at the
-// end, that leaves few of the same-address atomics to queue: the plain amax
-// of 8192x4096 15.5 -> 14.7 us. With four workgroups per CU (1024 atomics
-// spread over the launch) the extra read cost more than it saved (44.3 ->
-// 46.1 us on 8192x14336), so that path merges directly.
+// same). For launches of one or two workgroups per CU, whose maxima all
+// arrive at the end, that leaves few of the same-address atomics to queue:
+// the plain amax of 8192x4096 15.5 -> 14.7 us. With four workgroups per CU
+// (1024 atomics spread over the launch) the extra read cost more than it
+// saved (44.3 -> 46.1 us on 8192x14336), so that path merges directly.
 template <int THREADS, bool PEEK>
 __device__ __forceinline__ void workgroup_max_to(uint32_t m, uint32_t* out)
 {
@@ -98,9 +98,9 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_bf16_kernel(const uint4* __
 //
 // Each thread walks items of 16 rows x 8 columns. PIPE: it loads the next
 // item into the other of two register sets before transforming the current
-// one, so the butterflies overlap the loads in flight (one wave per SIMD
-// at this register count); else one item at a time, with more waves per
-// SIMD to overlap them instead.
+// one, so the butterflies overlap the loads in flight (two waves per SIMD
+// with buffer loads, see rht_load_item_buf); else one item at a time, with
+// more waves per SIMD to overlap them instead.
 
 // Load one item: 16 rows of 8 bf16, sign-flipped by the mask; with BOTH
 // also fold the raw magnitudes into pm.
@@ -113,6 +113,24 @@ __device__ __forceinline__ void rht_load_item(const uint16_t* __restrict__ x, in
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         v[i] = load16(base + i * cols);
+}
+
+// The same item through buffer loads (tensors under 2 GiB): one 32-bit
+// offset serves all 16 rows, the row stride rides in a scalar register, so
+// an item in flight holds no 64-bit addresses. That keeps the pipelined loop
+// at 215 VGPRs (247 with BOTH) and two waves per SIMD; with per-row 64-bit
+// addresses it took 256 VGPRs and 26 AGPRs, one wave per SIMD.
+__device__ __forceinline__ void rht_load_item_buf(__amdgpu_buffer_rsrc_t rsrc, int64_t cols, int64_t groups,
+                                                  int64_t it, uint4 (&v)[16])
+{
+    const int64_t rb = it / groups, cg = it - rb * groups;
+    const int off = (int)(((rb * 16) * cols + cg * 8) * 2);
+    const int rs = (int)(cols * 2);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, i * rs, 0);
+        v[i] = make_uint4(r[0], r[1], r[2], r[3]);
+    }
 }
 
 template <bool BOTH>
@@ -142,7 +160,7 @@ __device__ __forceinline__ void rht_item_max(uint4 (&v)[16], uint32_t mask, uint
     }
 }
 
-template <bool BOTH, bool PIPE>
+template <bool BOTH, bool PIPE, bool BUF>
 __global__ __launch_bounds__(kThreads) void amax_rht_kernel(const uint16_t* __restrict__ x,
                                                              int64_t rows, int64_t cols,
                                                              uint32_t mask,
@@ -162,17 +180,26 @@ __global__ __launch_bounds__(kThreads) void amax_rht_kernel(const uint16_t* __re
         }
     }
     uint4 va[16], vb[16];
+    // 0x00020000: the gfx9 raw-buffer configuration word (unused without BUF)
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x), 0, BUF ? (int)(rows * cols * 2) : 0, 0x00020000);
+    auto load = [&](int64_t i, uint4 (&v)[16]) {
+        if (BUF)
+            rht_load_item_buf(rsrc, cols, groups, i, v);
+        else
+            rht_load_item<BOTH>(x, cols, groups, i, v);
+    };
     if (PIPE && it < items)
-        rht_load_item<BOTH>(x, cols, groups, it, va);
+        load(it, va);
     while (PIPE && it < items) {
         if (it + stride < items)
-            rht_load_item<BOTH>(x, cols, groups, it + stride, vb);
+            load(it + stride, vb);
         rht_item_max<BOTH>(va, mask, pm, m);
         it += stride;
         if (it >= items)
             break;
         if (it + stride < items)
-            rht_load_item<BOTH>(x, cols, groups, it + stride, va);
+            load(it + stride, va);
         rht_item_max<BOTH>(vb, mask, pm, m);
         it += stride;
     }
@@ -220,16 +247,20 @@ hipError_t launch_amax_rht(const uint16_t* x, int64_t rows, int64_t cols, uint32
     hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(64), 0, stream, out, both ? 2 : 1);
     const int64_t items = (rows >> 4) * (cols >> 3);
     const bool pipe = both || items <= kRhtPipeItems;
+    const bool buf = rows * cols * 2 < ((int64_t)1 << 31);  // byte offsets fit the buffer loads
     const int grid = pipe ? grid_for(items, kThreads, kRhtPipeBlocks) : grid_for(items, kThreads, 1024);
-    if (both)
-        hipLaunchKernelGGL((amax_rht_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols,
-                           mask, out);
+    if (both && buf)
+        hipLaunchKernelGGL((amax_rht_kernel<true, true, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows,
+                           cols, mask, out);
+    else if (both)
+        hipLaunchKernelGGL((amax_rht_kernel<true, true, false>), dim3(grid), dim3(kThreads), 0, stream, x, rows,
+                           cols, mask, out);
     else if (pipe)
-        hipLaunchKernelGGL((amax_rht_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols,
-                           mask, out);
+        hipLaunchKernelGGL((amax_rht_kernel<false, true, true>), dim3(grid), dim3(kThreads), 0, stream, x, rows,
+                           cols, mask, out);
     else
-        hipLaunchKernelGGL((amax_rht_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, x, rows, cols,
-                           mask, out);
+        hipLaunchKernelGGL((amax_rht_kernel<false, false, false>), dim3(grid), dim3(kThreads), 0, stream, x, rows,
+                           cols, mask, out);
     return hipGetLastError();
 }
 
