@@ -165,6 +165,20 @@ def test_amax_planted_max_reused_output(pos):
     assert f32_bits(got2[1]) == f32_bits(rht_ref)
 
 
+@pytest.mark.parametrize("pos", [(8192, 0), (10000, 1234), (12287, 4095)])
+def test_amax_partial_last_round(pos):
+    """12288x4096 is one and a half rounds of the plain amax's grid-stride
+    loop (256 workgroups x 1024 threads x 16 vectors): rows 8192 onwards are
+    read by the last, partial round, whose loads past the end repeat the
+    last vector. A maximum planted at the start, inside and at the very end
+    of that region must come out exact."""
+    x = W.normal_tensor(12288, 4096, seed=37)
+    x[pos] = W.f32_to_bf16_bits(np.array([-512.0], np.float32))[0]
+    log(f"[test_amax_partial_last_round] {pos}")
+    got = host(F.nvfp4_amax(dev(x)))[0]
+    assert got == 512.0 and f32_bits(got) == f32_bits(oracle.amax(x))
+
+
 @pytest.mark.parametrize("name", ["ragged_grad", "grad", "act"])
 def test_amax_rht(name):
     x = wl(name)
